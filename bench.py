@@ -1,0 +1,219 @@
+"""Benchmark of the deterministic attention backward on one MI355X.
+
+One step = one dash_attn_bwd call (preprocess + persistent backward kernel with the
+ordered dQ reduction, dQ written by the last contributor) over one batch of
+synthetic bf16 inputs resident in HBM. The default workload is the full-mask
+configuration the headline metric is quoted on (B=8, H=Hkv=16, N=2048, d=128,
+16 384 tokens, hidden 2048) with the shift schedule; the naive ordered schedule
+and the atomic (non-deterministic) variant are timed beside it for the
+det/non-det ratio.
+
+Prints ONE JSON line on stdout (details on stderr).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "deterministic attn-bwd TFLOPS (full/causal, d=64/128) + det/non-det ratio"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA peak
+
+WORKLOADS = {
+    # name: (B, H, Hkv, N, d, causal, best deterministic schedule, other schedules, config index)
+    "full-d128-N2048": (8, 16, 16, 2048, 128, False, "shift", ("naive",), 1),
+    "causal-d64-N4096": (4, 32, 32, 4096, 64, True, "sym_shift", ("descending", "naive"), 2),
+    "causal-d128-N16384": (1, 16, 16, 16384, 128, True, "sym_shift", ("descending", "naive"), 3),
+    "gqa-causal-d128-N8192": (1, 32, 8, 8192, 128, True, "sym_shift", ("descending", "naive"), 4),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def flops_bwd(B, H, N, d, causal):
+    f = 2.5 * 4.0 * N * N * d * B * H
+    return f / 2.0 if causal else f
+
+
+def make_inputs(B, H, Hkv, N, d, causal, seed):
+    import numpy as np
+    import torch
+
+    from scheduling_fa_attn_amd import inputs
+    from scheduling_fa_attn_amd.forward_inputs import forward_stats
+
+    bits = inputs.make_qkvdo(B, H, Hkv, N, d, seed)
+    dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in bits.items()}
+    dev["o"], dev["lse"] = forward_stats(dev["q"], dev["k"], dev["v"], causal)
+    torch.cuda.synchronize()
+    return dev
+
+
+def time_schedule(dev, shape, causal, schedule, deterministic, steps, warmup, workspace):
+    """Returns (ms per step over the timed block, mean main-kernel ms from events, outputs)."""
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    B, H, Hkv, N, d = shape
+    dq = torch.empty_like(dev["q"])
+    dk = torch.empty_like(dev["k"])
+    dv = torch.empty_like(dev["v"])
+    scale = 1.0 / math.sqrt(d)
+    mask = "causal" if causal else "full"
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:  # materialise the HIP events
+        a.record()
+        b.record()
+
+    def call(i=None):
+        st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], dq, dk, dv,
+                                scale, mask, schedule, deterministic, workspace, stream=stream.cuda_stream,
+                                main_start=None if i is None else ev[i][0].cuda_event,
+                                main_stop=None if i is None else ev[i][1].cuda_event)
+        if st != dash.DASH_OK:
+            raise dash.DashError(st, "dash_attn_bwd")
+
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    err = dash.dash_last_kernel_error()
+    if err != dash.DASH_OK:
+        raise dash.DashError(err, "kernel")
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(steps):
+        call(i)
+    t_stop.record()
+    torch.cuda.synchronize()
+    err = dash.dash_last_kernel_error()
+    if err != dash.DASH_OK:
+        raise dash.DashError(err, "kernel")
+    total_ms = t_start.elapsed_time(t_stop)
+    main_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return total_ms / steps, main_ms, (dq, dk, dv)
+
+
+def cpu_baseline(shape, causal, seed, budget_s):
+    """The fp64 oracle backward on the host cores, on whole heads of the same workload."""
+    import numpy as np
+
+    from oracle import attention as oa
+    from scheduling_fa_attn_amd import inputs
+
+    B, H, Hkv, N, d = shape
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((x.get("num_threads", 0) for x in threadpool_info()), default=0) or os.cpu_count()
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    G = H // Hkv
+    scale = 1.0 / math.sqrt(d)
+    heads = 0
+    elapsed = 0.0
+    group = 0
+    # Whole KV-head groups (one KV head and its G query heads) of seeded inputs of the
+    # workload's shape, until the time budget is spent.
+    while heads < B * H and (heads == 0 or elapsed < budget_s):
+        bits = inputs.make_qkvdo(1, G, 1, N, d, seed * 1000 + group)
+        f = {k: inputs.bf16_bits_to_f32(v).astype(np.float64) for k, v in bits.items()}
+        o, lse = oa.forward(f["q"], f["k"], f["v"], causal, scale)
+        t0 = time.perf_counter()
+        oa.backward(f["q"], f["k"], f["v"], o, f["do"], lse, causal, scale)
+        elapsed += time.perf_counter() - t0
+        heads += G
+        group += 1
+    fl = flops_bwd(1, heads, N, d, causal)
+    return {"value": fl / elapsed / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "sample": f"{heads} of {B * H} (batch, query head) units at full N={N}, d={d}, seeded inputs of "
+                      f"the workload's shape; fp64 numpy backward only, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="full-d128-N2048", choices=list(WORKLOADS))
+    ap.add_argument("--schedule", default=None)
+    ap.add_argument("--no-compare", action="store_true", help="skip the other schedules and the atomic variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+              "the backward of independent (batch, KV head) units would shard over GPUs with no exchange.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    B, H, Hkv, N, d, causal, best, others, cfg_index = WORKLOADS[args.workload]
+    schedule = args.schedule or best
+    shape = (B, H, Hkv, N, d)
+    seed = 1000 + cfg_index
+    torch.cuda.set_device(0)
+    log(f"workload {args.workload}: B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} seed={seed}")
+    dev = make_inputs(B, H, Hkv, N, d, causal, seed)
+    ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    fl = flops_bwd(B, H, N, d, causal)
+
+    ms, main_ms, _ = time_schedule(dev, shape, causal, schedule, 1, args.steps, args.warmup, ws)
+    tflops = fl / (ms * 1e-3) / 1e12
+    log(f"{schedule} det: {ms:.3f} ms/step ({tflops:.1f} TFLOPS), main kernel {main_ms:.3f} ms")
+    extra = {schedule: round(tflops, 2)}
+    ratio = None
+    if not args.no_compare:
+        for s in others:
+            ms_s, _, _ = time_schedule(dev, shape, causal, s, 1, args.steps, args.warmup, ws)
+            extra[s] = round(fl / (ms_s * 1e-3) / 1e12, 2)
+            log(f"{s} det: {ms_s:.3f} ms/step ({extra[s]:.1f} TFLOPS)")
+        ms_a, _, _ = time_schedule(dev, shape, causal, schedule, 0, args.steps, args.warmup, ws)
+        extra["atomic_" + schedule] = round(fl / (ms_a * 1e-3) / 1e12, 2)
+        ratio = ms_a / ms
+        log(f"{schedule} atomic: {ms_a:.3f} ms/step ({extra['atomic_' + schedule]:.1f} TFLOPS); "
+            f"det/non-det throughput ratio {ratio:.3f}")
+
+    achieved = fl / (main_ms * 1e-3) / 1e12
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d,
+                   "mask": "causal" if causal else "full", "schedule": schedule, "deterministic": True,
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "det_nondet_ratio": None if ratio is None else round(ratio, 4),
+        "schedules_tflops": extra,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": f"bwd_main_kernel<{d},{4 if N >= 512 else 2}>", "main_kernel_ms": round(main_ms, 4)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(shape, causal, seed, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

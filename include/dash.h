@@ -1,0 +1,134 @@
+/*
+ * dash.h -- C ABI of the deterministic attention backward for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (DASH paper, arXiv 2601.21824, section 2.1; "Writing an Attention
+ * Kernel", section "In the real world"): given the forward inputs Q, K, V, the
+ * forward output O, the upstream gradient dO and the forward's per-row
+ * log-sum-exp, compute dQ, dK, dV of softmax attention by recomputing the
+ * probabilities tile by tile. KV tiles are spread over compute units; each CU keeps
+ * its KV tile's dK/dV in registers (reduction over the query axis, local), while
+ * the dQ partial sums of one query tile arrive from many CUs and are added in a
+ * fixed order (reduction over the key axis, global). The order is the one the
+ * selected schedule defines (section 3): naive (ascending KV index, the
+ * FlashAttention-3 deterministic baseline), descending Q-tile iteration (3.3),
+ * shift scheduling (3.4, full mask) or symmetric shift (3.4, causal mask).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Tensors are dense, row-major, bf16 unless stated:
+ *     q, o, dO, dq : [B, H,   N, d]
+ *     k, v, dk, dv : [B, Hkv, N, d]
+ *     lse          : [B, H, N] float32, natural-log log-sum-exp of the *scaled*
+ *                    scores softmax_scale * q.k of each query row.
+ *   Query head h reads key/value head h / (H / Hkv) (grouped-query attention).
+ *   dk and dv of a key/value head sum the contributions of all its query heads.
+ * - The causal mask is top-left aligned: key k is visible to query q iff k <= q.
+ * - d must be 64 or 128. Any N >= 1 is accepted (the last tile is partial).
+ * - Every pointer of dash_attn_bwd is a device pointer owned by the caller; the
+ *   library never frees or retains it. Outputs are overwritten, not accumulated.
+ * - `stream` is a hipStream_t (0 = the null stream). Calls return after enqueueing.
+ * - All argument checks run before anything is enqueued: on an error return no
+ *   kernel is launched and the outputs are untouched.
+ * - The library owns, per device, a schedule-table cache (built on the first call
+ *   for a given shape, mask and schedule; the build copies the table to the
+ *   device synchronously) and a 4-byte device error word. Both live until the
+ *   process ends. The cache is guarded by a mutex; calls from several host
+ *   threads are safe, but two calls that share a workspace must not overlap.
+ */
+#ifndef DASH_H
+#define DASH_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (negative = error). */
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = -1,   /* null pointer, bad size, H % Hkv != 0, ...          */
+  DASH_ERR_UNSUPPORTED = -2,   /* d not in {64,128}; schedule not defined for mask   */
+  DASH_ERR_WORKSPACE = -3,     /* workspace smaller than dash_attn_bwd_workspace_size */
+  DASH_ERR_NOT_CORESIDENT = -4,/* the persistent grid cannot be resident at once     */
+  DASH_ERR_HIP = -5,           /* a HIP runtime call failed                           */
+  DASH_ERR_TIMEOUT = -6,       /* a kernel's ordered-reduction wait timed out         */
+  DASH_ERR_PLACEMENT = -7      /* the workgroups did not land on the CUs the table expects */
+} dash_status;
+
+typedef enum { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 } dash_mask;
+
+/* Tile-to-CU schedules (DASH, section 3). shift is defined for the full mask only,
+ * sym_shift for the causal mask only (with an even number of KV tiles per head). */
+typedef enum {
+  DASH_SCHED_NAIVE = 0,
+  DASH_SCHED_DESCENDING = 1,
+  DASH_SCHED_SHIFT = 2,
+  DASH_SCHED_SYM_SHIFT = 3
+} dash_schedule;
+
+/* Bytes of caller-provided device workspace dash_attn_bwd needs for this shape:
+ * an fp32 dQ accumulator [B,H,N,d], the fp32 row terms D = rowsum(dO*O) [B,H,N]
+ * and the int32 ordering semaphores. Returns 0 for invalid sizes. */
+size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
+
+/* The backward pass (DASH, section 2.1; the schedules of section 3).
+ * deterministic = 1: dQ partial sums are added in the schedule's fixed order; the
+ *   result is bitwise identical from run to run.
+ * deterministic = 0: dQ partial sums are added with floating-point atomics
+ *   (completion order, not reproducible; kept for comparison, section 1). The
+ *   schedule still sets the tile order.
+ * softmax_scale must be finite and > 0 (1/sqrt(d) for standard attention).
+ * B == 0 or N == 0 is a no-op that returns DASH_OK.
+ * Errors: DASH_ERR_INVALID_ARG, _UNSUPPORTED, _WORKSPACE, _NOT_CORESIDENT, _HIP.
+ * Kernel-side failures (a timed-out wait) are reported by dash_last_kernel_error. */
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                  const void* dO, const float* lse,
+                  void* dq, void* dk, void* dv,
+                  int B, int H, int Hkv, int N, int d, float softmax_scale,
+                  int mask, int schedule, int deterministic,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Same as dash_attn_bwd, and additionally records the hipEvent_t main_start before
+ * and main_stop after the main backward kernel on `stream` (either may be null),
+ * so callers can time that kernel alone. */
+int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o,
+                        const void* dO, const float* lse,
+                        void* dq, void* dk, void* dv,
+                        int B, int H, int Hkv, int N, int d, float softmax_scale,
+                        int mask, int schedule, int deterministic,
+                        void* workspace, size_t workspace_bytes, void* stream,
+                        void* main_start, void* main_stop);
+
+/* Synchronizes the current device, returns the device error word left by the
+ * kernels since the last call (DASH_OK, DASH_ERR_TIMEOUT or DASH_ERR_PLACEMENT)
+ * and clears it. Returns DASH_ERR_HIP if the synchronization itself fails. */
+int dash_last_kernel_error(void);
+
+/* Human-readable name of a status code (static storage; never null). */
+const char* dash_status_string(int status);
+
+/* KV/Q tile edge (rows) the library uses for this sequence length: 64 when N < 512,
+ * else 128. The schedules work on a square grid of ceil(N / tile) tiles per head. */
+int dash_tile_size(int N);
+
+/* Host-only export of the schedule table, for checking (no GPU work).
+ * The table is built for `num_xcd` L2 domains of `cus_per_xcd` compute units each
+ * (the GPU library uses the topology it measures on the device).
+ * Writes up to `capacity` records of 7 ints into `records`:
+ *   (worker, b, h, g, i, j, rank)
+ * in worker order and, within a worker, in execution order. worker = xcd *
+ * cus_per_xcd + slot; i = KV tile, j = Q tile, rank = position of this task in the
+ * reduction order of dQ tile (b, h, j). *count receives the number of records (also
+ * when capacity is too small, in which case DASH_ERR_WORKSPACE is returned and
+ * nothing is written). *xcd_local (may be null) receives 1 when every dQ tile's
+ * contributors sit on one L2 domain. Errors: as dash_attn_bwd's argument checks. */
+int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
+                        int num_xcd, int cus_per_xcd,
+                        int* records, long long capacity, long long* count, int* xcd_local);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_H */

@@ -1,0 +1,390 @@
+// Host side of the C ABI declared in include/dash.h: argument checks, per-device state
+// (measured XCD topology, device error word, schedule-table cache) and kernel launches.
+#include "dash.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "kernels.h"
+#include "schedule.h"
+
+namespace {
+
+using dash::Sched;
+
+constexpr int kCtrInts = 16 * 64;  // one 256-byte line per XCD slot counter
+constexpr int64_t kMaxTasks = int64_t(1) << 30;
+
+int tile_for(int N) { return N < 512 ? 64 : 128; }
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct WsLayout {
+  size_t dqacc = 0, delta = 0, sem = 0, ctr = 0, total = 0;
+  int sem_stride = 0;
+};
+
+WsLayout ws_layout(int B, int H, int N, int d) {
+  WsLayout L;
+  L.sem_stride = static_cast<int>(cdiv(cdiv(N, 64) + 1, 32) * 32);
+  const size_t dq_bytes = align256(size_t(B) * H * N * d * sizeof(float));
+  const size_t delta_bytes = align256(size_t(B) * H * N * sizeof(float));
+  const size_t sem_bytes = align256(size_t(B) * H * L.sem_stride * sizeof(int));
+  L.dqacc = 0;
+  L.delta = L.dqacc + dq_bytes;
+  L.sem = L.delta + delta_bytes;
+  L.ctr = L.sem + sem_bytes;
+  L.total = L.ctr + kCtrInts * sizeof(int);
+  return L;
+}
+
+// Checks shared by every entry point; pointers are checked separately.
+int check_sizes(int B, int H, int Hkv, int N, int d, int mask, int schedule) {
+  if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return DASH_ERR_INVALID_ARG;
+  if (N > (1 << 22) || int64_t(B) * H > (int64_t(1) << 24)) return DASH_ERR_INVALID_ARG;
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_INVALID_ARG;
+  if (schedule < DASH_SCHED_NAIVE || schedule > DASH_SCHED_SYM_SHIFT) return DASH_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DASH_ERR_UNSUPPORTED;
+  const bool causal = mask == DASH_MASK_CAUSAL;
+  if (schedule == DASH_SCHED_SHIFT && causal) return DASH_ERR_UNSUPPORTED;
+  if (schedule == DASH_SCHED_SYM_SHIFT && !causal) return DASH_ERR_UNSUPPORTED;
+  const int64_t n = cdiv(N, tile_for(N));
+  if (schedule == DASH_SCHED_SYM_SHIFT && (n % 2) != 0) return DASH_ERR_UNSUPPORTED;
+  const int64_t per_head = causal ? n * (n + 1) / 2 : n * n;
+  if (int64_t(B) * H * per_head > kMaxTasks) return DASH_ERR_INVALID_ARG;
+  return DASH_OK;
+}
+
+struct DevTable {
+  void* buf = nullptr;  // worker_begin | items | tasks
+  const int* worker_begin = nullptr;
+  const int4* items = nullptr;
+  const int4* tasks = nullptr;
+  int workers = 0;
+  int tile = 0;
+  bool xcd_local = true;
+};
+
+struct DeviceState {
+  bool ready = false;
+  int status = DASH_OK;
+  int cus = 0;
+  int num_xcd = 1;
+  int cus_per_xcd = 1;
+  int* err = nullptr;
+  long long ticks_per_second = 100000000LL;
+  std::map<std::tuple<int, int, int, int, int, int, int>, DevTable> tables;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceState> g_devices;
+
+// Measures which XCD each workgroup of a one-per-CU grid lands on. A clean
+// round-robin split (every XCD id present with the same count) gives the table
+// topology; anything else falls back to one domain spanning all CUs.
+int init_device(int dev, DeviceState* st) {
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DASH_ERR_HIP;
+  st->cus = prop.multiProcessorCount;
+  int coop = 0;
+  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop)
+    return DASH_ERR_NOT_CORESIDENT;
+  int rate_khz = 0;
+  if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && rate_khz > 0)
+    st->ticks_per_second = static_cast<long long>(rate_khz) * 1000LL;
+  if (hipMalloc(reinterpret_cast<void**>(&st->err), 256) != hipSuccess) return DASH_ERR_HIP;
+  if (hipMemset(st->err, 0, 256) != hipSuccess) return DASH_ERR_HIP;
+  int* probe = nullptr;
+  if (hipMalloc(reinterpret_cast<void**>(&probe), sizeof(int) * st->cus) != hipSuccess) return DASH_ERR_HIP;
+  hipError_t e = dash::launch_topology_probe(probe, st->cus, nullptr);
+  std::vector<int> ids(st->cus, -1);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(ids.data(), probe, sizeof(int) * st->cus, hipMemcpyDeviceToHost);
+  hipFree(probe);
+  if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
+  if (e != hipSuccess) return DASH_ERR_HIP;
+  int max_id = -1;
+  std::vector<int> count(16, 0);
+  bool sane = true;
+  for (int x : ids) {
+    if (x < 0 || x >= 16) {
+      sane = false;
+      break;
+    }
+    count[x]++;
+    if (x > max_id) max_id = x;
+  }
+  st->num_xcd = 1;
+  st->cus_per_xcd = st->cus;
+  if (sane && max_id >= 1) {
+    const int X = max_id + 1;
+    bool even = (st->cus % X) == 0;
+    for (int x = 0; x < X && even; ++x) even = count[x] == st->cus / X;
+    if (even) {
+      st->num_xcd = X;
+      st->cus_per_xcd = st->cus / X;
+    }
+  }
+  st->ready = true;
+  return DASH_OK;
+}
+
+int get_device(DeviceState** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  DeviceState& st = g_devices[dev];
+  if (!st.ready) {
+    if (st.status != DASH_OK) return st.status;
+    const int s = init_device(dev, &st);
+    if (s != DASH_OK) {
+      st.status = s;
+      return s;
+    }
+  }
+  *out = &st;
+  return DASH_OK;
+}
+
+int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int schedule, const DevTable** out) {
+  const int tile = tile_for(N);
+  auto key = std::make_tuple(B, H, Hkv, N, tile, causal ? 1 : 0, schedule);
+  auto found = st->tables.find(key);
+  if (found != st->tables.end()) {
+    *out = &found->second;
+    return DASH_OK;
+  }
+  dash::SchedParams sp;
+  sp.B = B;
+  sp.H = H;
+  sp.Hkv = Hkv;
+  sp.N = N;
+  sp.tile = tile;
+  sp.causal = causal;
+  sp.kind = static_cast<Sched>(schedule);
+  sp.num_xcd = st->num_xcd;
+  sp.cus_per_xcd = st->cus_per_xcd;
+  dash::Table t;
+  std::string err;
+  const int s = dash::build_table(sp, &t, &err);
+  if (s != 0) return s;
+  const size_t wb_bytes = align256(sizeof(int32_t) * t.worker_begin.size());
+  const size_t it_bytes = align256(sizeof(dash::Item) * t.items.size());
+  const size_t tk_bytes = align256(sizeof(dash::Task) * (t.tasks.size() + 1));
+  std::vector<char> host(wb_bytes + it_bytes + tk_bytes, 0);
+  std::memcpy(host.data(), t.worker_begin.data(), sizeof(int32_t) * t.worker_begin.size());
+  std::memcpy(host.data() + wb_bytes, t.items.data(), sizeof(dash::Item) * t.items.size());
+  if (!t.tasks.empty())
+    std::memcpy(host.data() + wb_bytes + it_bytes, t.tasks.data(), sizeof(dash::Task) * t.tasks.size());
+  DevTable dt;
+  if (hipMalloc(&dt.buf, host.size()) != hipSuccess) return DASH_ERR_HIP;
+  if (hipMemcpy(dt.buf, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    hipFree(dt.buf);
+    return DASH_ERR_HIP;
+  }
+  char* base = static_cast<char*>(dt.buf);
+  dt.worker_begin = reinterpret_cast<const int*>(base);
+  dt.items = reinterpret_cast<const int4*>(base + wb_bytes);
+  dt.tasks = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes);
+  dt.workers = t.workers;
+  dt.tile = tile;
+  dt.xcd_local = t.xcd_local;
+  auto ins = st->tables.emplace(key, dt);
+  *out = &ins.first->second;
+  return DASH_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
+            void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int mask, int schedule,
+            int deterministic, void* workspace, size_t workspace_bytes, void* stream_ptr, void* ev_start,
+            void* ev_stop) {
+  int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
+  if (s != DASH_OK) return s;
+  if (deterministic != 0 && deterministic != 1) return DASH_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || !std::isfinite(scale)) return DASH_ERR_INVALID_ARG;
+  if (B == 0 || N == 0) return DASH_OK;
+  const void* ptrs[] = {q, k, v, o, dO, dq, dk, dv};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr || !aligned(ptr, 16)) return DASH_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return DASH_ERR_INVALID_ARG;
+  if (workspace == nullptr || !aligned(workspace, 256)) return DASH_ERR_INVALID_ARG;
+  const WsLayout L = ws_layout(B, H, N, d);
+  if (workspace_bytes < L.total) return DASH_ERR_WORKSPACE;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+  const bool causal = mask == DASH_MASK_CAUSAL;
+  DeviceState* st = nullptr;
+  const DevTable* tab = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    s = get_device(&st);
+    if (s != DASH_OK) return s;
+    s = get_table(st, B, H, Hkv, N, causal, schedule, &tab);
+    if (s != DASH_OK) return s;
+  }
+  char* ws = static_cast<char*>(workspace);
+  float* dqacc = reinterpret_cast<float*>(ws + L.dqacc);
+  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  int* sem = reinterpret_cast<int*>(ws + L.sem);
+  int* ctr = reinterpret_cast<int*>(ws + L.ctr);
+
+  dash::PreParams pp;
+  pp.o = static_cast<const __bf16*>(o);
+  pp.dO = static_cast<const __bf16*>(dO);
+  pp.delta = delta;
+  pp.rows = int64_t(B) * H * N;
+  pp.sem = sem;
+  pp.sem_count = int64_t(B) * H * L.sem_stride;
+  pp.ctr = ctr;
+  pp.ctr_count = kCtrInts;
+  pp.dqacc_zero = deterministic ? nullptr : dqacc;
+  pp.zero_count = int64_t(B) * H * N * d;
+  const int64_t pre_threads = pp.rows * (d / 8);
+  const int pre_grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(cdiv(pre_threads, 256), 1), 4096));
+  if (dash::launch_preprocess(pp, d, pre_grid, stream) != hipSuccess) return DASH_ERR_HIP;
+
+  dash::BwdParams bp;
+  bp.q = static_cast<const __bf16*>(q);
+  bp.k = static_cast<const __bf16*>(k);
+  bp.v = static_cast<const __bf16*>(v);
+  bp.dO = static_cast<const __bf16*>(dO);
+  bp.lse = lse;
+  bp.delta = delta;
+  bp.dq = static_cast<__bf16*>(dq);
+  bp.dk = static_cast<__bf16*>(dk);
+  bp.dv = static_cast<__bf16*>(dv);
+  bp.dqacc = dqacc;
+  bp.sem = sem;
+  bp.ctr = ctr;
+  bp.err = st->err;
+  bp.worker_begin = tab->worker_begin;
+  bp.items = tab->items;
+  bp.tasks = tab->tasks;
+  bp.B = B;
+  bp.H = H;
+  bp.Hkv = Hkv;
+  bp.N = N;
+  bp.sem_stride = L.sem_stride;
+  bp.scale = scale;
+  bp.scale_log2 = scale * 1.4426950408889634f;
+  bp.causal = causal ? 1 : 0;
+  bp.deterministic = deterministic;
+  bp.xcd_local = (tab->xcd_local && st->num_xcd > 1) ? 1 : 0;
+  bp.num_xcd = st->num_xcd;
+  bp.cus_per_xcd = st->cus_per_xcd;
+  bp.timeout_ticks = st->ticks_per_second * 5;  // 5 seconds per wait
+  if (ev_start && hipEventRecord(static_cast<hipEvent_t>(ev_start), stream) != hipSuccess) return DASH_ERR_HIP;
+  hipError_t e = dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
+  if (e != hipSuccess) return DASH_ERR_HIP;
+  if (ev_stop && hipEventRecord(static_cast<hipEvent_t>(ev_stop), stream) != hipSuccess) return DASH_ERR_HIP;
+  if (!deterministic) {
+    const int64_t count = int64_t(B) * H * N * d;
+    const int grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(cdiv(count / 4, 256), 1), 8192));
+    if (dash::launch_dq_cast(dqacc, dq, count, scale, grid, stream) != hipSuccess) return DASH_ERR_HIP;
+  }
+  return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d) {
+  if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (d != 64 && d != 128)) return 0;
+  if (N > (1 << 22) || int64_t(B) * H > (int64_t(1) << 24)) return 0;
+  return ws_layout(B, H, N, d).total;
+}
+
+int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
+                  void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float softmax_scale, int mask,
+                  int schedule, int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
+  return run_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, softmax_scale, mask, schedule, deterministic,
+                 workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                        const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                        float softmax_scale, int mask, int schedule, int deterministic, void* workspace,
+                        size_t workspace_bytes, void* stream, void* main_start, void* main_stop) {
+  return run_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, softmax_scale, mask, schedule, deterministic,
+                 workspace, workspace_bytes, stream, main_start, main_stop);
+}
+
+int dash_last_kernel_error(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  auto found = g_devices.find(dev);
+  if (found == g_devices.end() || !found->second.ready) return DASH_OK;
+  if (hipDeviceSynchronize() != hipSuccess) return DASH_ERR_HIP;
+  int v = 0;
+  if (hipMemcpy(&v, found->second.err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return DASH_ERR_HIP;
+  if (hipMemset(found->second.err, 0, sizeof(int)) != hipSuccess) return DASH_ERR_HIP;
+  return v;
+}
+
+const char* dash_status_string(int status) {
+  switch (status) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_INVALID_ARG: return "invalid argument";
+    case DASH_ERR_UNSUPPORTED: return "unsupported configuration";
+    case DASH_ERR_WORKSPACE: return "workspace too small";
+    case DASH_ERR_NOT_CORESIDENT: return "persistent grid cannot be co-resident";
+    case DASH_ERR_HIP: return "HIP runtime error";
+    case DASH_ERR_TIMEOUT: return "ordered-reduction wait timed out";
+    case DASH_ERR_PLACEMENT: return "workgroup placement does not match the schedule table";
+    default: return "unknown status";
+  }
+}
+
+int dash_tile_size(int N) { return tile_for(N); }
+
+int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
+                        int* records, long long capacity, long long* count, int* xcd_local) {
+  int s = check_sizes(B, H, Hkv, N, 64, mask, schedule);
+  if (s != DASH_OK) return s;
+  if (num_xcd <= 0 || cus_per_xcd <= 0 || count == nullptr || capacity < 0) return DASH_ERR_INVALID_ARG;
+  dash::SchedParams sp;
+  sp.B = B;
+  sp.H = H;
+  sp.Hkv = Hkv;
+  sp.N = N;
+  sp.tile = tile_for(N);
+  sp.causal = mask == DASH_MASK_CAUSAL;
+  sp.kind = static_cast<Sched>(schedule);
+  sp.num_xcd = num_xcd;
+  sp.cus_per_xcd = cus_per_xcd;
+  dash::Table t;
+  std::string err;
+  s = dash::build_table(sp, &t, &err);
+  if (s != 0) return s;
+  *count = static_cast<long long>(t.tasks.size());
+  if (xcd_local) *xcd_local = t.xcd_local ? 1 : 0;
+  if (static_cast<long long>(t.tasks.size()) > capacity) return DASH_ERR_WORKSPACE;
+  if (!t.tasks.empty() && records == nullptr) return DASH_ERR_INVALID_ARG;
+  for (size_t x = 0; x < t.tasks.size(); ++x) {
+    const dash::Item& it = t.items[t.task_item[x]];
+    int* r = records + 7 * x;
+    r[0] = t.task_worker[x];
+    r[1] = it.b;
+    r[2] = t.tasks[x].h;
+    r[3] = it.g;
+    r[4] = it.i;
+    r[5] = t.tasks[x].j;
+    r[6] = t.tasks[x].rank;
+  }
+  return DASH_OK;
+}
+
+}  // extern "C"

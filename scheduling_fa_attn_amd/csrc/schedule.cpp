@@ -1,0 +1,193 @@
+// Schedule-table builder: which CU runs which (KV tile, Q tile, query head) task,
+// in which order, and at which place of its dQ tile's reduction order.
+//
+// Sources: DASH paper (arXiv 2601.21824), section 3 (normalisation of n KV tiles to
+// n SMs, refined or aggregated otherwise), 3.2 (the FlashAttention-3 baseline:
+// ascending Q tiles, dQ reduced in ascending KV order), 3.3 (descending Q-tile
+// iteration), 3.4 (shift scheduling for the full mask, Fig. 6; symmetric shift with
+// two-phase folding for the causal mask, Fig. 7).
+//
+// MI355X placement. The GPU has several L2 domains (XCDs); the L2 of one XCD is not
+// coherent with the others. A "group" is the set of CUs that cooperate on the dQ
+// tiles of one KV head: L lanes, L = n (naive, descending, shift) or n/2 (symmetric
+// shift, one lane per KV-tile pair). A group never straddles an XCD: if L exceeds
+// the CUs of one XCD, the group takes the whole XCD and each CU runs several lanes
+// one after another (the paper's "aggregate"). KV heads (units of one batch element
+// and one KV head) go to groups round-robin; a group runs its units one after
+// another. With grouped-query attention the G query heads that read one KV head are
+// visited innermost, so a KV tile's tasks stay contiguous.
+#include "schedule.h"
+
+#include <algorithm>
+#include <numeric>
+
+namespace dash {
+
+namespace {
+
+// Query tiles of KV tile i in ascending order (causal: only j >= i).
+std::vector<int> q_tiles(int n, int i, bool causal) {
+  std::vector<int> js;
+  for (int j = causal ? i : 0; j < n; ++j) js.push_back(j);
+  return js;
+}
+
+struct ItemBuild {
+  int b, g, i;
+  std::vector<int> js;  // Q tiles in visiting order
+};
+
+}  // namespace
+
+int build_table(const SchedParams& p, Table* out, std::string* err) {
+  if (p.B < 0 || p.N < 0 || p.H <= 0 || p.Hkv <= 0 || p.H % p.Hkv != 0 || p.tile <= 0 ||
+      p.num_xcd <= 0 || p.cus_per_xcd <= 0) {
+    *err = "invalid sizes";
+    return -1;
+  }
+  const int n = tiles_per_head(p.N, p.tile);
+  const int G = p.H / p.Hkv;
+  if (p.kind == Sched::Shift && p.causal) {
+    *err = "shift scheduling is defined for the full mask only";
+    return -2;
+  }
+  if (p.kind == Sched::SymShift && !p.causal) {
+    *err = "symmetric shift scheduling is defined for the causal mask only";
+    return -2;
+  }
+  if (p.kind == Sched::SymShift && (n % 2) != 0) {
+    *err = "symmetric shift needs an even number of tiles per head";
+    return -2;
+  }
+  const int X = p.num_xcd, S = p.cus_per_xcd;
+  Table& t = *out;
+  t = Table();
+  t.workers = X * S;
+  t.n = n;
+  t.tile = p.tile;
+  t.xcd_local = true;
+
+  std::vector<std::vector<ItemBuild>> lanes(t.workers);
+  const int U = p.B * p.Hkv;  // units: (batch, KV head)
+  if (U > 0 && n > 0) {
+    const int L = (p.kind == Sched::SymShift) ? n / 2 : n;
+    int C, per_xcd;
+    if (L <= S) {
+      C = L;
+      per_xcd = S / C;
+    } else {
+      C = S;
+      per_xcd = 1;
+    }
+    const int NG = X * per_xcd;
+    // group gamma -> XCD gamma % X, CU slots [(gamma / X) * C, + C)
+    auto worker_of = [&](int gamma, int c) {
+      const int xcd = gamma % X;
+      const int slot = (gamma / X) * C + c;
+      return xcd * S + slot;
+    };
+    for (int gamma = 0; gamma < NG && gamma < U; ++gamma) {
+      std::vector<int64_t> free_at(C, 0);  // descending: unit-cost finish time per lane
+      for (int u = gamma; u < U; u += NG) {
+        const int b = u / p.Hkv, g = u % p.Hkv;
+        switch (p.kind) {
+          case Sched::Naive:
+            for (int v = 0; v < L; ++v)
+              lanes[worker_of(gamma, v % C)].push_back({b, g, v, q_tiles(n, v, p.causal)});
+            break;
+          case Sched::Descending:
+            for (int i = 0; i < n; ++i) {
+              std::vector<int> js = q_tiles(n, i, p.causal);
+              std::reverse(js.begin(), js.end());
+              int best = 0;
+              for (int c = 1; c < C; ++c)
+                if (free_at[c] < free_at[best]) best = c;
+              free_at[best] += static_cast<int64_t>(js.size()) * G;
+              lanes[worker_of(gamma, best)].push_back({b, g, i, std::move(js)});
+            }
+            break;
+          case Sched::Shift:
+            for (int v = 0; v < L; ++v) {
+              std::vector<int> js(n);
+              for (int s = 0; s < n; ++s) js[s] = (v + s) % n;
+              lanes[worker_of(gamma, v % C)].push_back({b, g, v, std::move(js)});
+            }
+            break;
+          case Sched::SymShift: {
+            const int half = n / 2;
+            for (int pr = 0; pr < L; ++pr) {
+              const int w = worker_of(gamma, pr % C);
+              std::vector<int> first;  // KV tile pr: phase 1 rectangle, then left triangle
+              for (int s = 0; s < half; ++s) first.push_back(half + (pr + s) % half);
+              for (int j = pr; j < half; ++j) first.push_back(j);
+              std::vector<int> second;  // KV tile n-1-pr: right triangle bottom-up
+              for (int j = n - 1; j >= n - 1 - pr; --j) second.push_back(j);
+              lanes[w].push_back({b, g, pr, std::move(first)});
+              lanes[w].push_back({b, g, n - 1 - pr, std::move(second)});
+            }
+            break;
+          }
+        }
+      }
+    }
+  }
+
+  // Flatten in worker order, heads innermost.
+  t.worker_begin.assign(t.workers + 1, 0);
+  struct Pos {
+    int worker, pos;
+  };
+  std::vector<Pos> where;  // per task: worker and position in that worker's list
+  for (int w = 0; w < t.workers; ++w) {
+    t.worker_begin[w] = static_cast<int32_t>(t.items.size());
+    int pos = 0;
+    for (const ItemBuild& it : lanes[w]) {
+      t.items.push_back({it.b, it.g, it.i, static_cast<int32_t>(t.tasks.size())});
+      for (int j : it.js) {
+        for (int hh = 0; hh < G; ++hh) {
+          t.tasks.push_back({it.g * G + hh, j, -1, 0});
+          t.task_worker.push_back(w);
+          t.task_item.push_back(static_cast<int32_t>(t.items.size() - 1));
+          where.push_back({w, pos++});
+        }
+      }
+    }
+  }
+  t.worker_begin[t.workers] = static_cast<int32_t>(t.items.size());
+  t.items.push_back({0, 0, 0, static_cast<int32_t>(t.tasks.size())});
+
+  // Ranks. naive / descending: ascending KV tile ("ordered by CTA index").
+  // shift / symmetric shift: ascending timestamp = (position in the lane, lane).
+  const bool by_time = (p.kind == Sched::Shift || p.kind == Sched::SymShift);
+  const int64_t chains = static_cast<int64_t>(p.B) * p.H * n;
+  std::vector<std::vector<int32_t>> members(static_cast<size_t>(chains));
+  for (size_t k = 0; k < t.tasks.size(); ++k) {
+    const Item& it = t.items[t.task_item[k]];
+    const int64_t c = (static_cast<int64_t>(it.b) * p.H + t.tasks[k].h) * n + t.tasks[k].j;
+    members[static_cast<size_t>(c)].push_back(static_cast<int32_t>(k));
+  }
+  for (auto& m : members) {
+    if (by_time) {
+      std::sort(m.begin(), m.end(), [&](int32_t a, int32_t b) {
+        if (where[a].pos != where[b].pos) return where[a].pos < where[b].pos;
+        return where[a].worker < where[b].worker;
+      });
+    } else {
+      std::sort(m.begin(), m.end(), [&](int32_t a, int32_t b) {
+        return t.items[t.task_item[a]].i < t.items[t.task_item[b]].i;
+      });
+    }
+    const int cnt = static_cast<int>(m.size());
+    int xcd0 = -1;
+    for (int r = 0; r < cnt; ++r) {
+      t.tasks[m[r]].rank = r;
+      t.tasks[m[r]].last = (r == cnt - 1) ? 1 : 0;
+      const int xcd = t.task_worker[m[r]] / S;
+      if (xcd0 < 0) xcd0 = xcd;
+      if (xcd != xcd0) t.xcd_local = false;
+    }
+  }
+  return 0;
+}
+
+}  // namespace dash

@@ -1,0 +1,55 @@
+// Tile-to-CU schedule tables for the deterministic attention backward.
+//
+// DASH paper (arXiv 2601.21824), section 3: n KV tiles per head, each KV tile's
+// tasks (one per Q tile, and per query head of a grouped-query head group) run
+// back to back on one CU; the dQ tile of (batch, query head, Q tile) receives one
+// partial sum per contributing KV tile, in an order fixed by the schedule.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace dash {
+
+enum class Sched : int { Naive = 0, Descending = 1, Shift = 2, SymShift = 3 };
+
+struct SchedParams {
+  int B = 0, H = 0, Hkv = 0, N = 0;
+  int tile = 128;      // KV / Q tile edge in rows
+  bool causal = false;
+  Sched kind = Sched::Naive;
+  int num_xcd = 1;     // L2 domains
+  int cus_per_xcd = 1; // compute units per L2 domain
+};
+
+// One task: query head h, Q tile j, place `rank` in dQ tile (b, h, j)'s reduction
+// order; `last` = 1 when rank is the final place (that task writes the bf16 dQ).
+struct Task {
+  int32_t h, j, rank, last;
+};
+
+// One KV item: batch b, KV head g, KV tile i; its tasks are tasks[t0, next item's t0).
+struct Item {
+  int32_t b, g, i, t0;
+};
+
+struct Table {
+  int workers = 0;                  // num_xcd * cus_per_xcd
+  int n = 0;                        // tiles per head
+  int tile = 0;
+  bool xcd_local = true;            // every dQ tile's contributors share one L2 domain
+  std::vector<int32_t> worker_begin;  // workers + 1 entries into items
+  std::vector<Item> items;            // items.size() = real items + 1 sentinel (t0 = tasks.size())
+  std::vector<Task> tasks;
+  std::vector<int32_t> task_worker;   // worker of each task (for export)
+  std::vector<int32_t> task_item;     // item of each task (for export)
+};
+
+// Number of tiles per head for sequence length N and tile edge `tile`.
+inline int tiles_per_head(int N, int tile) { return (N + tile - 1) / tile; }
+
+// Builds the table. Returns 0 on success, or a dash_status code with a message in *err.
+int build_table(const SchedParams& p, Table* out, std::string* err);
+
+}  // namespace dash

@@ -1,0 +1,140 @@
+"""ctypes binding of the C ABI in include/dash.h (argument marshalling only).
+
+Every function here has the name of the C entry point it calls. The HIP library
+must be built (scheduling_fa_attn_amd/build.py); loading fails loudly when it is
+missing. PyTorch is used only to hand device pointers and the current stream to
+the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH
+
+DASH_OK = 0
+DASH_ERR_INVALID_ARG = -1
+DASH_ERR_UNSUPPORTED = -2
+DASH_ERR_WORKSPACE = -3
+DASH_ERR_NOT_CORESIDENT = -4
+DASH_ERR_HIP = -5
+DASH_ERR_TIMEOUT = -6
+DASH_ERR_PLACEMENT = -7
+
+MASKS = {"full": 0, "causal": 1}
+SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "sym_shift": 3}
+
+EXPORTED = (
+    "dash_attn_bwd_workspace_size",
+    "dash_attn_bwd",
+    "dash_attn_bwd_timed",
+    "dash_last_kernel_error",
+    "dash_status_string",
+    "dash_tile_size",
+    "dash_schedule_table",
+)
+
+_lib = None
+
+
+class DashError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        super().__init__(f"{what}: {dash_status_string(status)} ({status})" if what else dash_status_string(status))
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"HIP library {path} is not built; run scheduling_fa_attn_amd/build.py "
+                           "or __graft_entry__.build()")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.dash_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]
+    lib.dash_attn_bwd_workspace_size.restype = sz
+    common = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
+    lib.dash_attn_bwd.argtypes = common
+    lib.dash_attn_bwd.restype = i
+    lib.dash_attn_bwd_timed.argtypes = common + [vp, vp]
+    lib.dash_attn_bwd_timed.restype = i
+    lib.dash_last_kernel_error.argtypes = []
+    lib.dash_last_kernel_error.restype = i
+    lib.dash_status_string.argtypes = [i]
+    lib.dash_status_string.restype = ctypes.c_char_p
+    lib.dash_tile_size.argtypes = [i]
+    lib.dash_tile_size.restype = i
+    lib.dash_schedule_table.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), ctypes.c_longlong,
+                                        ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
+    lib.dash_schedule_table.restype = i
+    _lib = lib
+    return lib
+
+
+def dash_status_string(status: int) -> str:
+    return load().dash_status_string(int(status)).decode()
+
+
+def dash_attn_bwd_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    return int(load().dash_attn_bwd_workspace_size(B, H, Hkv, N, d))
+
+
+def dash_tile_size(N: int) -> int:
+    return int(load().dash_tile_size(N))
+
+
+def dash_last_kernel_error() -> int:
+    return int(load().dash_last_kernel_error())
+
+
+def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):
+    """Host-only table export: returns (records [T, 7] int32, xcd_local)."""
+    lib = load()
+    m = MASKS.get(mask, mask)
+    s = SCHEDULES.get(schedule, schedule)
+    count = ctypes.c_longlong(0)
+    local = ctypes.c_int(0)
+    st = lib.dash_schedule_table(B, H, Hkv, N, m, s, num_xcd, cus_per_xcd, None, 0, ctypes.byref(count),
+                                 ctypes.byref(local))
+    if st not in (DASH_OK, DASH_ERR_WORKSPACE):
+        raise DashError(st, "dash_schedule_table")
+    rec = np.zeros((max(count.value, 1), 7), dtype=np.int32)
+    st = lib.dash_schedule_table(B, H, Hkv, N, m, s, num_xcd, cus_per_xcd,
+                                 rec.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), count.value,
+                                 ctypes.byref(count), ctypes.byref(local))
+    if st != DASH_OK:
+        raise DashError(st, "dash_schedule_table")
+    return rec[: count.value], bool(local.value)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def dash_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, softmax_scale, mask, schedule, deterministic, workspace,
+                  stream=None, main_start=None, main_stop=None) -> int:
+    """Call dash_attn_bwd (or dash_attn_bwd_timed when events are given) on torch device tensors.
+
+    q, o, dO, dq: [B, H, N, d] bf16; k, v, dk, dv: [B, Hkv, N, d] bf16; lse: [B, H, N] fp32;
+    workspace: a uint8 device tensor of at least dash_attn_bwd_workspace_size bytes.
+    Returns the status code (0 = success); nothing is checked here beyond marshalling.
+    """
+    import torch
+
+    lib = load()
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+            B, H, Hkv, N, d, float(softmax_scale), MASKS.get(mask, mask), SCHEDULES.get(schedule, schedule),
+            int(deterministic), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            ctypes.c_void_p(stream)]
+    if main_start is not None or main_stop is not None:
+        return int(lib.dash_attn_bwd_timed(*args, ctypes.c_void_p(main_start or 0),
+                                           ctypes.c_void_p(main_stop or 0)))
+    return int(lib.dash_attn_bwd(*args))

@@ -1,0 +1,75 @@
+"""The C-ABI library loads, exports every entry point of include/dash.h, and rejects bad
+arguments before touching the GPU (these calls return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from scheduling_fa_attn_amd import dash
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dash.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dash_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = dash.load()
+    names = header_functions()
+    assert set(names) == set(dash.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        assert dash.dash_status_string(code) != "unknown status"
+    assert dash.dash_status_string(42) == "unknown status"
+
+
+def test_workspace_size():
+    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64) >= 1 * 2 * 256 * 64 * 4
+    assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 96) == 0
+    assert dash.dash_attn_bwd_workspace_size(1, 3, 2, 256, 64) == 0
+
+
+def _call(**kw):
+    lib = dash.load()
+    args = dict(q=1 << 12, k=1 << 12, v=1 << 12, o=1 << 12, dO=1 << 12, lse=1 << 12, dq=1 << 12, dk=1 << 12,
+                dv=1 << 12, B=1, H=2, Hkv=2, N=256, d=64, scale=0.125, mask=0, schedule=0, det=1,
+                ws=1 << 12, ws_bytes=0, stream=None)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.dash_attn_bwd(*(vp(args[k]) for k in ("q", "k", "v", "o", "dO", "lse", "dq", "dk", "dv")),
+                             args["B"], args["H"], args["Hkv"], args["N"], args["d"], args["scale"],
+                             args["mask"], args["schedule"], args["det"], vp(args["ws"]), args["ws_bytes"],
+                             vp(args["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), dash.DASH_ERR_UNSUPPORTED),
+    (dict(H=3), dash.DASH_ERR_INVALID_ARG),
+    (dict(Hkv=0), dash.DASH_ERR_INVALID_ARG),
+    (dict(mask=2), dash.DASH_ERR_INVALID_ARG),
+    (dict(schedule=4), dash.DASH_ERR_INVALID_ARG),
+    (dict(mask=1, schedule=2), dash.DASH_ERR_UNSUPPORTED),
+    (dict(mask=0, schedule=3), dash.DASH_ERR_UNSUPPORTED),
+    (dict(det=2), dash.DASH_ERR_INVALID_ARG),
+    (dict(scale=0.0), dash.DASH_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), dash.DASH_ERR_INVALID_ARG),
+    (dict(q=None), dash.DASH_ERR_INVALID_ARG),
+    (dict(dq=(1 << 12) + 2), dash.DASH_ERR_INVALID_ARG),
+    (dict(ws=None), dash.DASH_ERR_INVALID_ARG),
+    (dict(ws_bytes=16), dash.DASH_ERR_WORKSPACE),
+])
+def test_argument_errors_before_any_launch(kw, status):
+    assert _call(**kw) == status
+
+
+def test_empty_inputs_are_a_no_op():
+    assert _call(B=0, q=None, ws=None) == dash.DASH_OK
+    assert _call(N=0, q=None, ws=None) == dash.DASH_OK
