@@ -9,38 +9,66 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libdash_mi355x.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
-SOURCES = [
-    os.path.join(HERE, "csrc", "bwd_kernels.hip"),
-    os.path.join(HERE, "csrc", "dash_api.cpp"),
-    os.path.join(HERE, "csrc", "schedule.cpp"),
-]
+# Profiling build (-DDASH_PROFILE): the main kernel also records per-wave phase cycle
+# counters, exported through dash_profile_attach. Not used by the default path.
+PROF_LIB_PATH = os.path.join(HERE, "libdash_mi355x_prof.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+BUILD_DIR = os.path.join(ROOT, "_build")
 
 # Packed fp32 instructions are kept out of the generated code (the leading '-'
 # disables the target feature).
-FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+COMMON = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I" + os.path.join(ROOT, "include"), "-I" + os.path.join(HERE, "csrc"),
 ]
+# MFMA results of the 4-wave main kernel are allocated in VGPRs (-amdgpu-mfma-vgpr-form):
+# the softmax reads them with VALU instructions, which cannot read AGPRs, so AGPR
+# results would need a copy each. (The 2-wave kernel keeps the default: this LLVM
+# crashes on it with the option.)
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+# (source, extra flags, object name)
+MAIN_FLAGS = {(64, 4): VGPR_FORM, (128, 4): [], (64, 2): [], (128, 2): []}
+UNITS = [
+    ("bwd_main.hip", [f"-DDASH_MAIN_D={d}", f"-DDASH_MAIN_NW={nw}"] + fl, f"bwd_main_d{d}_nw{nw}.o")
+    for (d, nw), fl in MAIN_FLAGS.items()
+] + [
+    ("aux_kernels.hip", [], "aux_kernels.o"),
+    ("dash_api.cpp", [], "dash_api.o"),
+    ("schedule.cpp", [], "schedule.o"),
+]
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    """Compile every source into LIB_PATH (always recompiles); returns the library path."""
-    tmp = LIB_PATH + ".tmp"
-    cmd = [HIPCC] + FLAGS + (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else [])
-    cmd += ["-x", "hip"] + SOURCES + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose or resource_usage:
-        sys.stderr.write(res.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+        raise RuntimeError(f"hipcc failed with exit code {res.returncode}: {' '.join(cmd)}")
+    return res
+
+
+def build(verbose: bool = False, resource_usage: bool = False, profile: bool = False) -> str:
+    """Compile every source and link LIB_PATH (PROF_LIB_PATH with profile=True; always
+    recompiles); returns the library path."""
+    out = PROF_LIB_PATH if profile else LIB_PATH
+    tag = "prof" if profile else "rel"
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    extra = (["-DDASH_PROFILE"] if profile else []) + (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else [])
+    objs = []
+    for src, flags, obj in UNITS:
+        o = os.path.join(BUILD_DIR, tag + "_" + obj)
+        res = _run([HIPCC] + COMMON + flags + extra + ["-c", "-x", "hip", os.path.join(HERE, "csrc", src), "-o", o],
+                   verbose)
+        if resource_usage:
+            sys.stderr.write(res.stderr)
+        objs.append(o)
+    tmp = out + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    build(verbose=True, resource_usage="--resource-usage" in sys.argv)
+    build(verbose=True, resource_usage="--resource-usage" in sys.argv, profile="--profile" in sys.argv)

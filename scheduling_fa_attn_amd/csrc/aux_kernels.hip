@@ -1,0 +1,95 @@
+// Auxiliary HIP kernels of the attention backward for gfx950: the preprocess
+// (D = rowsum(dO * O), -LSE*log2(e), clearing), the dQ cast of the atomic variant and
+// the XCD topology probe.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace dash {
+
+// ---------------------------------------------------------------------------------
+// Preprocess: D[row] = sum_e dO[row, e] * O[row, e] in fp32 with a fixed reduction
+// tree and nl[row] = -LSE[row] * log2(e); clears the ordering semaphores and the XCD
+// slot counters; for the atomic variant also clears the fp32 dQ accumulator.
+// ---------------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
+  constexpr int LPR = D / 8;  // lanes per row, 8 elements (16 bytes) per lane
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  const int64_t rows = p.rows;
+  for (int64_t base = tid; base < rows * LPR; base += nthreads) {
+    const int64_t row = base / LPR;
+    const int part = static_cast<int>(base % LPR);
+    const bf16x8 ov = *reinterpret_cast<const bf16x8*>(p.o + row * D + part * 8);
+    const bf16x8 dv = *reinterpret_cast<const bf16x8*>(p.dO + row * D + part * 8);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_fmaf(static_cast<float>(ov[e]), static_cast<float>(dv[e]), acc);
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, LPR);
+    if (part == 0) {
+      p.delta[row] = acc;
+      p.nlse2[row] = -p.lse[row] * 1.4426950408889634f;
+    }
+  }
+  for (int64_t x = tid; x < p.sem_count; x += nthreads) p.sem[x] = 0;
+  for (int64_t x = tid; x < p.ctr_count; x += nthreads) p.ctr[x] = 0;
+  if (p.dqacc_zero) {
+    floatx4* z = reinterpret_cast<floatx4*>(p.dqacc_zero);
+    const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t x = tid; x < p.zero_count / 4; x += nthreads) z[x] = zero;
+  }
+}
+
+// dQ = bf16(s * dQacc), for the atomic variant (the ordered variant writes dQ from
+// the last contributor of each tile).
+__global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
+                                                      int64_t count, float scale) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t x = tid; x < count / 4; x += nthreads) {
+    const floatx4 a = reinterpret_cast<const floatx4*>(acc)[x];
+    bf16x4 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) r[e] = static_cast<bf16>(a[e] * scale);
+    reinterpret_cast<bf16x4*>(dq)[x] = r;
+  }
+}
+
+// Records the XCD of every workgroup of a one-workgroup-per-CU grid.
+__global__ void __launch_bounds__(64) topology_probe_kernel(int* out) {
+  if (threadIdx.x == 0) out[blockIdx.x] = static_cast<int>(xcc_id());
+}
+
+hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t stream) {
+  if (d == 64) {
+    hipLaunchKernelGGL(preprocess_kernel<64>, dim3(grid), dim3(256), 0, stream, prm);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(preprocess_kernel<128>, dim3(grid), dim3(256), 0, stream, prm);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_cast(const float* acc, void* dq, int64_t count, float scale, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(dq_cast_kernel, dim3(grid), dim3(256), 0, stream, acc, reinterpret_cast<bf16*>(dq), count,
+                     scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream) {
+  // Same LDS footprint class as the main kernel: one workgroup per CU.
+  const int shmem = 83 * 1024;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(topology_probe_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+  if (e != hipSuccess) return e;
+  void* args[] = {&out};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(topology_probe_kernel), dim3(grid), dim3(64),
+                                    args, shmem, stream);
+}
+
+}  // namespace dash

@@ -1,0 +1,466 @@
+// Main HIP kernel of the deterministic attention backward for gfx950 (MI355X).
+//
+// This file is compiled once per head dimension and workgroup size (DASH_MAIN_D =
+// 64 or 128, DASH_MAIN_NW = 2 or 4 waves).
+//
+// Math (DASH paper, arXiv 2601.21824, section 2.1; "Writing an Attention Kernel",
+// section "In the real world"): per (batch b, query head h, key/value head g):
+//   P  = exp(s Q K^T - LSE)   (recomputed, masked entries 0)
+//   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D)
+//   dK = s dS^T Q,  dQ = s dS K
+// Work decomposition (section 2.1, Fig. 1 left; section 3.1): a workgroup owns one
+// KV tile at a time and keeps its dK/dV in registers while it visits Q tiles; the
+// dQ partial sum of every visit goes to an fp32 accumulator in global memory,
+// added in the order the schedule table fixes (ordered reduction, section 1) or
+// with float atomics (the non-deterministic variant kept for comparison).
+//
+// CDNA4 mapping of the main kernel
+// - One workgroup of NW waves per CU, persistent (one workgroup per CU, each reads
+//   its task list from the schedule table). The workgroup learns its XCD from the
+//   hardware (XCC_ID) and takes the next free slot of that XCD, so the table's CU
+//   groups are CUs that share one L2.
+// - KV tile = 32*NW rows; wave w owns KV rows [32w, 32w+32): their dK, dV (fp32) stay
+//   in AGPR/VGPR accumulators for the whole item, and their K, V rows sit in
+//   registers as MFMA B operands. Q tiles are visited in 64-row steps.
+// - Q, dO (64 x d), -LSE*log2(e) and D of the next step are copied global -> LDS with
+//   global_load_lds_dwordx4 while the current step computes (double buffer).
+// - All five contractions use v_mfma_f32_32x32x16_bf16. Operand layouts (A: lane
+//   holds row lane%32, 8 consecutive k; B: column lane%32, 8 consecutive k; D:
+//   column lane%32, rows 8*(r/4) + 4*(lane/32) + r%4):
+//     S  = Q K^T    A = Q (ds_read_b128 from LDS), B = K (registers)
+//     dP = dO V^T   A = dO (LDS), B = V (registers)
+//     dV += P^T dO  A = P (registers, straight from the S accumulators), B = dO read
+//                   with ds_read_b64_tr_b16 (LDS transpose read), rows permuted
+//                   the same way as P's accumulator rows
+//     dK += dS^T Q  likewise with dS and Q
+//     dQ = dS K     A = dS via an LDS round trip (stored [kv][q], read transposed),
+//                   B = K read transposed from the item's K tile in LDS
+// - LDS tiles are XOR-swizzled in 16-byte chunks so that both the row reads
+//   (ds_read_b128) and the transpose reads hit distinct banks.
+// - The dQ partial of a 64-row step is split over the waves by 32-column blocks;
+//   every wave waits for and passes on its own turn (one semaphore per step and
+//   wave), so the ordered reduction needs no workgroup barrier.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.h"
+#include "kernels.h"
+
+#if !defined(DASH_MAIN_NW) || !defined(DASH_MAIN_D)
+#error "DASH_MAIN_D (64 or 128) and DASH_MAIN_NW (2 or 4) must be defined"
+#endif
+
+namespace dash {
+
+// ---------------------------------------------------------------------------------
+// Main backward kernel.
+// ---------------------------------------------------------------------------------
+template <int D, int NW>
+struct BwdCfg {
+  static constexpr int BC = 32 * NW;    // KV (and Q) tile rows
+  static constexpr int BQ = 64;         // Q rows per step
+  static constexpr int SUBS = BC / BQ;  // steps per task
+  static constexpr int NT = NW * 64;    // threads
+  static constexpr int DB = D / 32;     // 32-column blocks of d
+  static constexpr int DK = D / 16;     // k-steps over d
+  static constexpr int KK = BC / 16;    // k-steps over the KV tile
+  static constexpr int ST = TileGeom<D>::STRIDE;         // LDS row stride of Q, dO, K tiles
+  static constexpr int NBLK = 2 * DB / NW;               // 32x32 dQ blocks per wave
+  static constexpr int NKD = DB / NW > 1 ? DB / NW : 1;  // distinct d blocks per wave
+  static constexpr int QT = BQ * ST;                     // bytes of one Q (or dO) tile
+  static constexpr int DST = BC * kDsStride;             // bytes of one dS^T tile [BC][64]
+  static constexpr int OFF_Q = 0;                        // 2 buffers
+  static constexpr int OFF_DO = OFF_Q + 2 * QT;          // 2 buffers
+  static constexpr int OFF_DS = OFF_DO + 2 * QT;         // 2 buffers
+  static constexpr int OFF_K = OFF_DS + 2 * DST;         // K tile [BC][D]
+  static constexpr int OFF_NL = OFF_K + BC * ST;         // 2 x 64 floats
+  static constexpr int OFF_DL = OFF_NL + 2 * 256;        // 2 x 64 floats
+  static constexpr int OFF_MISC = OFF_DL + 2 * 256;
+  static constexpr int BYTES = OFF_MISC + 64;
+  static_assert(NBLK >= 1 && NBLK * NW == 2 * DB, "dQ blocks must split evenly over waves");
+  static_assert(SUBS >= 1 && SUBS * BQ == BC, "KV tile must be a multiple of 64 rows");
+  static_assert(QT % 1024 == 0 && DST % 1024 == 0 && (BC * ST) % 1024 == 0, "1 KiB-aligned tiles");
+};
+
+template <int D, int NW>
+__global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+bwd_main_kernel(BwdParams p) {
+  using C = BwdCfg<D, NW>;
+  constexpr int BC = C::BC, BQ = C::BQ, SUBS = C::SUBS, DB = C::DB, DK = C::DK, KK = C::KK, ST = C::ST;
+  extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
+  LDS_AS char* smem = (LDS_AS char*)smem_raw;
+  LDS_AS int* sMisc = reinterpret_cast<LDS_AS int*>(smem + C::OFF_MISC);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int hi = lane >> 5;
+  const int L16 = lane & 15;
+  const int nb = (lane >> 4) & 1;
+
+  // Worker slot: XCD from hardware, slot = arrival order within that XCD.
+  if (tid == 0) {
+    unsigned x = (p.num_xcd == 1) ? 0u : xcc_id();
+    int v = -1;
+    if (x < static_cast<unsigned>(p.num_xcd)) {
+      const int slot = atomicAdd(p.ctr + x * 64, 1);
+      if (slot < p.cus_per_xcd) v = static_cast<int>(x) * p.cus_per_xcd + slot;
+    }
+    if (v < 0) raise_error(p.err, kErrPlacement);
+    sMisc[0] = v;
+  }
+  __syncthreads();
+  const int worker = sMisc[0];
+  if (worker < 0) return;
+
+  PROF_DECL
+  const int H = p.H, Hkv = p.Hkv, N = p.N;
+  const bool cross = !p.xcd_local;
+  bool failed = false;  // this wave gave up waiting (error reported); it keeps going without reducing
+  // The schedule table is read-only for the whole launch: reading it through the
+  // constant address space turns its uniform loads into scalar loads, which are
+  // counted apart from the vector-memory queue that the global->LDS copies use.
+  const CONST_AS int* worker_begin = (const CONST_AS int*)p.worker_begin;
+  const CONST_AS Quad* items = (const CONST_AS Quad*)p.items;
+  const CONST_AS Quad* tasks = (const CONST_AS Quad*)p.tasks;
+  const int it_begin = worker_begin[worker];
+  const int it_end = worker_begin[worker + 1];
+
+  // Per-lane parts of the LDS addresses (the rest is a compile-time offset).
+  // S, dP A operands: row pi(l32) (+32 qb), chunk hi (+2 ks).
+  const int a_lane = pi16(l32) * ST + 16 * hi;
+  // dV, dK B operands (transpose reads): row pi(16 hf + 8 s + 4 hi + j) - 16 hf - 2 s
+  // = hi + 4 j, column 16 nb + 4 (L16 % 4) (+32 db).
+  const int bt_lane = (hi + 4 * (L16 >> 2)) * ST + 2 * (16 * nb + 4 * (L16 & 3));
+  // dQ contraction: KV row 16 kk + 2 hi + s + 4 j, column 16 nb + 4 (L16 % 4) (+32 qb or +32 db).
+  const int kvrow_lane = 2 * hi + 4 * (L16 >> 2);
+  const int col_lane2 = 2 * (16 * nb + 4 * (L16 & 3));
+  const int ds_rd_lane = kvrow_lane * kDsStride + col_lane2;
+  const int kd_lane = kvrow_lane * ST + col_lane2;
+  // dS^T store: row 32 w + l32, bytes 8 hi (+16 t + 64 qb).
+  const int ds_wr_lane = (32 * w + l32) * kDsStride + 8 * hi;
+
+  LDS_AS char* sK = smem + C::OFF_K;
+
+  for (int it = it_begin; it < it_end; ++it) {
+    const Quad item = load_quad(items, it);
+    const int b = item.x, g = item.y, kv_tile = item.z;
+    const int t_begin = item.w, t_end = load_quad(items, it + 1).w;
+    const int n_steps = (t_end - t_begin) * SUBS;
+    const int kv0 = kv_tile * BC;
+    const int64_t bg = static_cast<int64_t>(b) * Hkv + g;
+    const bf16* Kg = p.k + bg * N * D;
+    const bf16* Vg = p.v + bg * N * D;
+
+    // Issues the global->LDS copies of step s (Q, dO, -LSE*log2e, D) into buffer s & 1.
+    auto issue_step = [&](int s) __attribute__((always_inline)) {
+      const Quad task = load_quad(tasks, t_begin + s / SUBS);
+      const int q0 = task.y * BC + (s % SUBS) * BQ;
+      const int64_t bh = static_cast<int64_t>(b) * H + task.x;
+      const int buf = s & 1;
+      dma_tile<D, BQ, NW>(smem + C::OFF_Q + buf * C::QT, p.q + bh * N * D, q0, N, w, lane);
+      dma_tile<D, BQ, NW>(smem + C::OFF_DO + buf * C::QT, p.dO + bh * N * D, q0, N, w, lane);
+      if (w == 0) dma_row64(smem + C::OFF_NL + buf * 256, p.nlse2 + bh * N, q0, N, lane);
+      if (w == 1) dma_row64(smem + C::OFF_DL + buf * 256, p.delta + bh * N, q0, N, lane);
+    };
+
+    // Item prologue: K tile to LDS, first step's tiles, K/V rows of this wave to registers.
+    dma_tile<D, BC, NW>(sK, Kg, kv0, N, w, lane);
+    issue_step(0);
+    bf16x8 kreg[DK], vreg[DK];
+    {
+      const int kvr = kv0 + 32 * w + l32;
+      const bool ok = kvr < N;
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        bf16x8 kz = {}, vz = {};
+        if (ok) {
+          kz = *reinterpret_cast<const bf16x8*>(Kg + static_cast<int64_t>(kvr) * D + ks * 16 + 8 * hi);
+          vz = *reinterpret_cast<const bf16x8*>(Vg + static_cast<int64_t>(kvr) * D + ks * 16 + 8 * hi);
+        }
+        kreg[ks] = kz;
+        vreg[ks] = vz;
+      }
+    }
+    floatx16 accK[DB], accV[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      accK[db] = floatx16{};
+      accV[db] = floatx16{};
+    }
+    wait_mem_done();
+    __syncthreads();
+    const int kvcol = kv0 + 32 * w + l32;  // this lane's KV row in S, P, dP, dS
+    PROF_MARK(kProfItem);
+
+    // dQ partial of step `ps` (its dS^T is in LDS buffer ps & 1) = dS K, this wave's
+    // 32x32 blocks; accumulator row m of block qb is Q row q0 + pi(32 qb + m).
+    auto dq_partial = [&](int ps, floatx16 (&dq)[C::NBLK]) __attribute__((always_inline)) {
+      const LDS_AS char* sdSp = smem + C::OFF_DS + (ps & 1) * C::DST;
+#pragma unroll
+      for (int t2 = 0; t2 < C::NBLK; ++t2) {
+        const int blk = w + NW * t2;
+        const int qb = blk / DB, db = blk % DB;
+        floatx16 acc = {};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * qb;
+          const bf16x8 a = join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
+          const int koff = kd_lane + 16 * kk * ST + 64 * db;
+          const bf16x8 bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
+          acc = mfma32(a, bk, acc);
+        }
+        dq[t2] = acc;
+      }
+    };
+    // Byte offset (within the head) of element r of this wave's dQ block t2 at step q0.
+    auto dq_off = [&](int q0s, int t2, int r) __attribute__((always_inline)) {
+      const int blk = w + NW * t2;
+      const int qb = blk / DB, db = blk % DB;
+      return (q0s + pi16(qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3))) * D + db * 32 + l32;
+    };
+
+    // Reduction of step ps's dQ partial, in three parts so that its memory latency
+    // overlaps the next step's work: (1) wait for the turn and issue the accumulator
+    // loads, (2) add and store, (3) after the stores are acknowledged, pass the turn on.
+    struct Pending {
+      int rank, last, q0;
+      int* sem;
+      float* acc_g;
+      bf16* dq_g;
+      bool go;
+    };
+    auto reduce_begin = [&](int ps, float (&ld)[C::NBLK][16]) __attribute__((always_inline)) -> Pending {
+      const Quad task = load_quad(tasks, t_begin + ps / SUBS);
+      Pending pd;
+      pd.rank = task.z;
+      pd.last = task.w;
+      pd.q0 = task.y * BC + (ps % SUBS) * BQ;
+      const int64_t bh = static_cast<int64_t>(b) * H + task.x;
+      pd.acc_g = p.dqacc + bh * N * D;
+      pd.dq_g = p.dq + bh * N * D;
+      pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
+      pd.go = !failed;
+      if (p.deterministic && pd.go && pd.rank > 0) {
+        if (cross) {
+          pd.go = wait_turn(pd.sem, pd.rank, p.err, p.timeout_ticks, true);
+        } else {
+          pd.go = wait_turn_local(pd.sem, pd.rank, p.err, p.timeout_ticks);
+        }
+        failed = !pd.go;
+      }
+      PROF_MARK(kProfWait);
+      if (p.deterministic && pd.go && pd.rank > 0) {
+        const rsrc_t rs = make_rsrc(pd.acc_g, N * D * 4);
+#pragma unroll
+        for (int t2 = 0; t2 < C::NBLK; ++t2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ld[t2][r] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * dq_off(pd.q0, t2, r), 0, kSC1));
+      } else {
+#pragma unroll
+        for (int t2 = 0; t2 < C::NBLK; ++t2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ld[t2][r] = 0.f;
+      }
+      return pd;
+    };
+    auto reduce_store = [&](const Pending& pd, const floatx16 (&dq)[C::NBLK], const float (&ld)[C::NBLK][16])
+        __attribute__((always_inline)) {
+      if (!pd.go) return;
+      if (!p.deterministic) {
+#pragma unroll
+        for (int t2 = 0; t2 < C::NBLK; ++t2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int off = dq_off(pd.q0, t2, r);
+            if (off < N * D) atomicAdd(pd.acc_g + off, dq[t2][r]);
+          }
+      } else if (pd.last) {
+        const rsrc_t rs = make_rsrc(pd.dq_g, N * D * 2);
+#pragma unroll
+        for (int t2 = 0; t2 < C::NBLK; ++t2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const bf16 v = static_cast<bf16>((ld[t2][r] + dq[t2][r]) * p.scale);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs,
+                                                  2 * dq_off(pd.q0, t2, r), 0, 0);
+          }
+      } else {
+        const rsrc_t rs = make_rsrc(pd.acc_g, N * D * 4);
+#pragma unroll
+        for (int t2 = 0; t2 < C::NBLK; ++t2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, ld[t2][r] + dq[t2][r]), rs,
+                                                  4 * dq_off(pd.q0, t2, r), 0, 0);
+      }
+    };
+    // Call after wait_mem_done(): this wave's accumulator stores are in the L2.
+    auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
+      if (!p.deterministic || !pd.go || pd.last) return;
+      if (cross) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (lane == 0) {
+        if (cross)
+          __hip_atomic_store(pd.sem, pd.rank + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          __hip_atomic_store(pd.sem, pd.rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    };
+
+    for (int s = 0; s < n_steps; ++s) {
+      PROF_COUNT(kProfSteps);
+      const int buf = s & 1;
+      const Quad task = load_quad(tasks, t_begin + s / SUBS);
+      const int j = task.y;
+      const int q0 = j * BC + (s % SUBS) * BQ;
+
+      // Previous step's dQ partial and the first half of its reduction.
+      floatx16 dq[C::NBLK];
+      float ld[C::NBLK][16];
+      Pending pd;
+      const bool have_prev = s > 0;
+      if (have_prev) {
+        dq_partial(s - 1, dq);
+        PROF_MARK(kProfDq);
+        pd = reduce_begin(s - 1, ld);
+      }
+      // The next step's copies go after the accumulator loads: waiting for those
+      // loads must not wait for the copies (the vector-memory counter is in order).
+      if (s + 1 < n_steps) issue_step(s + 1);
+
+      const LDS_AS char* sQ = smem + C::OFF_Q + buf * C::QT;
+      const LDS_AS char* sdO = smem + C::OFF_DO + buf * C::QT;
+      const LDS_AS char* sNL = smem + C::OFF_NL + buf * 256;
+      const LDS_AS char* sDL = smem + C::OFF_DL + buf * 256;
+      LDS_AS char* sdS = smem + C::OFF_DS + buf * C::DST;
+      const bool need_mask = (p.causal && j == kv_tile) || (kv0 + BC > N) || (q0 + BQ > N);
+
+      // One 32-row block of the step at a time keeps S, dP, P, dS of a single 32 x 32
+      // block live. Accumulator row m of the block is Q row pi(m).
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        // S = Q K^T and dP = dO V^T for this wave's 32 KV columns.
+        floatx16 S = {}, dP = {};
+#pragma unroll
+        for (int ks = 0; ks < DK; ++ks) {
+          const int off = a_lane + 32 * qb * ST + 32 * ks;
+          S = mfma32(lds_ld16(sQ, off), kreg[ks], S);
+          dP = mfma32(lds_ld16(sdO, off), vreg[ks], dP);
+        }
+        if (qb == 0 && have_prev) reduce_store(pd, dq, ld);
+        if (need_mask) {
+          // Masked entries (key after query, or row/column past N) get S = -inf, so
+          // that P = exp2(-inf) = 0 and dS = 0.
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qg = q0 + pi16(qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3));
+            if ((p.causal && kvcol > qg) || kvcol >= N || qg >= N) S[r] = -__builtin_inff();
+          }
+        }
+        // P = exp2(s log2(e) S - LSE log2(e)), dS = P (dP - D); rounded to bf16.
+        bf16x8 Pb[2], dSb[2];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int mrow = qb * 32 + 8 * t + 4 * hi;  // accumulator rows mrow .. mrow+3
+          const floatx4 nl = *reinterpret_cast<const LDS_AS floatx4*>(sNL + mrow * 4);
+          const floatx4 dl = *reinterpret_cast<const LDS_AS floatx4*>(sDL + mrow * 4);
+          bf16x4 v4;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * t + e;
+            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, nl[e]));
+            const float ds = pr * (dP[r] - dl[e]);
+            Pb[r >> 3][r & 7] = static_cast<bf16>(pr);
+            dSb[r >> 3][r & 7] = static_cast<bf16>(ds);
+            v4[e] = dSb[r >> 3][r & 7];
+          }
+          // dS^T of this wave's 32 KV rows to LDS ([kv][m]).
+          *reinterpret_cast<LDS_AS bf16x4*>(sdS + ds_wr_lane + 64 * qb + 16 * t) = v4;
+        }
+        // dV += P^T dO, dK += dS^T Q. The 8 k-values of k-step hf are accumulator
+        // rows 16hf + 4hi + {0..3} and 16hf + 8 + 4hi + {0..3}: Q/dO rows
+        // 16hf + hi + 4j and 16hf + 2 + hi + 4j.
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const int off = bt_lane + (32 * qb + 16 * hf) * ST + 64 * db;
+            const bf16x8 bo = join(lds_tr(sdO, off), lds_tr(sdO, off + 2 * ST));
+            const bf16x8 bq = join(lds_tr(sQ, off), lds_tr(sQ, off + 2 * ST));
+            accV[db] = mfma32(Pb[hf], bo, accV[db]);
+            accK[db] = mfma32(dSb[hf], bq, accK[db]);
+          }
+        }
+      }
+      PROF_MARK(kProfBody);
+      wait_mem_done();  // next step's tiles landed, previous step's dQ stores acknowledged
+      if (have_prev) reduce_signal(pd);
+      PROF_MARK(kProfReduce);
+      __syncthreads();  // dS^T of all waves and the next step's tiles are visible
+      PROF_MARK(kProfBarrier);
+    }
+    // The item's last step: its dQ partial and reduction.
+    {
+      floatx16 dq[C::NBLK];
+      float ld[C::NBLK][16];
+      dq_partial(n_steps - 1, dq);
+      PROF_MARK(kProfDq);
+      const Pending pd = reduce_begin(n_steps - 1, ld);
+      reduce_store(pd, dq, ld);
+      wait_mem_done();
+      reduce_signal(pd);
+      PROF_MARK(kProfReduce);
+    }
+
+    // Epilogue: dK = s dK, dV; bf16 stores of this wave's 32 KV rows.
+    bf16* dKg = p.dk + bg * N * D;
+    bf16* dVg = p.dv + bg * N * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kvr = kv0 + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
+        if (kvr < N) {
+          const int off = kvr * D + db * 32 + l32;
+          dKg[off] = static_cast<bf16>(accK[db][r] * p.scale);
+          dVg[off] = static_cast<bf16>(accV[db][r]);
+        }
+      }
+    }
+    // Every wave is done with this item's LDS (K tile, last step's buffers) before
+    // the next item's copies overwrite it.
+    __syncthreads();
+    PROF_MARK(kProfItem);
+  }
+  PROF_STORE(p, w, NW);
+}
+
+// ---------------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------------
+template <int D, int NW>
+static hipError_t launch_main_t(const BwdParams& prm, int grid, hipStream_t stream) {
+  using C = BwdCfg<D, NW>;
+  // At least 81 KiB of LDS so that exactly one workgroup fits on a CU.
+  const int shmem = C::BYTES > 83 * 1024 ? C::BYTES : 83 * 1024;
+  auto fn = bwd_main_kernel<D, NW>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
+  if (e != hipSuccess) return e;
+  BwdParams local = prm;
+  void* args[] = {&local};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(NW * 64), args,
+                                    shmem, stream);
+}
+
+// One (d, waves) instantiation per translation unit, selected by DASH_MAIN_D and
+// DASH_MAIN_NW, so that each can get its own code-generation flags.
+#define DASH_CAT2(a, b, c, d) a##b##c##d
+#define DASH_CAT(a, b, c, d) DASH_CAT2(a, b, c, d)
+hipError_t DASH_CAT(launch_main_d, DASH_MAIN_D, _nw, DASH_MAIN_NW)(const BwdParams& prm, int grid, hipStream_t stream) {
+  return launch_main_t<DASH_MAIN_D, DASH_MAIN_NW>(prm, grid, stream);
+}
+
+}  // namespace dash

@@ -25,23 +25,28 @@ constexpr int64_t kMaxTasks = int64_t(1) << 30;
 
 int tile_for(int N) { return N < 512 ? 64 : 128; }
 
+
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t dqacc = 0, delta = 0, sem = 0, ctr = 0, total = 0;
+  size_t dqacc = 0, delta = 0, nlse2 = 0, sem = 0, ctr = 0, total = 0;
   int sem_stride = 0;
 };
 
 WsLayout ws_layout(int B, int H, int N, int d) {
   WsLayout L;
-  L.sem_stride = static_cast<int>(cdiv(cdiv(N, 64) + 1, 32) * 32);
+  // One semaphore per 64-row Q step and wave (4 at most), for every step of the
+  // ceil(N / tile) tiles of a head (the last tile's second step may lie past N).
+  const int tile = tile_for(N);
+  L.sem_stride = static_cast<int>(cdiv(cdiv(N, tile) * (tile / 64) * 4, 32) * 32);
   const size_t dq_bytes = align256(size_t(B) * H * N * d * sizeof(float));
-  const size_t delta_bytes = align256(size_t(B) * H * N * sizeof(float));
+  const size_t row_bytes = align256(size_t(B) * H * N * sizeof(float));
   const size_t sem_bytes = align256(size_t(B) * H * L.sem_stride * sizeof(int));
   L.dqacc = 0;
   L.delta = L.dqacc + dq_bytes;
-  L.sem = L.delta + delta_bytes;
+  L.nlse2 = L.delta + row_bytes;
+  L.sem = L.nlse2 + row_bytes;
   L.ctr = L.sem + sem_bytes;
   L.total = L.ctr + kCtrInts * sizeof(int);
   return L;
@@ -87,6 +92,7 @@ struct DeviceState {
 
 std::mutex g_mu;
 std::map<int, DeviceState> g_devices;
+unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 
 // Measures which XCD each workgroup of a one-per-CU grid lands on. A clean
 // round-robin split (every XCD id present with the same count) gives the table
@@ -109,7 +115,7 @@ int init_device(int dev, DeviceState* st) {
   std::vector<int> ids(st->cus, -1);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(ids.data(), probe, sizeof(int) * st->cus, hipMemcpyDeviceToHost);
-  hipFree(probe);
+  (void)hipFree(probe);
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
   if (e != hipSuccess) return DASH_ERR_HIP;
   int max_id = -1;
@@ -187,7 +193,7 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   DevTable dt;
   if (hipMalloc(&dt.buf, host.size()) != hipSuccess) return DASH_ERR_HIP;
   if (hipMemcpy(dt.buf, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
-    hipFree(dt.buf);
+    (void)hipFree(dt.buf);
     return DASH_ERR_HIP;
   }
   char* base = static_cast<char*>(dt.buf);
@@ -235,13 +241,16 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   char* ws = static_cast<char*>(workspace);
   float* dqacc = reinterpret_cast<float*>(ws + L.dqacc);
   float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* nlse2 = reinterpret_cast<float*>(ws + L.nlse2);
   int* sem = reinterpret_cast<int*>(ws + L.sem);
   int* ctr = reinterpret_cast<int*>(ws + L.ctr);
 
   dash::PreParams pp;
   pp.o = static_cast<const __bf16*>(o);
   pp.dO = static_cast<const __bf16*>(dO);
+  pp.lse = lse;
   pp.delta = delta;
+  pp.nlse2 = nlse2;
   pp.rows = int64_t(B) * H * N;
   pp.sem = sem;
   pp.sem_count = int64_t(B) * H * L.sem_stride;
@@ -258,7 +267,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.k = static_cast<const __bf16*>(k);
   bp.v = static_cast<const __bf16*>(v);
   bp.dO = static_cast<const __bf16*>(dO);
-  bp.lse = lse;
+  bp.nlse2 = nlse2;
   bp.delta = delta;
   bp.dq = static_cast<__bf16*>(dq);
   bp.dk = static_cast<__bf16*>(dk);
@@ -283,6 +292,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.num_xcd = st->num_xcd;
   bp.cus_per_xcd = st->cus_per_xcd;
   bp.timeout_ticks = st->ticks_per_second * 5;  // 5 seconds per wait
+  bp.prof = g_prof;
   if (ev_start && hipEventRecord(static_cast<hipEvent_t>(ev_start), stream) != hipSuccess) return DASH_ERR_HIP;
   hipError_t e = dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream);
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
@@ -349,6 +359,17 @@ const char* dash_status_string(int status) {
 }
 
 int dash_tile_size(int N) { return tile_for(N); }
+
+#ifdef DASH_PROFILE
+// Profiling builds only: later calls write per-wave phase cycle counters of the main
+// kernel ([CUs][waves][8] uint64, see ProfSlot in kernels.h) into `buf` (device
+// memory owned by the caller, at least CUs * 4 * 8 * 8 bytes); null detaches.
+int dash_profile_attach(void* buf) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_prof = static_cast<unsigned long long*>(buf);
+  return DASH_OK;
+}
+#endif
 
 int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local) {

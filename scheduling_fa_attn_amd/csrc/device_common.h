@@ -1,0 +1,244 @@
+// Device-side helpers shared by the HIP kernels of the attention backward (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace dash {
+
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#define LDS_AS __attribute__((address_space(3)))
+#define GLB_AS __attribute__((address_space(1)))
+#define CONST_AS __attribute__((address_space(4)))
+
+// One record of the schedule table (item or task), read field by field through the
+// constant address space.
+struct Quad {
+  int x, y, z, w;
+};
+__device__ __forceinline__ Quad load_quad(const CONST_AS Quad* tab, int i) {
+  const CONST_AS int* f = reinterpret_cast<const CONST_AS int*>(tab + i);
+  return Quad{f[0], f[1], f[2], f[3]};
+}
+
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ unsigned xcc_id() {
+  // HW_REG_XCC_ID (hwreg 20), bits [3:0]: the XCD this wave runs on.
+  return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((16 - 1) << 11)) & 0xfu;
+}
+
+__device__ __forceinline__ int load_flag_sys(const int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+__device__ __forceinline__ void raise_error(int* err, int code) {
+  int expected = 0;
+  __hip_atomic_compare_exchange_strong(err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// Waits until every memory operation this wave issued has completed: global stores
+// acknowledged by the L2, global->LDS copies landed. The signal fences keep the
+// compiler from moving memory operations across it.
+__device__ __forceinline__ void wait_mem_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// Spin (the whole wave, one shared address) until *sem == want. Returns false if the
+// wait timed out or another wave reported an error; the caller then skips its
+// reduction step but keeps going, so that every barrier is still reached and the
+// kernel drains. Semaphores are read with agent-scope loads, which skip the CU's L1
+// and are served by the L2. With `cross_xcd` the contributors of one dQ tile may sit
+// on different XCDs, whose L2s are not coherent with each other: then an
+// agent-scope acquire fence (L2 invalidate) follows the wait.
+__device__ bool wait_turn(const int* sem, int want, int* err, long long timeout_ticks, bool cross_xcd) {
+  const long long t0 = wall_clock64();
+  int iter = 0;
+  while (true) {
+    const int s = __builtin_amdgcn_readfirstlane(__hip_atomic_load(sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (s == want) break;
+    if ((++iter & 31) == 0) {
+      if (__builtin_amdgcn_readfirstlane(load_flag_sys(err)) != 0) return false;
+      if (wall_clock64() - t0 > timeout_ticks) {
+        if (__lane_id() == 0) raise_error(err, kErrTimeout);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+  if (cross_xcd) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return true;
+}
+
+// Profiling builds (-DDASH_PROFILE) accumulate per-wave cycle counts (s_memtime) of
+// the phases of a step; see ProfSlot. Other builds compile the marks away.
+#ifdef DASH_PROFILE
+#define PROF_DECL                                      \
+  unsigned long long prof_acc[kProfSlots] = {};        \
+  unsigned long long prof_t = __builtin_readcyclecounter(); \
+  const unsigned long long prof_t0 = prof_t;
+#define PROF_MARK(slot)                                            \
+  do {                                                             \
+    const unsigned long long prof_now = __builtin_readcyclecounter(); \
+    prof_acc[slot] += prof_now - prof_t;                           \
+    prof_t = prof_now;                                             \
+  } while (0)
+#define PROF_COUNT(slot) (prof_acc[slot] += 1)
+#define PROF_STORE(prm, wave, nw)                                                       \
+  do {                                                                                  \
+    if ((prm).prof && (threadIdx.x & 63) == 0) {                                        \
+      prof_acc[kProfTotal] = __builtin_readcyclecounter() - prof_t0;                     \
+      unsigned long long* dst = (prm).prof + (static_cast<size_t>(blockIdx.x) * (nw) + (wave)) * kProfSlots; \
+      for (int k_ = 0; k_ < kProfSlots; ++k_) dst[k_] = prof_acc[k_];                    \
+    }                                                                                   \
+  } while (0)
+#else
+#define PROF_DECL
+#define PROF_MARK(slot) ((void)0)
+#define PROF_COUNT(slot) ((void)0)
+#define PROF_STORE(prm, wave, nw) ((void)0)
+#endif
+
+// Semaphore read through the scalar unit, bypassing the scalar cache (glc): served by
+// the L2 and counted by lgkmcnt, so polling does not wait for the vector-memory queue
+// (global->LDS copies in flight).
+__device__ __forceinline__ int sload_glc(const int* ptr) {
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0 glc\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+  return v;
+}
+
+// Wave-level wait for the dQ turn (XCD-local chains): scalar polls of *sem until it
+// equals `want`. Returns false on timeout or when another wave reported an error.
+__device__ bool wait_turn_local(const int* sem, int want, int* err, long long timeout_ticks) {
+  if (sload_glc(sem) == want) return true;
+  const long long t0 = wall_clock64();
+  int iter = 0;
+  while (true) {
+    __builtin_amdgcn_s_sleep(1);
+    if (sload_glc(sem) == want) return true;
+    if ((++iter & 31) == 0) {
+      if (sload_glc(err) != 0) return false;
+      if (wall_clock64() - t0 > timeout_ticks) {
+        if (__lane_id() == 0) raise_error(err, kErrTimeout);
+        return false;
+      }
+    }
+  }
+}
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+// Raw buffer descriptor over `bytes` bytes at `base`: loads past the end return 0 and
+// stores past the end are dropped, which is how rows past N are skipped.
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+constexpr int kSC1 = 16;  // buffer cache policy: device scope (skips the CU's L1)
+// (The raw buffer load/store builtins move 32-bit patterns as unsigned int: float
+// data is bit-cast, never converted.)
+
+// ---------------------------------------------------------------------------------
+// LDS tiles. Tiles are row-major bf16 with one 16-byte pad chunk per row (row stride
+// = row bytes + 16), so that consecutive rows start 16 bytes apart modulo the 256
+// bytes the 64 LDS banks cover.
+//
+// Row permutation. The 32 rows m of an MFMA operand (lane % 32) read Q/dO rows
+// pi(m), where pi swaps the two 2-bit fields of m inside each aligned group of 16:
+// m = 16G + 4a + j -> pi(m) = 16G + a + 4j. Then
+//  - the sixteen lanes of one ds_read_b128 phase read sixteen different rows, i.e.
+//    sixteen different 16-byte bank groups (conflict-free), and
+//  - four consecutive accumulator rows m..m+3 (what one ds_read_b64_tr_b16 group
+//    gathers for the P^T dO and dS^T Q operands) are physical rows four apart, so a
+//    transpose read of 4 rows x 4 chunks also hits sixteen different bank groups.
+// The same trick orders the KV rows of the dQ = dS K contraction (its k index):
+// k-step kk, lane half hi, read s and group row j use KV row 16kk + 2hi + s + 4j,
+// for both operands.
+// Every LDS address is then "per-lane part + compile-time constant".
+// ---------------------------------------------------------------------------------
+template <int D>
+struct TileGeom {
+  static constexpr int CPR = D / 8;           // 16-byte chunks per row
+  static constexpr int STRIDE = 2 * D + 16;   // bytes per LDS row
+};
+constexpr int kDsStride = 128 + 16;  // dS^T tile [kv][64 q]: bytes per LDS row
+
+__device__ __forceinline__ int pi16(int m) { return (m & ~15) | ((m >> 2) & 3) | ((m & 3) << 2); }
+
+__device__ __forceinline__ bf16x8 lds_ld16(const LDS_AS char* base, int off) {
+  return *reinterpret_cast<const LDS_AS bf16x8*>(base + off);
+}
+
+// Transpose read (ds_read_b64_tr_b16): lane j of each 16-lane group receives column
+// (n0 + j) of the group's 4 rows; this lane supplies the address of its row and of
+// the 4 columns n0 + 4*(lane%4) .. +3 (byte offset `off`).
+__device__ __forceinline__ shortx4 lds_tr(const LDS_AS char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<LDS_AS shortx4*>(const_cast<LDS_AS char*>(base) + off));
+}
+
+__device__ __forceinline__ bf16x8 join(shortx4 a, shortx4 b) {
+  typedef short shortx8 __attribute__((ext_vector_type(8)));
+  const shortx8 v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Global -> LDS copies (global_load_lds): lane l's bytes land at lds_base + l * size.
+// They are issued through inline assembly so that the compiler does not treat them
+// as LDS stores: otherwise it waits for them (s_waitcnt vmcnt(0)) before every LDS
+// read of the other buffer. Their completion is awaited explicitly (wait_mem_done)
+// before the barrier that publishes the buffer.
+__device__ __forceinline__ void dma16(const void* gptr, LDS_AS char* lds_base) {
+  const unsigned m0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds_base));
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* gptr, LDS_AS char* lds_base) {
+  const unsigned m0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds_base));
+  asm volatile("global_load_lds_dword %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+}
+
+// Copies rows [r0, r0 + ROWS) of a row-major [nrows, D] bf16 matrix into a padded
+// LDS tile with global_load_lds_dwordx4: instruction m fills LDS slots
+// [64m, 64m + 64) (lane l's 16 bytes land at slot 64m + l); pad slots are skipped.
+// Rows past nrows repeat row nrows - 1 (finite values; the kernel masks them).
+template <int D, int ROWS, int NW>
+__device__ __forceinline__ void dma_tile(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w, int lane) {
+  constexpr int SPR = TileGeom<D>::CPR + 1;  // slots per row
+  constexpr int NI = ROWS * SPR / 64;
+  static_assert((ROWS * SPR) % 64 == 0, "tile must fill whole 1 KiB blocks");
+#pragma unroll
+  for (int m = 0; m < (NI + NW - 1) / NW; ++m) {
+    const int blk = w + NW * m;
+    const int slot = blk * 64 + lane;
+    const int r = slot / SPR;
+    const int c = slot - r * SPR;
+    if (blk < NI && c < TileGeom<D>::CPR) {
+      int gr = r0 + r;
+      gr = gr < nrows ? gr : nrows - 1;
+      dma16(src + static_cast<int64_t>(gr) * D + c * 8, dst + blk * 1024);
+    }
+  }
+}
+
+// 64 floats of rows r0 + pi(m) (clamped to < nrows) into LDS slot m, one dword per lane.
+__device__ __forceinline__ void dma_row64(LDS_AS char* dst, const float* src, int r0, int nrows, int lane) {
+  int gr = r0 + pi16(lane);
+  gr = gr < nrows ? gr : nrows - 1;
+  dma4(src + gr, dst);
+}
+
+}  // namespace dash

@@ -13,7 +13,9 @@ constexpr int kErrPlacement = -7;
 struct PreParams {
   const __bf16* o;
   const __bf16* dO;
+  const float* lse;    // [rows] natural-log LSE of the scaled scores
   float* delta;        // [rows] D = rowsum(dO * O)
+  float* nlse2;        // [rows] -LSE * log2(e)
   int64_t rows;        // B * H * N
   int* sem;            // ordering semaphores to clear
   int64_t sem_count;
@@ -28,8 +30,8 @@ struct BwdParams {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dO;
-  const float* lse;
-  const float* delta;
+  const float* nlse2;  // [B*H*N] -LSE * log2(e)
+  const float* delta;  // [B*H*N] D = rowsum(dO * O)
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -41,7 +43,7 @@ struct BwdParams {
   const int4* items;
   const int4* tasks;
   int B, H, Hkv, N;
-  int sem_stride;      // semaphores per (b, h), padded
+  int sem_stride;      // semaphores per (b, h): 4 per 64-row Q step (one per wave), padded
   float scale;         // softmax scale s
   float scale_log2;    // s * log2(e)
   int causal;
@@ -50,12 +52,37 @@ struct BwdParams {
   int num_xcd;
   int cus_per_xcd;
   long long timeout_ticks;  // wall-clock ticks before a wait gives up
+  unsigned long long* prof; // profiling builds (DASH_PROFILE): per-wave phase cycle counters, or null
 };
 
-hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hipStream_t stream);
+// Phase counters of a profiling build, per wave: [grid][NW][kProfSlots] of 64-bit cycles
+// (s_memtime) or counts.
+constexpr int kProfSlots = 8;
+enum ProfSlot {
+  kProfBody = 0,     // step body: copies issued, S/dP, softmax, dV/dK, dS^T store
+  kProfBarrier = 1,  // waiting for this wave's copies and the step barrier
+  kProfDq = 2,       // dQ = dS K
+  kProfWait = 3,     // waiting for the dQ turn (semaphore)
+  kProfReduce = 4,   // dQ read-add-write (or atomics) and passing the turn on
+  kProfItem = 5,     // item prologue and epilogue
+  kProfSteps = 6,    // number of steps
+  kProfTotal = 7     // whole kernel
+};
+
+// Main kernel for head dimension d and a workgroup of nw waves (one translation unit each).
+hipError_t launch_main_d64_nw2(const BwdParams& prm, int grid, hipStream_t stream);
+hipError_t launch_main_d64_nw4(const BwdParams& prm, int grid, hipStream_t stream);
+hipError_t launch_main_d128_nw2(const BwdParams& prm, int grid, hipStream_t stream);
+hipError_t launch_main_d128_nw4(const BwdParams& prm, int grid, hipStream_t stream);
+inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hipStream_t stream) {
+  if (d == 64 && nw == 2) return launch_main_d64_nw2(prm, grid, stream);
+  if (d == 64 && nw == 4) return launch_main_d64_nw4(prm, grid, stream);
+  if (d == 128 && nw == 2) return launch_main_d128_nw2(prm, grid, stream);
+  if (d == 128 && nw == 4) return launch_main_d128_nw4(prm, grid, stream);
+  return hipErrorInvalidValue;
+}
 hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t stream);
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t count, float scale, int grid, hipStream_t stream);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
-int main_kernel_lds_bytes(int d, int nw);
 
 }  // namespace dash
