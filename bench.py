@@ -150,6 +150,9 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip the other schedules and the atomic variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (the reference for the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE scale factor) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
@@ -158,6 +161,17 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy:
+        torch.cuda.set_device(0)
+        n = args.calibrate_copy * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n * 4, "repeats": 3}), flush=True)
+        return
 
     from scheduling_fa_attn_amd import dash
 

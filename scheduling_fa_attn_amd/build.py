@@ -28,7 +28,7 @@ COMMON = [
 # crashes on it with the option.)
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # (source, extra flags, object name)
-MAIN_FLAGS = {(64, 4): VGPR_FORM, (128, 4): [], (64, 2): [], (128, 2): []}
+MAIN_FLAGS = {(64, 4): VGPR_FORM, (128, 4): VGPR_FORM, (64, 2): [], (128, 2): []}
 UNITS = [
     ("bwd_main.hip", [f"-DDASH_MAIN_D={d}", f"-DDASH_MAIN_NW={nw}"] + fl, f"bwd_main_d{d}_nw{nw}.o")
     for (d, nw), fl in MAIN_FLAGS.items()

@@ -142,6 +142,8 @@ bwd_main_kernel(BwdParams p) {
   const int ds_wr_lane = (32 * w + l32) * kDsStride + 8 * hi;
 
   LDS_AS char* sK = smem + C::OFF_K;
+  TileCopy<D, BQ, NW> qcopy;  // copy plan of the Q and dO tiles
+  qcopy.init(w, lane);
 
   for (int it = it_begin; it < it_end; ++it) {
     const Quad item = load_quad(items, it);
@@ -159,14 +161,18 @@ bwd_main_kernel(BwdParams p) {
       const int q0 = task.y * BC + (s % SUBS) * BQ;
       const int64_t bh = static_cast<int64_t>(b) * H + task.x;
       const int buf = s & 1;
-      dma_tile<D, BQ, NW>(smem + C::OFF_Q + buf * C::QT, p.q + bh * N * D, q0, N, w, lane);
-      dma_tile<D, BQ, NW>(smem + C::OFF_DO + buf * C::QT, p.dO + bh * N * D, q0, N, w, lane);
+      qcopy.issue(smem + C::OFF_Q + buf * C::QT, p.q + bh * N * D, q0, N, w);
+      qcopy.issue(smem + C::OFF_DO + buf * C::QT, p.dO + bh * N * D, q0, N, w);
       if (w == 0) dma_row64(smem + C::OFF_NL + buf * 256, p.nlse2 + bh * N, q0, N, lane);
       if (w == 1) dma_row64(smem + C::OFF_DL + buf * 256, p.delta + bh * N, q0, N, lane);
     };
 
     // Item prologue: K tile to LDS, first step's tiles, K/V rows of this wave to registers.
-    dma_tile<D, BC, NW>(sK, Kg, kv0, N, w, lane);
+    {
+      TileCopy<D, BC, NW> kcopy;  // once per item: plan computed in place
+      kcopy.init(w, lane);
+      kcopy.issue(sK, Kg, kv0, N, w);
+    }
     issue_step(0);
     bf16x8 kreg[DK], vreg[DK];
     {
@@ -194,41 +200,48 @@ bwd_main_kernel(BwdParams p) {
     const int kvcol = kv0 + 32 * w + l32;  // this lane's KV row in S, P, dP, dS
     PROF_MARK(kProfItem);
 
-    // dQ partial of step `ps` (its dS^T is in LDS buffer ps & 1) = dS K, this wave's
-    // 32x32 blocks; accumulator row m of block qb is Q row q0 + pi(32 qb + m).
-    auto dq_partial = [&](int ps, floatx16 (&dq)[C::NBLK]) __attribute__((always_inline)) {
+    // Block t2 of this wave's dQ partial of step `ps` (its dS^T is in LDS buffer
+    // ps & 1) = dS K; accumulator row m of block qb is Q row q0 + pi(32 qb + m).
+    auto dq_block = [&](int ps, int t2) __attribute__((always_inline)) -> floatx16 {
       const LDS_AS char* sdSp = smem + C::OFF_DS + (ps & 1) * C::DST;
-#pragma unroll
-      for (int t2 = 0; t2 < C::NBLK; ++t2) {
-        const int blk = w + NW * t2;
-        const int qb = blk / DB, db = blk % DB;
-        floatx16 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * qb;
-          const bf16x8 a = join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
-          const int koff = kd_lane + 16 * kk * ST + 64 * db;
-          const bf16x8 bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
-          acc = mfma32(a, bk, acc);
-        }
-        dq[t2] = acc;
-      }
-    };
-    // Byte offset (within the head) of element r of this wave's dQ block t2 at step q0.
-    auto dq_off = [&](int q0s, int t2, int r) __attribute__((always_inline)) {
       const int blk = w + NW * t2;
       const int qb = blk / DB, db = blk % DB;
-      return (q0s + pi16(qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3))) * D + db * 32 + l32;
+      floatx16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * qb;
+        const bf16x8 a = join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
+        const int koff = kd_lane + 16 * kk * ST + 64 * db;
+        const bf16x8 bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
+        acc = mfma32(a, bk, acc);
+      }
+      return acc;
+    };
+
+    // dQ addressing. Element r of this wave's block t2 at a step sits at row
+    // q0 + 32 qb + 16 (t / 2) + 2 (t % 2) + hi + 4 e (r = 4 t + e) and column 32 db + l32.
+    // Buffer descriptors start at row q0, so the per-element byte offset is a per-lane
+    // base (row hi, column) plus a compile-time constant.
+    auto blk_base = [&](int t2) __attribute__((always_inline)) {
+      const int blk = w + NW * t2;
+      return hi * D + (blk % DB) * 32 + l32;
+    };
+    auto row_const = [&](int t2, int r) __attribute__((always_inline)) {
+      const int qb = (w + NW * t2) / DB;  // wave-uniform
+      const int t = r >> 2, e = r & 3;
+      return (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e) * D;
     };
 
     // Reduction of step ps's dQ partial, in three parts so that its memory latency
-    // overlaps the next step's work: (1) wait for the turn and issue the accumulator
-    // loads, (2) add and store, (3) after the stores are acknowledged, pass the turn on.
+    // overlaps other work: (1) wait for the turn and issue the accumulator loads,
+    // (2) add and store, (3) after the stores are acknowledged, pass the turn on.
     struct Pending {
-      int rank, last, q0;
+      int rank, last;
       int* sem;
-      float* acc_g;
-      bf16* dq_g;
+      rsrc_t acc_rs;  // fp32 accumulator rows [q0, N) of (b, h)
+      rsrc_t dq_rs;   // bf16 dQ rows [q0, N) of (b, h)
+      float* acc_g;   // accumulator row q0 (atomic variant)
+      int rows;       // rows from q0 to N (may be <= 0 for a step past N)
       bool go;
     };
     auto reduce_begin = [&](int ps, float (&ld)[C::NBLK][16]) __attribute__((always_inline)) -> Pending {
@@ -236,10 +249,13 @@ bwd_main_kernel(BwdParams p) {
       Pending pd;
       pd.rank = task.z;
       pd.last = task.w;
-      pd.q0 = task.y * BC + (ps % SUBS) * BQ;
+      const int q0s = task.y * BC + (ps % SUBS) * BQ;
       const int64_t bh = static_cast<int64_t>(b) * H + task.x;
-      pd.acc_g = p.dqacc + bh * N * D;
-      pd.dq_g = p.dq + bh * N * D;
+      pd.rows = N - q0s;
+      const int nrec = pd.rows > 0 ? pd.rows * D : 0;
+      pd.acc_g = p.dqacc + bh * N * D + static_cast<int64_t>(q0s) * D;
+      pd.acc_rs = make_rsrc(pd.acc_g, nrec * 4);
+      pd.dq_rs = make_rsrc(p.dq + bh * N * D + static_cast<int64_t>(q0s) * D, nrec * 2);
       pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
       pd.go = !failed;
       if (p.deterministic && pd.go && pd.rank > 0) {
@@ -252,50 +268,59 @@ bwd_main_kernel(BwdParams p) {
       }
       PROF_MARK(kProfWait);
       if (p.deterministic && pd.go && pd.rank > 0) {
-        const rsrc_t rs = make_rsrc(pd.acc_g, N * D * 4);
 #pragma unroll
-        for (int t2 = 0; t2 < C::NBLK; ++t2)
+        for (int t2 = 0; t2 < C::NBLK; ++t2) {
+          const int vb = 4 * blk_base(t2);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ld[t2][r] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * dq_off(pd.q0, t2, r), 0, kSC1));
-      } else {
-#pragma unroll
-        for (int t2 = 0; t2 < C::NBLK; ++t2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ld[t2][r] = 0.f;
+          for (int r = 0; r < 16; ++r)
+            ld[t2][r] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(pd.acc_rs, vb + 4 * row_const(t2, r), 0, kSC1));
+        }
       }
       return pd;
     };
-    auto reduce_store = [&](const Pending& pd, const floatx16 (&dq)[C::NBLK], const float (&ld)[C::NBLK][16])
+    auto reduce_store = [&](const Pending& pd, int t2, const floatx16& dq, const float (&ld)[C::NBLK][16])
         __attribute__((always_inline)) {
       if (!pd.go) return;
       if (!p.deterministic) {
 #pragma unroll
-        for (int t2 = 0; t2 < C::NBLK; ++t2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int off = dq_off(pd.q0, t2, r);
-            if (off < N * D) atomicAdd(pd.acc_g + off, dq[t2][r]);
-          }
-      } else if (pd.last) {
-        const rsrc_t rs = make_rsrc(pd.dq_g, N * D * 2);
-#pragma unroll
-        for (int t2 = 0; t2 < C::NBLK; ++t2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const bf16 v = static_cast<bf16>((ld[t2][r] + dq[t2][r]) * p.scale);
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, v), rs,
-                                                  2 * dq_off(pd.q0, t2, r), 0, 0);
-          }
-      } else {
-        const rsrc_t rs = make_rsrc(pd.acc_g, N * D * 4);
-#pragma unroll
-        for (int t2 = 0; t2 < C::NBLK; ++t2)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, ld[t2][r] + dq[t2][r]), rs,
-                                                  4 * dq_off(pd.q0, t2, r), 0, 0);
+        for (int r = 0; r < 16; ++r) {
+          const int off = blk_base(t2) + row_const(t2, r);
+          if (off < pd.rows * D) atomicAdd(pd.acc_g + off, dq[r]);
+        }
+        return;
       }
+      const bool add = pd.rank > 0;
+      if (pd.last) {
+        const int vb = 2 * blk_base(t2);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = add ? ld[t2][r] + dq[r] : dq[r];
+          const bf16 hv = static_cast<bf16>(v * p.scale);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), pd.dq_rs,
+                                                vb + 2 * row_const(t2, r), 0, 0);
+        }
+      } else {
+        const int vb = 4 * blk_base(t2);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float v = add ? ld[t2][r] + dq[r] : dq[r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), pd.acc_rs, vb + 4 * row_const(t2, r),
+                                                0, 0);
+        }
+      }
+    };
+    // The whole reduction of step ps except passing the turn on.
+    auto reduce_step = [&](int ps) __attribute__((always_inline)) -> Pending {
+      float ld[C::NBLK][16];
+      const Pending pd = reduce_begin(ps, ld);
+#pragma unroll
+      for (int t2 = 0; t2 < C::NBLK; ++t2) {
+        const floatx16 dq = dq_block(ps, t2);
+        reduce_store(pd, t2, dq, ld);
+      }
+      PROF_MARK(kProfDq);
+      return pd;
     };
     // Call after wait_mem_done(): this wave's accumulator stores are in the L2.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
@@ -316,18 +341,16 @@ bwd_main_kernel(BwdParams p) {
       const int j = task.y;
       const int q0 = j * BC + (s % SUBS) * BQ;
 
-      // Previous step's dQ partial and the first half of its reduction.
-      floatx16 dq[C::NBLK];
-      float ld[C::NBLK][16];
+      // Previous step's dQ partial and its reduction: wait for the turn and issue the
+      // accumulator loads first, then run the dQ MFMAs while the loads are in flight,
+      // then add and store. The stores are acknowledged during this step's body; the
+      // turn is passed on after the body.
       Pending pd;
       const bool have_prev = s > 0;
-      if (have_prev) {
-        dq_partial(s - 1, dq);
-        PROF_MARK(kProfDq);
-        pd = reduce_begin(s - 1, ld);
-      }
-      // The next step's copies go after the accumulator loads: waiting for those
-      // loads must not wait for the copies (the vector-memory counter is in order).
+      if (have_prev) pd = reduce_step(s - 1);
+      // The next step's copies go after the accumulator loads were consumed: waiting
+      // for those loads must not wait for the copies (the vector-memory counter is in
+      // order).
       if (s + 1 < n_steps) issue_step(s + 1);
 
       const LDS_AS char* sQ = smem + C::OFF_Q + buf * C::QT;
@@ -349,7 +372,6 @@ bwd_main_kernel(BwdParams p) {
           S = mfma32(lds_ld16(sQ, off), kreg[ks], S);
           dP = mfma32(lds_ld16(sdO, off), vreg[ks], dP);
         }
-        if (qb == 0 && have_prev) reduce_store(pd, dq, ld);
         if (need_mask) {
           // Masked entries (key after query, or row/column past N) get S = -inf, so
           // that P = exp2(-inf) = 0 and dS = 0.
@@ -403,12 +425,7 @@ bwd_main_kernel(BwdParams p) {
     }
     // The item's last step: its dQ partial and reduction.
     {
-      floatx16 dq[C::NBLK];
-      float ld[C::NBLK][16];
-      dq_partial(n_steps - 1, dq);
-      PROF_MARK(kProfDq);
-      const Pending pd = reduce_begin(n_steps - 1, ld);
-      reduce_store(pd, dq, ld);
+      const Pending pd = reduce_step(n_steps - 1);
       wait_mem_done();
       reduce_signal(pd);
       PROF_MARK(kProfReduce);

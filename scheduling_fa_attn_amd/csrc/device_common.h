@@ -197,48 +197,75 @@ __device__ __forceinline__ bf16x8 join(shortx4 a, shortx4 b) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Global -> LDS copies (global_load_lds): lane l's bytes land at lds_base + l * size.
-// They are issued through inline assembly so that the compiler does not treat them
-// as LDS stores: otherwise it waits for them (s_waitcnt vmcnt(0)) before every LDS
-// read of the other buffer. Their completion is awaited explicitly (wait_mem_done)
-// before the barrier that publishes the buffer.
-__device__ __forceinline__ void dma16(const void* gptr, LDS_AS char* lds_base) {
+// Global -> LDS copies (global_load_lds, scalar base + 32-bit per-lane byte offset):
+// lane l's bytes land at lds_base + l * size. They are issued through inline assembly
+// so that the compiler does not treat them as LDS stores: otherwise it waits for them
+// (s_waitcnt vmcnt(0)) before every LDS read of the other buffer. Their completion is
+// awaited explicitly (wait_mem_done) before the barrier that publishes the buffer.
+__device__ __forceinline__ void dma16(const void* sbase, unsigned voff, LDS_AS char* lds_base) {
   const unsigned m0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds_base));
-  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+  asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* gptr, LDS_AS char* lds_base) {
+__device__ __forceinline__ void dma4(const void* sbase, unsigned voff, LDS_AS char* lds_base) {
   const unsigned m0 = static_cast<unsigned>(reinterpret_cast<uintptr_t>(lds_base));
-  asm volatile("global_load_lds_dword %0, off" : : "v"(gptr), "{m0}"(m0) : "memory");
+  asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(sbase), "{m0}"(m0) : "memory");
 }
 
-// Copies rows [r0, r0 + ROWS) of a row-major [nrows, D] bf16 matrix into a padded
-// LDS tile with global_load_lds_dwordx4: instruction m fills LDS slots
-// [64m, 64m + 64) (lane l's 16 bytes land at slot 64m + l); pad slots are skipped.
-// Rows past nrows repeat row nrows - 1 (finite values; the kernel masks them).
+// Copy plan of a ROWS x D bf16 tile into a padded LDS tile: instruction m of wave w
+// fills LDS slots [64 blk, 64 blk + 64), blk = w + NW m; lane l's slot holds chunk c
+// of row r. voff[m] is the lane's byte offset (r D + 8 c) * 2 from the tile's first
+// global row (pad slots re-read chunk 0 of their row: harmless). Computed once.
 template <int D, int ROWS, int NW>
-__device__ __forceinline__ void dma_tile(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w, int lane) {
-  constexpr int SPR = TileGeom<D>::CPR + 1;  // slots per row
-  constexpr int NI = ROWS * SPR / 64;
+struct TileCopy {
+  static constexpr int SPR = TileGeom<D>::CPR + 1;  // slots per row
+  static constexpr int NI = ROWS * SPR / 64;         // instructions per tile
+  static constexpr int PER_WAVE = (NI + NW - 1) / NW;
   static_assert((ROWS * SPR) % 64 == 0, "tile must fill whole 1 KiB blocks");
+  unsigned voff[PER_WAVE];
+  __device__ __forceinline__ void init(int w, int lane) {
 #pragma unroll
-  for (int m = 0; m < (NI + NW - 1) / NW; ++m) {
-    const int blk = w + NW * m;
-    const int slot = blk * 64 + lane;
-    const int r = slot / SPR;
-    const int c = slot - r * SPR;
-    if (blk < NI && c < TileGeom<D>::CPR) {
-      int gr = r0 + r;
-      gr = gr < nrows ? gr : nrows - 1;
-      dma16(src + static_cast<int64_t>(gr) * D + c * 8, dst + blk * 1024);
+    for (int m = 0; m < PER_WAVE; ++m) {
+      const int slot = (w + NW * m) * 64 + lane;
+      const int r = slot / SPR;
+      int c = slot - r * SPR;
+      c = c < TileGeom<D>::CPR ? c : 0;
+      voff[m] = static_cast<unsigned>((r * D + c * 8) * 2);
     }
   }
-}
+  // Rows [r0, r0 + ROWS) of the row-major [nrows, D] matrix at src (0 <= r0, 1 <= nrows;
+  // r0 may be >= nrows for a step past the end). Rows past nrows repeat row nrows - 1
+  // (finite values; the kernel masks them): then every offset is taken from row 0 of
+  // the matrix with the row clamped in signed arithmetic, so no address leaves
+  // [src, src + nrows * D).
+  __device__ __forceinline__ void issue(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w) const {
+    const bool ragged = r0 + ROWS > nrows;
+    const bf16* base = ragged ? src : src + static_cast<int64_t>(r0) * D;
+#pragma unroll
+    for (int m = 0; m < PER_WAVE; ++m) {
+      const int blk = w + NW * m;
+      if (blk < NI) {
+        unsigned v = voff[m];
+        if (ragged) {
+          int r = r0 + static_cast<int>(v / (2 * D));
+          r = r < nrows - 1 ? r : nrows - 1;
+          v = static_cast<unsigned>(r) * (2 * D) + (v % (2 * D));
+        }
+        dma16(base, v, dst + blk * 1024);
+      }
+    }
+  }
+};
 
 // 64 floats of rows r0 + pi(m) (clamped to < nrows) into LDS slot m, one dword per lane.
+// As in TileCopy::issue, a ragged step addresses from row 0 with a signed clamp.
 __device__ __forceinline__ void dma_row64(LDS_AS char* dst, const float* src, int r0, int nrows, int lane) {
-  int gr = r0 + pi16(lane);
-  gr = gr < nrows ? gr : nrows - 1;
-  dma4(src + gr, dst);
+  if (r0 + 64 > nrows) {
+    int r = r0 + pi16(lane);
+    r = r < nrows - 1 ? r : nrows - 1;
+    dma4(src, static_cast<unsigned>(r * 4), dst);
+  } else {
+    dma4(src + r0, static_cast<unsigned>(pi16(lane) * 4), dst);
+  }
 }
 
 }  // namespace dash
