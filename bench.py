@@ -2,11 +2,12 @@
 
 One step = one dash_attn_bwd call (preprocess + persistent backward kernel with the
 ordered dQ reduction, dQ written by the last contributor) over one batch of
-synthetic bf16 inputs resident in HBM. The default workload is the full-mask
-configuration the headline metric is quoted on (B=8, H=Hkv=16, N=2048, d=128,
-16 384 tokens, hidden 2048) with the shift schedule; the naive ordered schedule
-and the atomic (non-deterministic) variant are timed beside it for the
-det/non-det ratio.
+synthetic bf16 inputs resident in HBM. The headline workload is the full-mask
+configuration the metric is quoted on (B=8, H=Hkv=16, N=2048, d=128, 16 384
+tokens, hidden 2048) with the shift schedule; the naive ordered schedule and the
+atomic (non-deterministic) variant are timed beside it for the det/non-det ratio.
+The three causal configurations (d=64 N=4096, d=128 N=16384, GQA d=128 N=8192)
+are timed the same way and reported under "other_workloads" (--only skips them).
 
 Prints ONE JSON line on stdout (details on stderr).
 """
@@ -140,6 +141,74 @@ def cpu_baseline(shape, causal, seed, budget_s):
                       f"the workload's shape; fp64 numpy backward only, {elapsed:.1f} s"}
 
 
+def measure_workload(name, schedule, steps, warmup, compare):
+    """Times one workload: the chosen (or best) deterministic schedule, and with `compare`
+    the other deterministic schedules and the atomic variant of the chosen one."""
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    B, H, Hkv, N, d, causal, best, others, cfg_index = WORKLOADS[name]
+    schedule = schedule or best
+    shape = (B, H, Hkv, N, d)
+    seed = 1000 + cfg_index
+    log(f"workload {name}: B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} seed={seed}")
+    dev = make_inputs(B, H, Hkv, N, d, causal, seed)
+    ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    fl = flops_bwd(B, H, N, d, causal)
+    ms, main_ms, _ = time_schedule(dev, shape, causal, schedule, 1, steps, warmup, ws)
+    tflops = fl / (ms * 1e-3) / 1e12
+    log(f"  {schedule} det: {ms:.3f} ms/step ({tflops:.1f} TFLOPS), main kernel {main_ms:.3f} ms")
+    extra = {schedule: round(tflops, 2)}
+    ratio = None
+    if compare:
+        for s in others:
+            ms_s, _, _ = time_schedule(dev, shape, causal, s, 1, steps, warmup, ws)
+            extra[s] = round(fl / (ms_s * 1e-3) / 1e12, 2)
+            log(f"  {s} det: {ms_s:.3f} ms/step ({extra[s]:.1f} TFLOPS)")
+        ms_a, _, _ = time_schedule(dev, shape, causal, schedule, 0, steps, warmup, ws)
+        extra["atomic_" + schedule] = round(fl / (ms_a * 1e-3) / 1e12, 2)
+        ratio = ms_a / ms
+        log(f"  {schedule} atomic: {ms_a:.3f} ms/step ({extra['atomic_' + schedule]:.1f} TFLOPS); "
+            f"det/non-det throughput ratio {ratio:.3f}")
+    del dev, ws
+    torch.cuda.empty_cache()
+    return {"schedule": schedule, "tflops": round(tflops, 2), "ms_per_step": round(ms, 4),
+            "main_kernel_ms": round(main_ms, 4), "det_nondet_ratio": None if ratio is None else round(ratio, 4),
+            "schedules_tflops": extra,
+            "roofline_frac": round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
+# Sources of the main kernel: the HBM-traffic figures in profiles/ hold for the kernel
+# these hashed to when the counters were taken.
+KERNEL_SOURCES = ("scheduling_fa_attn_amd/csrc/bwd_main.hip", "scheduling_fa_attn_amd/csrc/device_common.h",
+                  "scheduling_fa_attn_amd/csrc/kernels.h", "scheduling_fa_attn_amd/build.py")
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_bytes(workload, kernel):
+    """HBM bytes per launch of the main kernel (FETCH + WRITE, calibrated), from the
+    counter summary in profiles/, or None when there is none for this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic__{workload}.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel") != kernel or t.get("source_hash") != kernel_source_hash():
+        return None
+    return int(t["fetch_bytes"] + t["write_bytes"])
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -148,6 +217,7 @@ def main():
     ap.add_argument("--workload", default="full-d128-N2048", choices=list(WORKLOADS))
     ap.add_argument("--schedule", default=None)
     ap.add_argument("--no-compare", action="store_true", help="skip the other schedules and the atomic variant")
+    ap.add_argument("--only", action="store_true", help="measure only --workload (not the other configurations)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -173,59 +243,47 @@ def main():
         print(json.dumps({"copy_bytes": n * 4, "repeats": 3}), flush=True)
         return
 
-    from scheduling_fa_attn_amd import dash
-
-    B, H, Hkv, N, d, causal, best, others, cfg_index = WORKLOADS[args.workload]
-    schedule = args.schedule or best
-    shape = (B, H, Hkv, N, d)
-    seed = 1000 + cfg_index
     torch.cuda.set_device(0)
-    log(f"workload {args.workload}: B={B} H={H} Hkv={Hkv} N={N} d={d} causal={causal} seed={seed}")
-    dev = make_inputs(B, H, Hkv, N, d, causal, seed)
-    ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    main_res = measure_workload(args.workload, args.schedule, args.steps, args.warmup, not args.no_compare)
+    B, H, Hkv, N, d, causal, _, _, cfg_index = WORKLOADS[args.workload]
+    others = {}
+    if not args.only:
+        for name in WORKLOADS:
+            if name != args.workload:
+                r = measure_workload(name, None, args.steps, args.warmup, not args.no_compare)
+                others[name] = {k: r[k] for k in ("schedule", "tflops", "ms_per_step", "main_kernel_ms",
+                                                  "det_nondet_ratio", "schedules_tflops", "roofline_frac")}
     fl = flops_bwd(B, H, N, d, causal)
-
-    ms, main_ms, _ = time_schedule(dev, shape, causal, schedule, 1, args.steps, args.warmup, ws)
-    tflops = fl / (ms * 1e-3) / 1e12
-    log(f"{schedule} det: {ms:.3f} ms/step ({tflops:.1f} TFLOPS), main kernel {main_ms:.3f} ms")
-    extra = {schedule: round(tflops, 2)}
-    ratio = None
-    if not args.no_compare:
-        for s in others:
-            ms_s, _, _ = time_schedule(dev, shape, causal, s, 1, args.steps, args.warmup, ws)
-            extra[s] = round(fl / (ms_s * 1e-3) / 1e12, 2)
-            log(f"{s} det: {ms_s:.3f} ms/step ({extra[s]:.1f} TFLOPS)")
-        ms_a, _, _ = time_schedule(dev, shape, causal, schedule, 0, args.steps, args.warmup, ws)
-        extra["atomic_" + schedule] = round(fl / (ms_a * 1e-3) / 1e12, 2)
-        ratio = ms_a / ms
-        log(f"{schedule} atomic: {ms_a:.3f} ms/step ({extra['atomic_' + schedule]:.1f} TFLOPS); "
-            f"det/non-det throughput ratio {ratio:.3f}")
-
+    main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
+    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}>"
     result = {
         "metric": METRIC,
-        "value": round(tflops, 3),
+        "value": round(main_res["tflops"], 3),
         "unit": "TFLOPS",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(main_res["ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": args.workload, "B": B, "H": H, "Hkv": Hkv, "N": N, "d": d,
-                   "mask": "causal" if causal else "full", "schedule": schedule, "deterministic": True,
-                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
-        "det_nondet_ratio": None if ratio is None else round(ratio, 4),
-        "schedules_tflops": extra,
+                   "mask": "causal" if causal else "full", "schedule": main_res["schedule"],
+                   "deterministic": True, "seed": 1000 + cfg_index},
+        "det_nondet_ratio": main_res["det_nondet_ratio"],
+        "schedules_tflops": main_res["schedules_tflops"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": f"bwd_main_kernel<{d},{4 if N >= 512 else 2}>", "main_kernel_ms": round(main_ms, 4)},
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_bytes(args.workload, kernel),
+                     "kernel": kernel, "main_kernel_ms": round(main_ms, 4)},
     }
+    if others:
+        result["other_workloads"] = others
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(shape, causal, seed, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline((B, H, Hkv, N, d), causal, 1000 + cfg_index, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

@@ -8,11 +8,13 @@ import pytest
 
 from scheduling_fa_attn_amd import dash
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "dash.h")
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
+HEADER = os.path.join(INCLUDE, "dash.h")
+PROF_HEADER = os.path.join(INCLUDE, "dash_profile.h")
 
 
-def header_functions():
-    text = open(HEADER).read()
+def header_functions(path=HEADER):
+    text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(dash_[a-z_0-9]+)\s*\(", text)))
 
@@ -23,6 +25,23 @@ def test_exports_every_declared_symbol():
     assert set(names) == set(dash.EXPORTED)
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_profiling_build_exports():
+    """The profiling build (-DDASH_PROFILE) exports dash.h plus dash_profile.h; the
+    release build exports nothing of dash_profile.h."""
+    from scheduling_fa_attn_amd.build import PROF_LIB_PATH
+
+    extra = header_functions(PROF_HEADER)
+    assert extra == ["dash_profile_attach"]
+    rel = ctypes.CDLL(dash.load()._name)
+    for name in extra:
+        assert not hasattr(rel, name), name
+    if not os.path.exists(PROF_LIB_PATH):
+        pytest.skip("profiling library not built")
+    prof = ctypes.CDLL(PROF_LIB_PATH)
+    for name in header_functions() + extra:
+        assert hasattr(prof, name), name
 
 
 def test_status_strings():
