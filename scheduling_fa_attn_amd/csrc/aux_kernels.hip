@@ -11,7 +11,8 @@ namespace dash {
 
 // ---------------------------------------------------------------------------------
 // Preprocess: D[row] = sum_e dO[row, e] * O[row, e] in fp32 with a fixed reduction
-// tree and nl[row] = -LSE[row] * log2(e); clears the ordering semaphores and the XCD
+// tree and nl[row] = -LSE[row] * log2(e), stored with the head's rows padded to the
+// tile (padding: D = 0, nl = -inf); clears the ordering semaphores and the XCD
 // slot counters; for the atomic variant also clears the fp32 dQ accumulator.
 // ---------------------------------------------------------------------------------
 template <int D>
@@ -31,8 +32,19 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, LPR);
     if (part == 0) {
-      p.delta[row] = acc;
-      p.nlse2[row] = -p.lse[row] * 1.4426950408889634f;
+      const int64_t out = (row / p.N) * p.row_stride + row % p.N;
+      p.delta[out] = acc;
+      p.nlse2[out] = -p.lse[row] * 1.4426950408889634f;
+    }
+  }
+  // Rows past N (up to the tile boundary): P = exp2(S * c - inf) = 0 there, dS = 0.
+  const int pad = p.row_stride - p.N;
+  if (pad > 0) {
+    const int64_t heads = p.rows / p.N;
+    for (int64_t x = tid; x < heads * pad; x += nthreads) {
+      const int64_t out = (x / pad) * p.row_stride + p.N + x % pad;
+      p.delta[out] = 0.f;
+      p.nlse2[out] = -__builtin_inff();
     }
   }
   for (int64_t x = tid; x < p.sem_count; x += nthreads) p.sem[x] = 0;

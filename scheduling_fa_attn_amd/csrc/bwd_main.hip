@@ -144,6 +144,7 @@ bwd_main_kernel(BwdParams p) {
   LDS_AS char* sK = smem + C::OFF_K;
   TileCopy<D, BQ, NW> qcopy;  // copy plan of the Q and dO tiles
   qcopy.init(w, lane);
+  const unsigned row_lane = static_cast<unsigned>(pi16(lane) * 4);  // LDS slot m <- row pi(m)
 
   for (int it = it_begin; it < it_end; ++it) {
     const Quad item = load_quad(items, it);
@@ -163,8 +164,9 @@ bwd_main_kernel(BwdParams p) {
       const int buf = s & 1;
       qcopy.issue(smem + C::OFF_Q + buf * C::QT, p.q + bh * N * D, q0, N, w);
       qcopy.issue(smem + C::OFF_DO + buf * C::QT, p.dO + bh * N * D, q0, N, w);
-      if (w == 0) dma_row64(smem + C::OFF_NL + buf * 256, p.nlse2 + bh * N, q0, N, lane);
-      if (w == 1) dma_row64(smem + C::OFF_DL + buf * 256, p.delta + bh * N, q0, N, lane);
+      // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
+      if (w == 0) dma4(p.nlse2 + bh * p.row_stride + q0, row_lane, smem + C::OFF_NL + buf * 256);
+      if (w == 1) dma4(p.delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + buf * 256);
     };
 
     // Item prologue: K tile to LDS, first step's tiles, K/V rows of this wave to registers.
@@ -197,6 +199,15 @@ bwd_main_kernel(BwdParams p) {
     }
     wait_mem_done();
     __syncthreads();
+    if (kv0 + BC > N) {
+      // Ragged KV tile: K rows past N become zero in LDS, so that the (unmasked,
+      // finite) dS of those columns adds nothing to dQ. Their K/V registers are zero
+      // already and their dK/dV rows are never stored.
+      const int r0 = N - kv0;
+      LDS_AS floatx4* z = reinterpret_cast<LDS_AS floatx4*>(sK + r0 * ST);
+      for (int x = tid; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+    }
     const int kvcol = kv0 + 32 * w + l32;  // this lane's KV row in S, P, dP, dS
     PROF_MARK(kProfItem);
 
@@ -206,14 +217,23 @@ bwd_main_kernel(BwdParams p) {
       const LDS_AS char* sdSp = smem + C::OFF_DS + (ps & 1) * C::DST;
       const int blk = w + NW * t2;
       const int qb = blk / DB, db = blk % DB;
+      // Operands of k-step kk: A = dS (transpose reads of dS^T), B = K (transpose reads
+      // of the K tile); loaded one k-step ahead of their MFMA.
+      auto load = [&](int kk, bf16x8& a, bf16x8& bk) __attribute__((always_inline)) {
+        const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * qb;
+        a = join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
+        const int koff = kd_lane + 16 * kk * ST + 64 * db;
+        bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
+      };
       floatx16 acc = {};
+      bf16x8 a[2], bk[2];
+      load(0, a[0], bk[0]);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * qb;
-        const bf16x8 a = join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
-        const int koff = kd_lane + 16 * kk * ST + 64 * db;
-        const bf16x8 bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
-        acc = mfma32(a, bk, acc);
+        if (kk + 1 < KK) load(kk + 1, a[(kk + 1) & 1], bk[(kk + 1) & 1]);
+        acc = mfma32(a[kk & 1], bk[kk & 1], acc);
+        __builtin_amdgcn_sched_barrier(0);
       }
       return acc;
     };
@@ -358,64 +378,135 @@ bwd_main_kernel(BwdParams p) {
       const LDS_AS char* sNL = smem + C::OFF_NL + buf * 256;
       const LDS_AS char* sDL = smem + C::OFF_DL + buf * 256;
       LDS_AS char* sdS = smem + C::OFF_DS + buf * C::DST;
-      const bool need_mask = (p.causal && j == kv_tile) || (kv0 + BC > N) || (q0 + BQ > N);
+      // Only the diagonal task of a causal mask needs a mask: rows past N have
+      // -LSE*log2(e) = -inf (P = 0) and columns past N meet zero K rows in dQ.
+      const bool diag = p.causal && j == kv_tile;
+      // Causal diagonal: P = 0 (so dS = 0) where the key comes after the query, i.e.
+      // where pi(m) < kvcol - q0. Branch-free: elsewhere the threshold is below every row.
+      const int mask_thr = diag ? kvcol - q0 - hi : -1;  // compared with pi(m) - hi
 
-      // One 32-row block of the step at a time keeps S, dP, P, dS of a single 32 x 32
-      // block live. Accumulator row m of the block is Q row pi(m).
+      // The step body as an explicit software pipeline of "slots" separated by
+      // scheduling barriers: each slot issues the LDS reads of the next slot's MFMA
+      // operands, its own MFMAs, and a slice of the other 32-row block's softmax
+      // (VALU), so that LDS latency and VALU work sit under the matrix cores.
+      // Accumulator row m of a 32-row block qb is Q row pi(m).
+      //
+      // S = Q K^T and dP = dO V^T (block qb, this wave's 32 KV columns): A operands
+      // from LDS, B = K/V rows in registers.
+      auto sdp_off = [&](int qb, int ks) __attribute__((always_inline)) { return a_lane + 32 * qb * ST + 32 * ks; };
+      // dV += P^T dO, dK += dS^T Q: iteration it = (hf, db); its B operands are the
+      // transpose reads of dO and Q at Q/dO rows 16hf + hi + 4j (and + 2).
+      auto bt_off = [&](int qb, int it) __attribute__((always_inline)) {
+        return bt_lane + (32 * qb + 16 * (it / DB)) * ST + 64 * (it % DB);
+      };
+      auto load_bt = [&](int qb, int it, bf16x8& bo, bf16x8& bq) __attribute__((always_inline)) {
+        const int off = bt_off(qb, it);
+        bo = join(lds_tr(sdO, off), lds_tr(sdO, off + 2 * ST));
+        bq = join(lds_tr(sQ, off), lds_tr(sQ, off + 2 * ST));
+      };
+      // Softmax of elements r0, r0+1 of block qb: P = exp2(s log2(e) S - LSE log2(e)),
+      // dS = P (dP - D), both rounded to bf16 into Pb/dSb; after the fourth element of
+      // a row group t, dS^T of the group goes to LDS ([kv][m]).
+      auto softmax2 = [&](int qb, int r0, const floatx16& S, const floatx16& dP, const floatx4& nl, const floatx4& dl,
+                          bf16x8 (&Pb)[2], bf16x8 (&dSb)[2]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        // S = Q K^T and dP = dO V^T for this wave's 32 KV columns.
-        floatx16 S = {}, dP = {};
-#pragma unroll
-        for (int ks = 0; ks < DK; ++ks) {
-          const int off = a_lane + 32 * qb * ST + 32 * ks;
-          S = mfma32(lds_ld16(sQ, off), kreg[ks], S);
-          dP = mfma32(lds_ld16(sdO, off), vreg[ks], dP);
+        for (int r = r0; r < r0 + 2; ++r) {
+          const int t = r >> 2, e = r & 3;
+          // Row of element r: pi(m) = 32qb + 16(t/2) + 2(t%2) + 4e + hi.
+          const int prow = 32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e;
+          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, nl[e]));
+          pr = prow < mask_thr ? 0.f : pr;
+          const float ds = pr * (dP[r] - dl[e]);
+          Pb[r >> 3][r & 7] = static_cast<bf16>(pr);
+          dSb[r >> 3][r & 7] = static_cast<bf16>(ds);
         }
-        if (need_mask) {
-          // Masked entries (key after query, or row/column past N) get S = -inf, so
-          // that P = exp2(-inf) = 0 and dS = 0.
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int qg = q0 + pi16(qb * 32 + 8 * (r >> 2) + 4 * hi + (r & 3));
-            if ((p.causal && kvcol > qg) || kvcol >= N || qg >= N) S[r] = -__builtin_inff();
-          }
-        }
-        // P = exp2(s log2(e) S - LSE log2(e)), dS = P (dP - D); rounded to bf16.
-        bf16x8 Pb[2], dSb[2];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int mrow = qb * 32 + 8 * t + 4 * hi;  // accumulator rows mrow .. mrow+3
-          const floatx4 nl = *reinterpret_cast<const LDS_AS floatx4*>(sNL + mrow * 4);
-          const floatx4 dl = *reinterpret_cast<const LDS_AS floatx4*>(sDL + mrow * 4);
+        if ((r0 & 3) == 2) {
+          const int t = r0 >> 2;
           bf16x4 v4;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * t + e;
-            const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, nl[e]));
-            const float ds = pr * (dP[r] - dl[e]);
-            Pb[r >> 3][r & 7] = static_cast<bf16>(pr);
-            dSb[r >> 3][r & 7] = static_cast<bf16>(ds);
-            v4[e] = dSb[r >> 3][r & 7];
-          }
-          // dS^T of this wave's 32 KV rows to LDS ([kv][m]).
+          for (int e = 0; e < 4; ++e) v4[e] = dSb[t >> 1][4 * (t & 1) + e];
           *reinterpret_cast<LDS_AS bf16x4*>(sdS + ds_wr_lane + 64 * qb + 16 * t) = v4;
         }
-        // dV += P^T dO, dK += dS^T Q. The 8 k-values of k-step hf are accumulator
-        // rows 16hf + 4hi + {0..3} and 16hf + 8 + 4hi + {0..3}: Q/dO rows
-        // 16hf + hi + 4j and 16hf + 2 + hi + 4j.
+      };
+      // -LSE*log2(e) and D of row group t (accumulator rows 8t + 4hi .. +3) of block qb.
+      auto load_rows = [&](int qb, int t, floatx4& nl, floatx4& dl) __attribute__((always_inline)) {
+        const int mrow = qb * 32 + 8 * t + 4 * hi;
+        nl = *reinterpret_cast<const LDS_AS floatx4*>(sNL + mrow * 4);
+        dl = *reinterpret_cast<const LDS_AS floatx4*>(sDL + mrow * 4);
+      };
+      // Softmax of block qb spread over 8 slots (2 elements each); the row terms of
+      // group t are loaded one slot before its first element (ring of 2).
+      auto softmax_slot = [&](int qb, int slot, const floatx16& S, const floatx16& dP, floatx4 (&nlr)[2],
+                              floatx4 (&dlr)[2], bf16x8 (&Pb)[2], bf16x8 (&dSb)[2]) __attribute__((always_inline)) {
+        const int t = slot >> 1;
+        softmax2(qb, 2 * slot, S, dP, nlr[t & 1], dlr[t & 1], Pb, dSb);
+        if ((slot & 1) && t + 1 < 4) load_rows(qb, t + 1, nlr[(t + 1) & 1], dlr[(t + 1) & 1]);
+      };
+#define SLOT() __builtin_amdgcn_sched_barrier(0)
+      floatx16 S0 = {}, dP0 = {}, S1 = {}, dP1 = {};
+      bf16x8 P0[2], dS0[2], P1[2], dS1[2];
+      floatx4 nlr[2], dlr[2];
+      bf16x8 aq[2], ad[2], bo[2], bq[2];
+      static_assert(DK == 8 || DK == 4, "S/dP slots");
+      constexpr int NIT = 2 * DB;  // dV/dK (hf, db) iterations, 2 MFMAs each
+      // Block 0: S/dP (A operands one k-step ahead).
+      aq[0] = lds_ld16(sQ, sdp_off(0, 0));
+      ad[0] = lds_ld16(sdO, sdp_off(0, 0));
+      SLOT();
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            const int off = bt_lane + (32 * qb + 16 * hf) * ST + 64 * db;
-            const bf16x8 bo = join(lds_tr(sdO, off), lds_tr(sdO, off + 2 * ST));
-            const bf16x8 bq = join(lds_tr(sQ, off), lds_tr(sQ, off + 2 * ST));
-            accV[db] = mfma32(Pb[hf], bo, accV[db]);
-            accK[db] = mfma32(dSb[hf], bq, accK[db]);
-          }
+      for (int ks = 0; ks < DK; ++ks) {
+        if (ks + 1 < DK) {
+          aq[(ks + 1) & 1] = lds_ld16(sQ, sdp_off(0, ks + 1));
+          ad[(ks + 1) & 1] = lds_ld16(sdO, sdp_off(0, ks + 1));
+        } else {
+          aq[0] = lds_ld16(sQ, sdp_off(1, 0));
+          ad[0] = lds_ld16(sdO, sdp_off(1, 0));
+          load_rows(0, 0, nlr[0], dlr[0]);
         }
+        S0 = mfma32(aq[ks & 1], kreg[ks], S0);
+        dP0 = mfma32(ad[ks & 1], vreg[ks], dP0);
+        SLOT();
       }
+      // Block 1: S/dP, with block 0's softmax (8 slots of 2 elements over the DK k-steps).
+#pragma unroll
+      for (int ks = 0; ks < DK; ++ks) {
+        if (ks + 1 < DK) {
+          aq[(ks + 1) & 1] = lds_ld16(sQ, sdp_off(1, ks + 1));
+          ad[(ks + 1) & 1] = lds_ld16(sdO, sdp_off(1, ks + 1));
+        } else {
+          load_bt(0, 0, bo[0], bq[0]);
+        }
+        S1 = mfma32(aq[ks & 1], kreg[ks], S1);
+        dP1 = mfma32(ad[ks & 1], vreg[ks], dP1);
+#pragma unroll
+        for (int sl = (8 / DK) * ks; sl < (8 / DK) * (ks + 1); ++sl) softmax_slot(0, sl, S0, dP0, nlr, dlr, P0, dS0);
+        if (ks + 1 == DK) load_rows(1, 0, nlr[0], dlr[0]);
+        SLOT();
+      }
+      // Block 0: dV/dK (B operands one iteration ahead), with block 1's softmax.
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (it + 1 < NIT)
+          load_bt(0, it + 1, bo[(it + 1) & 1], bq[(it + 1) & 1]);
+        else
+          load_bt(1, 0, bo[0], bq[0]);
+        const int hf = it / DB, db = it % DB;
+        mfma32_acc(accV[db], P0[hf], bo[it & 1]);
+        mfma32_acc(accK[db], dS0[hf], bq[it & 1]);
+#pragma unroll
+        for (int sl = (8 / NIT) * it; sl < (8 / NIT) * (it + 1); ++sl) softmax_slot(1, sl, S1, dP1, nlr, dlr, P1, dS1);
+        SLOT();
+      }
+      // Block 1: dV/dK.
+#pragma unroll
+      for (int it = 0; it < NIT; ++it) {
+        if (it + 1 < NIT) load_bt(1, it + 1, bo[(it + 1) & 1], bq[(it + 1) & 1]);
+        const int hf = it / DB, db = it % DB;
+        mfma32_acc(accV[db], P1[hf], bo[it & 1]);
+        mfma32_acc(accK[db], dS1[hf], bq[it & 1]);
+        SLOT();
+      }
+#undef SLOT
       PROF_MARK(kProfBody);
       wait_mem_done();  // next step's tiles landed, previous step's dQ stores acknowledged
       if (have_prev) reduce_signal(pd);
@@ -432,6 +523,7 @@ bwd_main_kernel(BwdParams p) {
     }
 
     // Epilogue: dK = s dK, dV; bf16 stores of this wave's 32 KV rows.
+    mfma_drain();
     bf16* dKg = p.dk + bg * N * D;
     bf16* dVg = p.dv + bg * N * D;
 #pragma unroll

@@ -32,6 +32,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 struct WsLayout {
   size_t dqacc = 0, delta = 0, nlse2 = 0, sem = 0, ctr = 0, total = 0;
   int sem_stride = 0;
+  int row_stride = 0;  // rows per head of D and -LSE*log2(e): N rounded up to the tile
 };
 
 WsLayout ws_layout(int B, int H, int N, int d) {
@@ -41,7 +42,8 @@ WsLayout ws_layout(int B, int H, int N, int d) {
   const int tile = tile_for(N);
   L.sem_stride = static_cast<int>(cdiv(cdiv(N, tile) * (tile / 64) * 4, 32) * 32);
   const size_t dq_bytes = align256(size_t(B) * H * N * d * sizeof(float));
-  const size_t row_bytes = align256(size_t(B) * H * N * sizeof(float));
+  L.row_stride = static_cast<int>(cdiv(N, tile) * tile);
+  const size_t row_bytes = align256(size_t(B) * H * L.row_stride * sizeof(float));
   const size_t sem_bytes = align256(size_t(B) * H * L.sem_stride * sizeof(int));
   L.dqacc = 0;
   L.delta = L.dqacc + dq_bytes;
@@ -252,6 +254,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   pp.delta = delta;
   pp.nlse2 = nlse2;
   pp.rows = int64_t(B) * H * N;
+  pp.N = N;
+  pp.row_stride = L.row_stride;
   pp.sem = sem;
   pp.sem_count = int64_t(B) * H * L.sem_stride;
   pp.ctr = ctr;
@@ -284,6 +288,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.Hkv = Hkv;
   bp.N = N;
   bp.sem_stride = L.sem_stride;
+  bp.row_stride = L.row_stride;
   bp.scale = scale;
   bp.scale_log2 = scale * 1.4426950408889634f;
   bp.causal = causal ? 1 : 0;

@@ -34,6 +34,28 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// dK/dV accumulation with the accumulator pinned in AGPRs: these 32x32 fp32 blocks
+// are touched only by MFMAs for a whole KV item, so keeping them out of the VGPRs
+// leaves the VGPRs to the softmax and to operands in flight. Written as inline
+// assembly (the compiler's MFMA form is one per function); the compiler's hazard
+// checks do not look inside it, so the s_nop covers the wait states a VALU write of
+// an A/B operand needs before an MFMA reads it. Dependent MFMAs on the same
+// accumulator are at least 7 MFMAs apart here.
+__device__ __forceinline__ void mfma32_acc(floatx16& acc, bf16x8 a, bf16x8 b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last MFMA writing an AGPR accumulator and VALU reads of it
+// (v_accvgpr_read): more than the 16-pass pipeline depth.
+__device__ __forceinline__ void mfma_drain() {
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+}
+
+// Scheduling hints (__builtin_amdgcn_sched_group_barrier): the instructions of the
+// current scheduling region are placed in groups of `n` instructions of a class, in
+// the order the calls appear.
+enum SchedClass { kSchedVALU = 0x2, kSchedMFMA = 0x8, kSchedDSRead = 0x100, kSchedDSWrite = 0x200 };
+#define SCHED_GROUP(cls, n) __builtin_amdgcn_sched_group_barrier((cls), (n), 0)
+
 __device__ __forceinline__ unsigned xcc_id() {
   // HW_REG_XCC_ID (hwreg 20), bits [3:0]: the XCD this wave runs on.
   return __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((16 - 1) << 11)) & 0xfu;

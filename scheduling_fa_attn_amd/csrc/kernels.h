@@ -14,9 +14,11 @@ struct PreParams {
   const __bf16* o;
   const __bf16* dO;
   const float* lse;    // [rows] natural-log LSE of the scaled scores
-  float* delta;        // [rows] D = rowsum(dO * O)
-  float* nlse2;        // [rows] -LSE * log2(e)
+  float* delta;        // [B*H][row_stride] D = rowsum(dO * O); 0 past N
+  float* nlse2;        // [B*H][row_stride] -LSE * log2(e); -inf past N
   int64_t rows;        // B * H * N
+  int N;
+  int row_stride;      // N rounded up to the tile
   int* sem;            // ordering semaphores to clear
   int64_t sem_count;
   int* ctr;            // XCD slot counters to clear
@@ -30,8 +32,8 @@ struct BwdParams {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dO;
-  const float* nlse2;  // [B*H*N] -LSE * log2(e)
-  const float* delta;  // [B*H*N] D = rowsum(dO * O)
+  const float* nlse2;  // [B*H][row_stride] -LSE * log2(e); -inf past N
+  const float* delta;  // [B*H][row_stride] D = rowsum(dO * O); 0 past N
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
@@ -44,6 +46,7 @@ struct BwdParams {
   const int4* tasks;
   int B, H, Hkv, N;
   int sem_stride;      // semaphores per (b, h): 4 per 64-row Q step (one per wave), padded
+  int row_stride;      // row stride of nlse2 / delta per (b, h): N rounded up to the tile
   float scale;         // softmax scale s
   float scale_log2;    // s * log2(e)
   int causal;
