@@ -212,8 +212,8 @@ bwd_main_kernel(BwdParams p) {
     PROF_MARK(kProfItem);
 
     // Block t2 of this wave's dQ partial of step `ps` (its dS^T is in LDS buffer
-    // ps & 1) = dS K; accumulator row m of block qb is Q row q0 + pi(32 qb + m).
-    auto dq_block = [&](int ps, int t2) __attribute__((always_inline)) -> floatx16 {
+    // ps & 1) = init + dS K; accumulator row m of block qb is Q row q0 + pi(32 qb + m).
+    auto dq_block = [&](int ps, int t2, const floatx16& init) __attribute__((always_inline)) -> floatx16 {
       const LDS_AS char* sdSp = smem + C::OFF_DS + (ps & 1) * C::DST;
       const int blk = w + NW * t2;
       const int qb = blk / DB, db = blk % DB;
@@ -225,7 +225,7 @@ bwd_main_kernel(BwdParams p) {
         const int koff = kd_lane + 16 * kk * ST + 64 * db;
         bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
       };
-      floatx16 acc = {};
+      floatx16 acc = init;
       bf16x8 a[2], bk[2];
       load(0, a[0], bk[0]);
       __builtin_amdgcn_sched_barrier(0);
@@ -252,9 +252,11 @@ bwd_main_kernel(BwdParams p) {
       return (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e) * D;
     };
 
-    // Reduction of step ps's dQ partial, in three parts so that its memory latency
-    // overlaps other work: (1) wait for the turn and issue the accumulator loads,
-    // (2) add and store, (3) after the stores are acknowledged, pass the turn on.
+    // Reduction of step ps's dQ partial, in parts spread over the next step so that its
+    // memory latency overlaps the step's work: (1) wait for the turn and issue the
+    // accumulator loads, (2) per 32x32 block, the dQ MFMAs start from the loaded
+    // accumulator and the sum is stored, (3) after the stores are acknowledged, pass
+    // the turn on.
     struct Pending {
       int rank, last;
       int* sem;
@@ -264,7 +266,7 @@ bwd_main_kernel(BwdParams p) {
       int rows;       // rows from q0 to N (may be <= 0 for a step past N)
       bool go;
     };
-    auto reduce_begin = [&](int ps, float (&ld)[C::NBLK][16]) __attribute__((always_inline)) -> Pending {
+    auto reduce_begin = [&](int ps, floatx16 (&ld)[C::NBLK]) __attribute__((always_inline)) -> Pending {
       const Quad task = load_quad(tasks, t_begin + ps / SUBS);
       Pending pd;
       pd.rank = task.z;
@@ -287,36 +289,32 @@ bwd_main_kernel(BwdParams p) {
         failed = !pd.go;
       }
       PROF_MARK(kProfWait);
-      if (p.deterministic && pd.go && pd.rank > 0) {
+      // Running sum so far; the first contributor (and the atomic variant) reads
+      // through an empty descriptor, which returns zeros without touching memory.
+      const bool add = p.deterministic && pd.go && pd.rank > 0;
+      const rsrc_t lrs = make_rsrc(pd.acc_g, add ? nrec * 4 : 0);
 #pragma unroll
-        for (int t2 = 0; t2 < C::NBLK; ++t2) {
-          const int vb = 4 * blk_base(t2);
+      for (int t2 = 0; t2 < C::NBLK; ++t2) {
+        const int vb = 4 * blk_base(t2);
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            ld[t2][r] = __builtin_bit_cast(
-                float, __builtin_amdgcn_raw_buffer_load_b32(pd.acc_rs, vb + 4 * row_const(t2, r), 0, kSC1));
-        }
+        for (int r = 0; r < 16; ++r)
+          ld[t2][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, vb + 4 * row_const(t2, r), 0, kSC1));
       }
       return pd;
     };
-    auto reduce_store = [&](const Pending& pd, int t2, const floatx16& dq, const float (&ld)[C::NBLK][16])
-        __attribute__((always_inline)) {
+    auto reduce_store = [&](const Pending& pd, int t2, const floatx16& v) __attribute__((always_inline)) {
       if (!pd.go) return;
       if (!p.deterministic) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int off = blk_base(t2) + row_const(t2, r);
-          if (off < pd.rows * D) atomicAdd(pd.acc_g + off, dq[r]);
+          if (off < pd.rows * D) atomicAdd(pd.acc_g + off, v[r]);
         }
-        return;
-      }
-      const bool add = pd.rank > 0;
-      if (pd.last) {
+      } else if (pd.last) {
         const int vb = 2 * blk_base(t2);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float v = add ? ld[t2][r] + dq[r] : dq[r];
-          const bf16 hv = static_cast<bf16>(v * p.scale);
+          const bf16 hv = static_cast<bf16>(v[r] * p.scale);
           __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), pd.dq_rs,
                                                 vb + 2 * row_const(t2, r), 0, 0);
         }
@@ -324,23 +322,19 @@ bwd_main_kernel(BwdParams p) {
         const int vb = 4 * blk_base(t2);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float v = add ? ld[t2][r] + dq[r] : dq[r];
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), pd.acc_rs, vb + 4 * row_const(t2, r),
-                                                0, 0);
+          // Element copied to a scalar first: a bit-cast of a vector element lvalue
+          // reads the vector's first element.
+          const float x = v[r];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), pd.acc_rs, vb + 4 * row_const(t2, r), 0,
+                                                0);
         }
       }
     };
-    // The whole reduction of step ps except passing the turn on.
-    auto reduce_step = [&](int ps) __attribute__((always_inline)) -> Pending {
-      float ld[C::NBLK][16];
-      const Pending pd = reduce_begin(ps, ld);
+    // dQ blocks [t0, t1) of step ps and their stores.
+    auto reduce_blocks = [&](int ps, const Pending& pd, const floatx16 (&ld)[C::NBLK], int t0, int t1)
+        __attribute__((always_inline)) {
 #pragma unroll
-      for (int t2 = 0; t2 < C::NBLK; ++t2) {
-        const floatx16 dq = dq_block(ps, t2);
-        reduce_store(pd, t2, dq, ld);
-      }
-      PROF_MARK(kProfDq);
-      return pd;
+      for (int t2 = t0; t2 < t1; ++t2) reduce_store(pd, t2, dq_block(ps, t2, ld[t2]));
     };
     // Call after wait_mem_done(): this wave's accumulator stores are in the L2.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
@@ -361,17 +355,15 @@ bwd_main_kernel(BwdParams p) {
       const int j = task.y;
       const int q0 = j * BC + (s % SUBS) * BQ;
 
-      // Previous step's dQ partial and its reduction: wait for the turn and issue the
-      // accumulator loads first, then run the dQ MFMAs while the loads are in flight,
-      // then add and store. The stores are acknowledged during this step's body; the
-      // turn is passed on after the body.
+      // Previous step's reduction, part 1: wait for the turn, issue the accumulator
+      // loads. The next step's copies go after them: waiting for those loads must not
+      // wait for the copies (the vector-memory counter is in order).
       Pending pd;
+      floatx16 ld[C::NBLK];
       const bool have_prev = s > 0;
-      if (have_prev) pd = reduce_step(s - 1);
-      // The next step's copies go after the accumulator loads were consumed: waiting
-      // for those loads must not wait for the copies (the vector-memory counter is in
-      // order).
+      if (have_prev) pd = reduce_begin(s - 1, ld);
       if (s + 1 < n_steps) issue_step(s + 1);
+      constexpr int kBlkA = (C::NBLK + 1) / 2;  // dQ blocks reduced after the first S/dP block
 
       const LDS_AS char* sQ = smem + C::OFF_Q + buf * C::QT;
       const LDS_AS char* sdO = smem + C::OFF_DO + buf * C::QT;
@@ -467,6 +459,10 @@ bwd_main_kernel(BwdParams p) {
         dP0 = mfma32(ad[ks & 1], vreg[ks], dP0);
         SLOT();
       }
+      // Previous step's reduction, part 2 (first blocks): the loads have had block 0's
+      // S/dP to arrive.
+      if (have_prev) reduce_blocks(s - 1, pd, ld, 0, kBlkA);
+      SLOT();
       // Block 1: S/dP, with block 0's softmax (8 slots of 2 elements over the DK k-steps).
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
@@ -483,6 +479,8 @@ bwd_main_kernel(BwdParams p) {
         if (ks + 1 == DK) load_rows(1, 0, nlr[0], dlr[0]);
         SLOT();
       }
+      if (have_prev) reduce_blocks(s - 1, pd, ld, kBlkA, C::NBLK);
+      SLOT();
       // Block 0: dV/dK (B operands one iteration ahead), with block 1's softmax.
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
@@ -516,7 +514,10 @@ bwd_main_kernel(BwdParams p) {
     }
     // The item's last step: its dQ partial and reduction.
     {
-      const Pending pd = reduce_step(n_steps - 1);
+      floatx16 ld[C::NBLK];
+      const Pending pd = reduce_begin(n_steps - 1, ld);
+      reduce_blocks(n_steps - 1, pd, ld, 0, C::NBLK);
+      PROF_MARK(kProfDq);
       wait_mem_done();
       reduce_signal(pd);
       PROF_MARK(kProfReduce);
