@@ -362,7 +362,6 @@ bwd_main_kernel(BwdParams p) {
       floatx16 ld[C::NBLK];
       const bool have_prev = s > 0;
       if (have_prev) pd = reduce_begin(s - 1, ld);
-      if (s + 1 < n_steps) issue_step(s + 1);
       constexpr int kBlkA = (C::NBLK + 1) / 2;  // dQ blocks reduced after the first S/dP block
 
       const LDS_AS char* sQ = smem + C::OFF_Q + buf * C::QT;
@@ -373,9 +372,17 @@ bwd_main_kernel(BwdParams p) {
       // Only the diagonal task of a causal mask needs a mask: rows past N have
       // -LSE*log2(e) = -inf (P = 0) and columns past N meet zero K rows in dQ.
       const bool diag = p.causal && j == kv_tile;
-      // Causal diagonal: P = 0 (so dS = 0) where the key comes after the query, i.e.
-      // where pi(m) < kvcol - q0. Branch-free: elsewhere the threshold is below every row.
-      const int mask_thr = diag ? kvcol - q0 - hi : -1;  // compared with pi(m) - hi
+      // Causal diagonal (diagonal steps only): S = -inf, hence P = 0 and dS = 0, where the
+      // key comes after the query, i.e. where pi(m) < kvcol - q0. Row of element r of
+      // block qb: pi(m) = 32qb + 16(t/2) + 2(t%2) + 4e + hi (r = 4t + e).
+      const int mask_thr = kvcol - q0 - hi;
+      auto mask_diag = [&](int qb, floatx16& S) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = r >> 2, e = r & 3;
+          if (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e < mask_thr) S[r] = -__builtin_inff();
+        }
+      };
 
       // The step body as an explicit software pipeline of "slots" separated by
       // scheduling barriers: each slot issues the LDS reads of the next slot's MFMA
@@ -404,10 +411,7 @@ bwd_main_kernel(BwdParams p) {
 #pragma unroll
         for (int r = r0; r < r0 + 2; ++r) {
           const int t = r >> 2, e = r & 3;
-          // Row of element r: pi(m) = 32qb + 16(t/2) + 2(t%2) + 4e + hi.
-          const int prow = 32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e;
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, nl[e]));
-          pr = prow < mask_thr ? 0.f : pr;
+          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, nl[e]));
           const float ds = pr * (dP[r] - dl[e]);
           Pb[r >> 3][r & 7] = static_cast<bf16>(pr);
           dSb[r >> 3][r & 7] = static_cast<bf16>(ds);
@@ -462,6 +466,7 @@ bwd_main_kernel(BwdParams p) {
       // Previous step's reduction, part 2 (first blocks): the loads have had block 0's
       // S/dP to arrive.
       if (have_prev) reduce_blocks(s - 1, pd, ld, 0, kBlkA);
+      if (diag) mask_diag(0, S0);
       SLOT();
       // Block 1: S/dP, with block 0's softmax (8 slots of 2 elements over the DK k-steps).
 #pragma unroll
@@ -479,7 +484,16 @@ bwd_main_kernel(BwdParams p) {
         if (ks + 1 == DK) load_rows(1, 0, nlr[0], dlr[0]);
         SLOT();
       }
-      if (have_prev) reduce_blocks(s - 1, pd, ld, kBlkA, C::NBLK);
+      if (have_prev) {
+        // Rest of the previous step's reduction; once its stores are acknowledged the
+        // turn is passed on, half a step earlier than the step's end.
+        reduce_blocks(s - 1, pd, ld, kBlkA, C::NBLK);
+        wait_mem_done();
+        reduce_signal(pd);
+      }
+      // The next step's copies: after every vector-memory load this step waits for.
+      if (s + 1 < n_steps) issue_step(s + 1);
+      if (diag) mask_diag(1, S1);
       SLOT();
       // Block 0: dV/dK (B operands one iteration ahead), with block 1's softmax.
 #pragma unroll
@@ -506,8 +520,7 @@ bwd_main_kernel(BwdParams p) {
       }
 #undef SLOT
       PROF_MARK(kProfBody);
-      wait_mem_done();  // next step's tiles landed, previous step's dQ stores acknowledged
-      if (have_prev) reduce_signal(pd);
+      wait_mem_done();  // next step's tiles have landed
       PROF_MARK(kProfReduce);
       __syncthreads();  // dS^T of all waves and the next step's tiles are visible
       PROF_MARK(kProfBarrier);
