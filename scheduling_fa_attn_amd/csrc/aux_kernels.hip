@@ -10,10 +10,12 @@
 namespace dash {
 
 // ---------------------------------------------------------------------------------
-// Preprocess: D[row] = sum_e dO[row, e] * O[row, e] in fp32 with a fixed reduction
+// Preprocess: -D[row] = -sum_e dO[row, e] * O[row, e] in fp32 with a fixed reduction
 // tree and nl[row] = -LSE[row] * log2(e), stored with the head's rows padded to the
-// tile (padding: D = 0, nl = -inf); clears the ordering semaphores and the XCD
+// tile (padding: -D = 0, nl = -inf); clears the ordering semaphores and the XCD
 // slot counters; for the atomic variant also clears the fp32 dQ accumulator.
+// (-D is stored negated because the main kernel starts its dP = dO V^T accumulation
+// from it, which yields dP - D directly.)
 // ---------------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
@@ -33,7 +35,7 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
     for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, LPR);
     if (part == 0) {
       const int64_t out = (row / p.N) * p.row_stride + row % p.N;
-      p.delta[out] = acc;
+      p.neg_delta[out] = -acc;
       p.nlse2[out] = -p.lse[row] * 1.4426950408889634f;
     }
   }
@@ -43,7 +45,7 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
     const int64_t heads = p.rows / p.N;
     for (int64_t x = tid; x < heads * pad; x += nthreads) {
       const int64_t out = (x / pad) * p.row_stride + p.N + x % pad;
-      p.delta[out] = 0.f;
+      p.neg_delta[out] = 0.f;
       p.nlse2[out] = -__builtin_inff();
     }
   }
@@ -57,17 +59,23 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 }
 
 // dQ = bf16(s * dQacc), for the atomic variant (the ordered variant writes dQ from
-// the last contributor of each tile).
+// the last contributor of each tile); the accumulator is row-major with row_stride
+// rows per head, of which the first N are output.
 __global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                      int64_t count, float scale) {
+                                                      int64_t quads, int N, int row_stride, int d, float scale) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
-  for (int64_t x = tid; x < count / 4; x += nthreads) {
-    const floatx4 a = reinterpret_cast<const floatx4*>(acc)[x];
+  const int qpr = d / 4;  // float4 per row
+  for (int64_t x = tid; x < quads; x += nthreads) {
+    const int64_t row_all = x / qpr;
+    const int col = static_cast<int>(x % qpr) * 4;
+    const int64_t bh = row_all / N;
+    const int row = static_cast<int>(row_all % N);
+    const floatx4 a = *reinterpret_cast<const floatx4*>(acc + (bh * row_stride + row) * d + col);
     bf16x4 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) r[e] = static_cast<bf16>(a[e] * scale);
-    reinterpret_cast<bf16x4*>(dq)[x] = r;
+    *reinterpret_cast<bf16x4*>(dq + row_all * d + col) = r;
   }
 }
 
@@ -87,9 +95,13 @@ hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_dq_cast(const float* acc, void* dq, int64_t count, float scale, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL(dq_cast_kernel, dim3(grid), dim3(256), 0, stream, acc, reinterpret_cast<bf16*>(dq), count,
-                     scale);
+hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
+                          hipStream_t stream) {
+  const int64_t quads = heads * N * (d / 4);
+  int64_t grid = (quads + 255) / 256;
+  grid = grid < 1 ? 1 : (grid > 8192 ? 8192 : grid);
+  hipLaunchKernelGGL(dq_cast_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
+                     reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale);
   return hipGetLastError();
 }
 

@@ -7,6 +7,7 @@
 // section "In the real world"): per (batch b, query head h, key/value head g):
 //   P  = exp(s Q K^T - LSE)   (recomputed, masked entries 0)
 //   dV = P^T dO,  dP = dO V^T,  D = rowsum(dO * O),  dS = P * (dP - D)
+//   (the dP accumulation starts from -D, so the accumulator holds dP - D)
 //   dK = s dS^T Q,  dQ = s dS K
 // Work decomposition (section 2.1, Fig. 1 left; section 3.1): a workgroup owns one
 // KV tile at a time and keeps its dK/dV in registers while it visits Q tiles; the
@@ -22,7 +23,7 @@
 // - KV tile = 32*NW rows; wave w owns KV rows [32w, 32w+32): their dK, dV (fp32) stay
 //   in AGPR/VGPR accumulators for the whole item, and their K, V rows sit in
 //   registers as MFMA B operands. Q tiles are visited in 64-row steps.
-// - Q, dO (64 x d), -LSE*log2(e) and D of the next step are copied global -> LDS with
+// - Q, dO (64 x d), -LSE*log2(e) and -D of the next step are copied global -> LDS with
 //   global_load_lds_dwordx4 while the current step computes (double buffer).
 // - All five contractions use v_mfma_f32_32x32x16_bf16. Operand layouts (A: lane
 //   holds row lane%32, 8 consecutive k; B: column lane%32, 8 consecutive k; D:
@@ -35,11 +36,14 @@
 //     dK += dS^T Q  likewise with dS and Q
 //     dQ = dS K     A = dS via an LDS round trip (stored [kv][q], read transposed),
 //                   B = K read transposed from the item's K tile in LDS
-// - LDS tiles are XOR-swizzled in 16-byte chunks so that both the row reads
-//   (ds_read_b128) and the transpose reads hit distinct banks.
+// - LDS tiles have one 16-byte pad chunk per row and operand rows are visited in a
+//   permuted order (pi16), so that both the row reads (ds_read_b128) and the
+//   transpose reads hit distinct banks with addresses "lane base + constant".
 // - The dQ partial of a 64-row step is split over the waves by 32-column blocks;
 //   every wave waits for and passes on its own turn (one semaphore per step and
-//   wave), so the ordered reduction needs no workgroup barrier.
+//   wave), so the ordered reduction needs no workgroup barrier. The ordered variant's
+//   fp32 accumulator is kept in the MFMA accumulator's order (kDqBlock), so a wave
+//   reads and writes a block with four contiguous 1 KiB accesses at fixed offsets.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -73,8 +77,8 @@ struct BwdCfg {
   static constexpr int OFF_DO = OFF_Q + 2 * QT;          // 2 buffers
   static constexpr int OFF_DS = OFF_DO + 2 * QT;         // 2 buffers
   static constexpr int OFF_K = OFF_DS + 2 * DST;         // K tile [BC][D]
-  static constexpr int OFF_NL = OFF_K + BC * ST;         // 2 x 64 floats
-  static constexpr int OFF_DL = OFF_NL + 2 * 256;        // 2 x 64 floats
+  static constexpr int OFF_NL = OFF_K + BC * ST;         // 2 x 64 floats: -LSE*log2(e)
+  static constexpr int OFF_DL = OFF_NL + 2 * 256;        // 2 x 64 floats: -D
   static constexpr int OFF_MISC = OFF_DL + 2 * 256;
   static constexpr int BYTES = OFF_MISC + 64;
   static_assert(NBLK >= 1 && NBLK * NW == 2 * DB, "dQ blocks must split evenly over waves");
@@ -156,7 +160,7 @@ bwd_main_kernel(BwdParams p) {
     const bf16* Kg = p.k + bg * N * D;
     const bf16* Vg = p.v + bg * N * D;
 
-    // Issues the global->LDS copies of step s (Q, dO, -LSE*log2e, D) into buffer s & 1.
+    // Issues the global->LDS copies of step s (Q, dO, -LSE*log2e, -D) into buffer s & 1.
     auto issue_step = [&](int s) __attribute__((always_inline)) {
       const Quad task = load_quad(tasks, t_begin + s / SUBS);
       const int q0 = task.y * BC + (s % SUBS) * BQ;
@@ -166,7 +170,7 @@ bwd_main_kernel(BwdParams p) {
       qcopy.issue(smem + C::OFF_DO + buf * C::QT, p.dO + bh * N * D, q0, N, w);
       // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
       if (w == 0) dma4(p.nlse2 + bh * p.row_stride + q0, row_lane, smem + C::OFF_NL + buf * 256);
-      if (w == 1) dma4(p.delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + buf * 256);
+      if (w == 1) dma4(p.neg_delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + buf * 256);
     };
 
     // Item prologue: K tile to LDS, first step's tiles, K/V rows of this wave to registers.
@@ -239,9 +243,10 @@ bwd_main_kernel(BwdParams p) {
     };
 
     // dQ addressing. Element r of this wave's block t2 at a step sits at row
-    // q0 + 32 qb + 16 (t / 2) + 2 (t % 2) + hi + 4 e (r = 4 t + e) and column 32 db + l32.
-    // Buffer descriptors start at row q0, so the per-element byte offset is a per-lane
-    // base (row hi, column) plus a compile-time constant.
+    // q0 + 32 qb + 16 (t / 2) + 2 (t % 2) + hi + 4 e (r = 4 t + e) and column 32 db + l32
+    // (the bf16 output and the atomic variant's row-major accumulator). In the ordered
+    // variant's accumulator the block is number w + NW t2 of the step's 2 DB blocks and
+    // elements 4 t .. 4 t + 3 of this lane sit at float 256 t + 4 lane (kDqBlock).
     auto blk_base = [&](int t2) __attribute__((always_inline)) {
       const int blk = w + NW * t2;
       return hi * D + (blk % DB) * 32 + l32;
@@ -251,6 +256,8 @@ bwd_main_kernel(BwdParams p) {
       const int t = r >> 2, e = r & 3;
       return (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e) * D;
     };
+    const int acc_lane = lane * 16;  // byte offset of this lane's first 4 floats in a block
+    constexpr int kBlkBytes = kDqBlock * 4;
 
     // Reduction of step ps's dQ partial, in parts spread over the next step so that its
     // memory latency overlaps the step's work: (1) wait for the turn and issue the
@@ -260,10 +267,9 @@ bwd_main_kernel(BwdParams p) {
     struct Pending {
       int rank, last;
       int* sem;
-      rsrc_t acc_rs;  // fp32 accumulator rows [q0, N) of (b, h)
+      rsrc_t acc_rs;  // the step's 2 DB fp32 accumulator blocks
       rsrc_t dq_rs;   // bf16 dQ rows [q0, N) of (b, h)
-      float* acc_g;   // accumulator row q0 (atomic variant)
-      int rows;       // rows from q0 to N (may be <= 0 for a step past N)
+      float* acc_g;   // atomic variant: accumulator row q0 (row-major)
       bool go;
     };
     auto reduce_begin = [&](int ps, floatx16 (&ld)[C::NBLK]) __attribute__((always_inline)) -> Pending {
@@ -273,11 +279,12 @@ bwd_main_kernel(BwdParams p) {
       pd.last = task.w;
       const int q0s = task.y * BC + (ps % SUBS) * BQ;
       const int64_t bh = static_cast<int64_t>(b) * H + task.x;
-      pd.rows = N - q0s;
-      const int nrec = pd.rows > 0 ? pd.rows * D : 0;
-      pd.acc_g = p.dqacc + bh * N * D + static_cast<int64_t>(q0s) * D;
-      pd.acc_rs = make_rsrc(pd.acc_g, nrec * 4);
-      pd.dq_rs = make_rsrc(p.dq + bh * N * D + static_cast<int64_t>(q0s) * D, nrec * 2);
+      const int rows = N - q0s;  // may be <= 0 for a step past N
+      // Accumulator rows are padded to the tile, so the step's blocks always exist.
+      float* const acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
+      pd.acc_g = p.dqacc + (bh * p.row_stride + q0s) * D;
+      pd.acc_rs = make_rsrc(acc_blk, 2 * DB * kBlkBytes);
+      pd.dq_rs = make_rsrc(p.dq + bh * N * D + static_cast<int64_t>(q0s) * D, rows > 0 ? rows * D * 2 : 0);
       pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
       pd.go = !failed;
       if (p.deterministic && pd.go && pd.rank > 0) {
@@ -292,24 +299,29 @@ bwd_main_kernel(BwdParams p) {
       // Running sum so far; the first contributor (and the atomic variant) reads
       // through an empty descriptor, which returns zeros without touching memory.
       const bool add = p.deterministic && pd.go && pd.rank > 0;
-      const rsrc_t lrs = make_rsrc(pd.acc_g, add ? nrec * 4 : 0);
+      const rsrc_t lrs = make_rsrc(acc_blk, add ? 2 * DB * kBlkBytes : 0);
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
-        const int vb = 4 * blk_base(t2);
+        const int soff = (w + NW * t2) * kBlkBytes;  // wave-uniform block offset
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          ld[t2][r] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrs, vb + 4 * row_const(t2, r), 0, kSC1));
+        for (int i = 0; i < 4; ++i) {
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_lane + 1024 * i, soff, kSC1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const unsigned u = v[e];
+            ld[t2][4 * i + e] = __builtin_bit_cast(float, u);
+          }
+        }
       }
       return pd;
     };
     auto reduce_store = [&](const Pending& pd, int t2, const floatx16& v) __attribute__((always_inline)) {
       if (!pd.go) return;
       if (!p.deterministic) {
+        // Rows past N exist (padding) and are never output.
+        float* dst = pd.acc_g + blk_base(t2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int off = blk_base(t2) + row_const(t2, r);
-          if (off < pd.rows * D) atomicAdd(pd.acc_g + off, v[r]);
-        }
+        for (int r = 0; r < 16; ++r) atomicAdd(dst + row_const(t2, r), v[r]);
       } else if (pd.last) {
         const int vb = 2 * blk_base(t2);
 #pragma unroll
@@ -319,14 +331,18 @@ bwd_main_kernel(BwdParams p) {
                                                 vb + 2 * row_const(t2, r), 0, 0);
         }
       } else {
-        const int vb = 4 * blk_base(t2);
+        const int soff = (w + NW * t2) * kBlkBytes;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          // Element copied to a scalar first: a bit-cast of a vector element lvalue
-          // reads the vector's first element.
-          const float x = v[r];
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, x), pd.acc_rs, vb + 4 * row_const(t2, r), 0,
-                                                0);
+        for (int i = 0; i < 4; ++i) {
+          u32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // Element copied to a scalar first: a bit-cast of a vector element lvalue
+            // reads the vector's first element.
+            const float f = v[4 * i + e];
+            x[e] = __builtin_bit_cast(unsigned, f);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_lane + 1024 * i, soff, 0);
         }
       }
     };
@@ -404,44 +420,53 @@ bwd_main_kernel(BwdParams p) {
         bq = join(lds_tr(sQ, off), lds_tr(sQ, off + 2 * ST));
       };
       // Softmax of elements r0, r0+1 of block qb: P = exp2(s log2(e) S - LSE log2(e)),
-      // dS = P (dP - D), both rounded to bf16 into Pb/dSb; after the fourth element of
-      // a row group t, dS^T of the group goes to LDS ([kv][m]).
-      auto softmax2 = [&](int qb, int r0, const floatx16& S, const floatx16& dP, const floatx4& nl, const floatx4& dl,
-                          bf16x8 (&Pb)[2], bf16x8 (&dSb)[2]) __attribute__((always_inline)) {
-#pragma unroll
-        for (int r = r0; r < r0 + 2; ++r) {
-          const int t = r >> 2, e = r & 3;
-          const float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, nl[e]));
-          const float ds = pr * (dP[r] - dl[e]);
-          Pb[r >> 3][r & 7] = static_cast<bf16>(pr);
-          dSb[r >> 3][r & 7] = static_cast<bf16>(ds);
-        }
+      // dS = P (dP - D) (the dP accumulator already holds dP - D), both rounded to bf16
+      // in pairs into Pw/dSw; after the fourth element of a row group t, dS^T of the
+      // group goes to LDS ([kv][m]).
+      auto softmax2 = [&](int qb, int r0, const floatx16& S, const floatx16& dP, const floatx4& nl, u32x4 (&Pw)[2],
+                          u32x4 (&dSw)[2]) __attribute__((always_inline)) {
+        const int e0 = r0 & 3;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r0], p.scale_log2, nl[e0]));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r0 + 1], p.scale_log2, nl[e0 + 1]));
+        Pw[r0 >> 3][(r0 & 7) >> 1] = pack_bf16(p0, p1);
+        dSw[r0 >> 3][(r0 & 7) >> 1] = pack_bf16(p0 * dP[r0], p1 * dP[r0 + 1]);
         if ((r0 & 3) == 2) {
           const int t = r0 >> 2;
-          bf16x4 v4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v4[e] = dSb[t >> 1][4 * (t & 1) + e];
-          *reinterpret_cast<LDS_AS bf16x4*>(sdS + ds_wr_lane + 64 * qb + 16 * t) = v4;
+          u32x2 v2;
+          v2[0] = dSw[t >> 1][2 * (t & 1)];
+          v2[1] = dSw[t >> 1][2 * (t & 1) + 1];
+          *reinterpret_cast<LDS_AS u32x2*>(sdS + ds_wr_lane + 64 * qb + 16 * t) = v2;
         }
       };
-      // -LSE*log2(e) and D of row group t (accumulator rows 8t + 4hi .. +3) of block qb.
-      auto load_rows = [&](int qb, int t, floatx4& nl, floatx4& dl) __attribute__((always_inline)) {
-        const int mrow = qb * 32 + 8 * t + 4 * hi;
-        nl = *reinterpret_cast<const LDS_AS floatx4*>(sNL + mrow * 4);
-        dl = *reinterpret_cast<const LDS_AS floatx4*>(sDL + mrow * 4);
+      // -LSE*log2(e) of row group t (accumulator rows 8t + 4hi .. +3) of block qb.
+      auto load_nl = [&](int qb, int t) __attribute__((always_inline)) -> floatx4 {
+        return *reinterpret_cast<const LDS_AS floatx4*>(sNL + (qb * 32 + 8 * t + 4 * hi) * 4);
+      };
+      // -D of the 16 accumulator rows of block qb, in accumulator order: the start
+      // value of the block's dP accumulation.
+      auto load_negd = [&](int qb) __attribute__((always_inline)) -> floatx16 {
+        floatx16 x;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const floatx4 d4 = *reinterpret_cast<const LDS_AS floatx4*>(sDL + (qb * 32 + 8 * t + 4 * hi) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[4 * t + e] = d4[e];
+        }
+        return x;
       };
       // Softmax of block qb spread over 8 slots (2 elements each); the row terms of
       // group t are loaded one slot before its first element (ring of 2).
       auto softmax_slot = [&](int qb, int slot, const floatx16& S, const floatx16& dP, floatx4 (&nlr)[2],
-                              floatx4 (&dlr)[2], bf16x8 (&Pb)[2], bf16x8 (&dSb)[2]) __attribute__((always_inline)) {
+                              u32x4 (&Pw)[2], u32x4 (&dSw)[2]) __attribute__((always_inline)) {
         const int t = slot >> 1;
-        softmax2(qb, 2 * slot, S, dP, nlr[t & 1], dlr[t & 1], Pb, dSb);
-        if ((slot & 1) && t + 1 < 4) load_rows(qb, t + 1, nlr[(t + 1) & 1], dlr[(t + 1) & 1]);
+        softmax2(qb, 2 * slot, S, dP, nlr[t & 1], Pw, dSw);
+        if ((slot & 1) && t + 1 < 4) nlr[(t + 1) & 1] = load_nl(qb, t + 1);
       };
 #define SLOT() __builtin_amdgcn_sched_barrier(0)
-      floatx16 S0 = {}, dP0 = {}, S1 = {}, dP1 = {};
-      bf16x8 P0[2], dS0[2], P1[2], dS1[2];
-      floatx4 nlr[2], dlr[2];
+      floatx16 S0 = {}, S1 = {};
+      floatx16 dP0 = load_negd(0), dP1;
+      u32x4 P0[2], dS0[2], P1[2], dS1[2];
+      floatx4 nlr[2];
       bf16x8 aq[2], ad[2], bo[2], bq[2];
       static_assert(DK == 8 || DK == 4, "S/dP slots");
       constexpr int NIT = 2 * DB;  // dV/dK (hf, db) iterations, 2 MFMAs each
@@ -457,8 +482,9 @@ bwd_main_kernel(BwdParams p) {
         } else {
           aq[0] = lds_ld16(sQ, sdp_off(1, 0));
           ad[0] = lds_ld16(sdO, sdp_off(1, 0));
-          load_rows(0, 0, nlr[0], dlr[0]);
+          nlr[0] = load_nl(0, 0);
         }
+        if (ks == DK / 2) dP1 = load_negd(1);
         S0 = mfma32(aq[ks & 1], kreg[ks], S0);
         dP0 = mfma32(ad[ks & 1], vreg[ks], dP0);
         SLOT();
@@ -480,8 +506,8 @@ bwd_main_kernel(BwdParams p) {
         S1 = mfma32(aq[ks & 1], kreg[ks], S1);
         dP1 = mfma32(ad[ks & 1], vreg[ks], dP1);
 #pragma unroll
-        for (int sl = (8 / DK) * ks; sl < (8 / DK) * (ks + 1); ++sl) softmax_slot(0, sl, S0, dP0, nlr, dlr, P0, dS0);
-        if (ks + 1 == DK) load_rows(1, 0, nlr[0], dlr[0]);
+        for (int sl = (8 / DK) * ks; sl < (8 / DK) * (ks + 1); ++sl) softmax_slot(0, sl, S0, dP0, nlr, P0, dS0);
+        if (ks + 1 == DK) nlr[0] = load_nl(1, 0);
         SLOT();
       }
       if (have_prev) {
@@ -503,10 +529,10 @@ bwd_main_kernel(BwdParams p) {
         else
           load_bt(1, 0, bo[0], bq[0]);
         const int hf = it / DB, db = it % DB;
-        mfma32_acc(accV[db], P0[hf], bo[it & 1]);
-        mfma32_acc(accK[db], dS0[hf], bq[it & 1]);
+        mfma32_acc(accV[db], as_bf16x8(P0[hf]), bo[it & 1]);
+        mfma32_acc(accK[db], as_bf16x8(dS0[hf]), bq[it & 1]);
 #pragma unroll
-        for (int sl = (8 / NIT) * it; sl < (8 / NIT) * (it + 1); ++sl) softmax_slot(1, sl, S1, dP1, nlr, dlr, P1, dS1);
+        for (int sl = (8 / NIT) * it; sl < (8 / NIT) * (it + 1); ++sl) softmax_slot(1, sl, S1, dP1, nlr, P1, dS1);
         SLOT();
       }
       // Block 1: dV/dK.
@@ -514,8 +540,8 @@ bwd_main_kernel(BwdParams p) {
       for (int it = 0; it < NIT; ++it) {
         if (it + 1 < NIT) load_bt(1, it + 1, bo[(it + 1) & 1], bq[(it + 1) & 1]);
         const int hf = it / DB, db = it % DB;
-        mfma32_acc(accV[db], P1[hf], bo[it & 1]);
-        mfma32_acc(accK[db], dS1[hf], bq[it & 1]);
+        mfma32_acc(accV[db], as_bf16x8(P1[hf]), bo[it & 1]);
+        mfma32_acc(accK[db], as_bf16x8(dS1[hf]), bq[it & 1]);
         SLOT();
       }
 #undef SLOT

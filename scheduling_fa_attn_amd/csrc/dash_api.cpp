@@ -30,9 +30,9 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t dqacc = 0, delta = 0, nlse2 = 0, sem = 0, ctr = 0, total = 0;
+  size_t dqacc = 0, neg_delta = 0, nlse2 = 0, sem = 0, ctr = 0, total = 0;
   int sem_stride = 0;
-  int row_stride = 0;  // rows per head of D and -LSE*log2(e): N rounded up to the tile
+  int row_stride = 0;  // rows per head of -D, -LSE*log2(e) and the dQ accumulator: N rounded up to the tile
 };
 
 WsLayout ws_layout(int B, int H, int N, int d) {
@@ -41,13 +41,13 @@ WsLayout ws_layout(int B, int H, int N, int d) {
   // ceil(N / tile) tiles of a head (the last tile's second step may lie past N).
   const int tile = tile_for(N);
   L.sem_stride = static_cast<int>(cdiv(cdiv(N, tile) * (tile / 64) * 4, 32) * 32);
-  const size_t dq_bytes = align256(size_t(B) * H * N * d * sizeof(float));
   L.row_stride = static_cast<int>(cdiv(N, tile) * tile);
+  const size_t dq_bytes = align256(size_t(B) * H * L.row_stride * d * sizeof(float));
   const size_t row_bytes = align256(size_t(B) * H * L.row_stride * sizeof(float));
   const size_t sem_bytes = align256(size_t(B) * H * L.sem_stride * sizeof(int));
   L.dqacc = 0;
-  L.delta = L.dqacc + dq_bytes;
-  L.nlse2 = L.delta + row_bytes;
+  L.neg_delta = L.dqacc + dq_bytes;
+  L.nlse2 = L.neg_delta + row_bytes;
   L.sem = L.nlse2 + row_bytes;
   L.ctr = L.sem + sem_bytes;
   L.total = L.ctr + kCtrInts * sizeof(int);
@@ -242,7 +242,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   }
   char* ws = static_cast<char*>(workspace);
   float* dqacc = reinterpret_cast<float*>(ws + L.dqacc);
-  float* delta = reinterpret_cast<float*>(ws + L.delta);
+  float* neg_delta = reinterpret_cast<float*>(ws + L.neg_delta);
   float* nlse2 = reinterpret_cast<float*>(ws + L.nlse2);
   int* sem = reinterpret_cast<int*>(ws + L.sem);
   int* ctr = reinterpret_cast<int*>(ws + L.ctr);
@@ -251,7 +251,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   pp.o = static_cast<const __bf16*>(o);
   pp.dO = static_cast<const __bf16*>(dO);
   pp.lse = lse;
-  pp.delta = delta;
+  pp.neg_delta = neg_delta;
   pp.nlse2 = nlse2;
   pp.rows = int64_t(B) * H * N;
   pp.N = N;
@@ -261,7 +261,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   pp.ctr = ctr;
   pp.ctr_count = kCtrInts;
   pp.dqacc_zero = deterministic ? nullptr : dqacc;
-  pp.zero_count = int64_t(B) * H * N * d;
+  pp.zero_count = int64_t(B) * H * L.row_stride * d;
   const int64_t pre_threads = pp.rows * (d / 8);
   const int pre_grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(cdiv(pre_threads, 256), 1), 4096));
   if (dash::launch_preprocess(pp, d, pre_grid, stream) != hipSuccess) return DASH_ERR_HIP;
@@ -272,7 +272,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.v = static_cast<const __bf16*>(v);
   bp.dO = static_cast<const __bf16*>(dO);
   bp.nlse2 = nlse2;
-  bp.delta = delta;
+  bp.neg_delta = neg_delta;
   bp.dq = static_cast<__bf16*>(dq);
   bp.dk = static_cast<__bf16*>(dk);
   bp.dv = static_cast<__bf16*>(dv);
@@ -304,9 +304,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (e != hipSuccess) return DASH_ERR_HIP;
   if (ev_stop && hipEventRecord(static_cast<hipEvent_t>(ev_stop), stream) != hipSuccess) return DASH_ERR_HIP;
   if (!deterministic) {
-    const int64_t count = int64_t(B) * H * N * d;
-    const int grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(cdiv(count / 4, 256), 1), 8192));
-    if (dash::launch_dq_cast(dqacc, dq, count, scale, grid, stream) != hipSuccess) return DASH_ERR_HIP;
+    if (dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream) != hipSuccess)
+      return DASH_ERR_HIP;
   }
   return DASH_OK;
 }

@@ -14,7 +14,7 @@ struct PreParams {
   const __bf16* o;
   const __bf16* dO;
   const float* lse;    // [rows] natural-log LSE of the scaled scores
-  float* delta;        // [B*H][row_stride] D = rowsum(dO * O); 0 past N
+  float* neg_delta;    // [B*H][row_stride] -D = -rowsum(dO * O); 0 past N
   float* nlse2;        // [B*H][row_stride] -LSE * log2(e); -inf past N
   int64_t rows;        // B * H * N
   int N;
@@ -33,11 +33,11 @@ struct BwdParams {
   const __bf16* v;
   const __bf16* dO;
   const float* nlse2;  // [B*H][row_stride] -LSE * log2(e); -inf past N
-  const float* delta;  // [B*H][row_stride] D = rowsum(dO * O); 0 past N
+  const float* neg_delta;  // [B*H][row_stride] -D = -rowsum(dO * O); 0 past N
   __bf16* dq;
   __bf16* dk;
   __bf16* dv;
-  float* dqacc;
+  float* dqacc;        // fp32 dQ accumulator (layouts described at kDqBlock)
   int* sem;
   int* ctr;
   int* err;
@@ -46,7 +46,7 @@ struct BwdParams {
   const int4* tasks;
   int B, H, Hkv, N;
   int sem_stride;      // semaphores per (b, h): 4 per 64-row Q step (one per wave), padded
-  int row_stride;      // row stride of nlse2 / delta per (b, h): N rounded up to the tile
+  int row_stride;      // rows per (b, h) of nlse2, neg_delta and dqacc: N rounded up to the tile
   float scale;         // softmax scale s
   float scale_log2;    // s * log2(e)
   int causal;
@@ -57,6 +57,18 @@ struct BwdParams {
   long long timeout_ticks;  // wall-clock ticks before a wait gives up
   unsigned long long* prof; // profiling builds (DASH_PROFILE): per-wave phase cycle counters, or null
 };
+
+// fp32 dQ accumulator layouts (rows per (b, h) padded to row_stride).
+// - Ordered variant, block layout: the rows are cut into 32-row blocks and the d
+//   columns into 32-column blocks; block (qblk, db) is kDqBlock floats at
+//   ((bh * row_stride / 32 + qblk) * d / 32 + db) * kDqBlock, in the order of a 32x32
+//   MFMA accumulator: element r = 4 i + e (i, e in 0..3) of lane l (0..63) is float
+//   256 i + 4 l + e, and it belongs to row 16 (i / 2) + 2 (i % 2) + l / 32 + 4 e, column
+//   l % 32 of the block. (Rows are in the permuted order in which the kernel's dS
+//   operand visits them.) A wave then moves one block with four 1 KiB accesses.
+// - Atomic variant: row-major [bh][row_stride][d], so that the per-element float atomics
+//   of a wave hit whole cache lines.
+constexpr int kDqBlock = 32 * 32;
 
 // Phase counters of a profiling build, per wave: [grid][NW][kProfSlots] of 64-bit cycles
 // (s_memtime) or counts.
@@ -85,7 +97,9 @@ inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hip
   return hipErrorInvalidValue;
 }
 hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t stream);
-hipError_t launch_dq_cast(const float* acc, void* dq, int64_t count, float scale, int grid, hipStream_t stream);
+// dQ = bf16(scale * dqacc) for rows < N, from the atomic variant's row-major layout.
+hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
+                          hipStream_t stream);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
 
 }  // namespace dash
