@@ -213,7 +213,8 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps before each timed block (the clock needs ~30 ms of load to settle)")
     ap.add_argument("--workload", default="full-d128-N2048", choices=list(WORKLOADS))
     ap.add_argument("--schedule", default=None)
     ap.add_argument("--no-compare", action="store_true", help="skip the other schedules and the atomic variant")

@@ -35,7 +35,8 @@
 //                   the same way as P's accumulator rows
 //     dK += dS^T Q  likewise with dS and Q
 //     dQ = dS K     A = dS via an LDS round trip (stored [kv][q], read transposed),
-//                   B = K read transposed from the item's K tile in LDS
+//                   B = K, read transposed from the item's K tile in LDS once per
+//                   item and held in AGPRs with the accumulator
 // - LDS tiles have one 16-byte pad chunk per row and operand rows are visited in a
 //   permuted order (pi16), so that both the row reads (ds_read_b128) and the
 //   transpose reads hit distinct banks with addresses "lane base + constant".
@@ -213,33 +214,43 @@ bwd_main_kernel(BwdParams p) {
       __syncthreads();
     }
     const int kvcol = kv0 + 32 * w + l32;  // this lane's KV row in S, P, dP, dS
+    // B operands of this wave's dQ blocks for the whole item: K^T of d block db_k(kd)
+    // (kd < NKD), k-step kk covering KV rows 16 kk .. 16 kk + 15 in the order the dS
+    // operand visits them (transpose reads of the K tile).
+    auto db_k = [&](int kd) __attribute__((always_inline)) { return (w + NW * kd) % DB; };
+    bf16x8 kT[C::NKD][KK];
+#pragma unroll
+    for (int kd = 0; kd < C::NKD; ++kd) {
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int koff = kd_lane + 16 * kk * ST + 64 * db_k(kd);
+        kT[kd][kk] = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
+      }
+    }
     PROF_MARK(kProfItem);
 
     // Block t2 of this wave's dQ partial of step `ps` (its dS^T is in LDS buffer
-    // ps & 1) = init + dS K; accumulator row m of block qb is Q row q0 + pi(32 qb + m).
-    auto dq_block = [&](int ps, int t2, const floatx16& init) __attribute__((always_inline)) -> floatx16 {
+    // ps & 1) = init + dS K, accumulated in place; accumulator row m of block qb is Q
+    // row q0 + pi(32 qb + m). Block t2 uses d block db_k(t2 % NKD).
+    auto dq_block = [&](int ps, int t2, floatx16& acc) __attribute__((always_inline)) {
       const LDS_AS char* sdSp = smem + C::OFF_DS + (ps & 1) * C::DST;
-      const int blk = w + NW * t2;
-      const int qb = blk / DB, db = blk % DB;
-      // Operands of k-step kk: A = dS (transpose reads of dS^T), B = K (transpose reads
-      // of the K tile); loaded one k-step ahead of their MFMA.
-      auto load = [&](int kk, bf16x8& a, bf16x8& bk) __attribute__((always_inline)) {
+      const int qb = (w + NW * t2) / DB;
+      const int kd = t2 % C::NKD;
+      // A operand of k-step kk = dS (transpose reads of dS^T), loaded one k-step ahead.
+      auto load = [&](int kk) __attribute__((always_inline)) -> bf16x8 {
         const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * qb;
-        a = join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
-        const int koff = kd_lane + 16 * kk * ST + 64 * db;
-        bk = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
+        return join(lds_tr(sdSp, off), lds_tr(sdSp, off + kDsStride));
       };
-      floatx16 acc = init;
-      bf16x8 a[2], bk[2];
-      load(0, a[0], bk[0]);
+      bf16x8 a[2];
+      a[0] = load(0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        if (kk + 1 < KK) load(kk + 1, a[(kk + 1) & 1], bk[(kk + 1) & 1]);
-        acc = mfma32(a[kk & 1], bk[kk & 1], acc);
+        if (kk + 1 < KK) a[(kk + 1) & 1] = load(kk + 1);
+        mfma32_vab(acc, a[kk & 1], kT[kd][kk]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      return acc;
+      mfma_result_wait(acc);
     };
 
     // dQ addressing. Element r of this wave's block t2 at a step sits at row
@@ -346,11 +357,15 @@ bwd_main_kernel(BwdParams p) {
         }
       }
     };
-    // dQ blocks [t0, t1) of step ps and their stores.
-    auto reduce_blocks = [&](int ps, const Pending& pd, const floatx16 (&ld)[C::NBLK], int t0, int t1)
+    // dQ blocks [t0, t1) of step ps (accumulated onto the loaded running sums) and
+    // their stores.
+    auto reduce_blocks = [&](int ps, const Pending& pd, floatx16 (&ld)[C::NBLK], int t0, int t1)
         __attribute__((always_inline)) {
 #pragma unroll
-      for (int t2 = t0; t2 < t1; ++t2) reduce_store(pd, t2, dq_block(ps, t2, ld[t2]));
+      for (int t2 = t0; t2 < t1; ++t2) {
+        dq_block(ps, t2, ld[t2]);
+        reduce_store(pd, t2, ld[t2]);
+      }
     };
     // Call after wait_mem_done(): this wave's accumulator stores are in the L2.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {

@@ -55,6 +55,19 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 __device__ __forceinline__ void mfma32_acc(floatx16& acc, bf16x8 a, bf16x8 b) {
   asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
+// MFMA with the accumulator in VGPRs and the B operand in AGPRs (an operand held in
+// AGPRs for a whole KV item). Back-to-back MFMAs accumulating into the same registers
+// need no wait states; reads of the result by other instructions need
+// mfma_result_wait() first.
+__device__ __forceinline__ void mfma32_vab(floatx16& acc, bf16x8 a, const bf16x8& b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+}
+// Wait states between an inline-assembly MFMA writing `acc` (VGPRs) and memory or VALU
+// instructions reading it (12 for a store, 13 for VALU; 16 given). Ties the value to
+// the wait so that no reader is scheduled before it.
+__device__ __forceinline__ void mfma_result_wait(floatx16& acc) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc));
+}
 // Wait states between the last MFMA writing an AGPR accumulator and VALU reads of it
 // (v_accvgpr_read): more than the 16-pass pipeline depth.
 __device__ __forceinline__ void mfma_drain() {
