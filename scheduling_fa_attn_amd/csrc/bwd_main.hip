@@ -28,8 +28,8 @@
 // - All five contractions use v_mfma_f32_32x32x16_bf16. Operand layouts (A: lane
 //   holds row lane%32, 8 consecutive k; B: column lane%32, 8 consecutive k; D:
 //   column lane%32, rows 8*(r/4) + 4*(lane/32) + r%4):
-//     S  = Q K^T    A = Q (ds_read_b128 from LDS), B = K (registers)
-//     dP = dO V^T   A = dO (LDS), B = V (registers)
+//     S  = Q K^T    A = Q (ds_read_b128 from LDS), B = K (AGPRs, loaded per item)
+//     dP = dO V^T   A = dO (LDS), B = V (AGPRs)
 //     dV += P^T dO  A = P (registers, straight from the S accumulators), B = dO read
 //                   with ds_read_b64_tr_b16 (LDS transpose read), rows permuted
 //                   the same way as P's accumulator rows
@@ -87,7 +87,9 @@ struct BwdCfg {
   static_assert(QT % 1024 == 0 && DST % 1024 == 0 && (BC * ST) % 1024 == 0, "1 KiB-aligned tiles");
 };
 
-template <int D, int NW>
+// DET: ordered reduction (p.deterministic != 0) or float atomics; one kernel each, so
+// that neither carries the other's code and registers.
+template <int D, int NW, bool DET>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_main_kernel(BwdParams p) {
   using C = BwdCfg<D, NW>;
@@ -192,8 +194,8 @@ bwd_main_kernel(BwdParams p) {
           kz = *reinterpret_cast<const bf16x8*>(Kg + static_cast<int64_t>(kvr) * D + ks * 16 + 8 * hi);
           vz = *reinterpret_cast<const bf16x8*>(Vg + static_cast<int64_t>(kvr) * D + ks * 16 + 8 * hi);
         }
-        kreg[ks] = kz;
-        vreg[ks] = vz;
+        kreg[ks] = to_agpr(kz);
+        vreg[ks] = to_agpr(vz);
       }
     }
     floatx16 accK[DB], accV[DB];
@@ -224,7 +226,7 @@ bwd_main_kernel(BwdParams p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int koff = kd_lane + 16 * kk * ST + 64 * db_k(kd);
-        kT[kd][kk] = join(lds_tr(sK, koff), lds_tr(sK, koff + ST));
+        kT[kd][kk] = to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST)));
       }
     }
     PROF_MARK(kProfItem);
@@ -270,20 +272,24 @@ bwd_main_kernel(BwdParams p) {
     const int acc_lane = lane * 16;  // byte offset of this lane's first 4 floats in a block
     constexpr int kBlkBytes = kDqBlock * 4;
 
-    // Reduction of step ps's dQ partial, in parts spread over the next step so that its
-    // memory latency overlaps the step's work: (1) wait for the turn and issue the
-    // accumulator loads, (2) per 32x32 block, the dQ MFMAs start from the loaded
-    // accumulator and the sum is stored, (3) after the stores are acknowledged, pass
-    // the turn on.
+    // Ordered reduction of step ps's dQ partial (DASH paper, section 3.1: contributions
+    // to one dQ tile are added in the order the schedule table ranks them). Its parts
+    // are spread so that memory latency overlaps other work: (1) the bookkeeping and a
+    // poll of the turn during the last MFMA phase of step ps, (2) once the turn has come,
+    // the running-sum loads (then or, failing that, at the start of step ps + 1, after a
+    // blocking wait), (3) the dQ MFMAs, which start from the loaded running sum, inside
+    // the S/dP slots of step ps + 1, (4) the stores, spread over the following slots,
+    // (5) after the stores are acknowledged, the turn is passed on.
     struct Pending {
       int rank, last;
       int* sem;
-      rsrc_t acc_rs;  // the step's 2 DB fp32 accumulator blocks
+      float* acc_blk; // the step's first fp32 accumulator block
+      rsrc_t acc_rs;  // the step's 2 DB fp32 accumulator blocks (atomic variant: its rows
+                      // q0 .. q0 + 63 of the row-major accumulator)
       rsrc_t dq_rs;   // bf16 dQ rows [q0, N) of (b, h)
-      float* acc_g;   // atomic variant: accumulator row q0 (row-major)
       bool go;
     };
-    auto reduce_begin = [&](int ps, floatx16 (&ld)[C::NBLK]) __attribute__((always_inline)) -> Pending {
+    auto reduce_prepare = [&](int ps) __attribute__((always_inline)) -> Pending {
       const Quad task = load_quad(tasks, t_begin + ps / SUBS);
       Pending pd;
       pd.rank = task.z;
@@ -292,13 +298,21 @@ bwd_main_kernel(BwdParams p) {
       const int64_t bh = static_cast<int64_t>(b) * H + task.x;
       const int rows = N - q0s;  // may be <= 0 for a step past N
       // Accumulator rows are padded to the tile, so the step's blocks always exist.
-      float* const acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
-      pd.acc_g = p.dqacc + (bh * p.row_stride + q0s) * D;
-      pd.acc_rs = make_rsrc(acc_blk, 2 * DB * kBlkBytes);
+      pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
+      pd.acc_rs = DET ? make_rsrc(pd.acc_blk, 2 * DB * kBlkBytes)
+                      : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, 64 * D * 4);
       pd.dq_rs = make_rsrc(p.dq + bh * N * D + static_cast<int64_t>(q0s) * D, rows > 0 ? rows * D * 2 : 0);
       pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
       pd.go = !failed;
-      if (p.deterministic && pd.go && pd.rank > 0) {
+      return pd;
+    };
+    // Does this contribution have to wait for its turn at all?
+    auto reduce_needs_turn = [&](const Pending& pd) __attribute__((always_inline)) {
+      return DET && pd.go && pd.rank > 0;
+    };
+    // Blocking wait for the turn.
+    auto reduce_wait = [&](Pending& pd) __attribute__((always_inline)) {
+      if (reduce_needs_turn(pd)) {
         if (cross) {
           pd.go = wait_turn(pd.sem, pd.rank, p.err, p.timeout_ticks, true);
         } else {
@@ -306,17 +320,20 @@ bwd_main_kernel(BwdParams p) {
         }
         failed = !pd.go;
       }
-      PROF_MARK(kProfWait);
-      // Running sum so far; the first contributor (and the atomic variant) reads
-      // through an empty descriptor, which returns zeros without touching memory.
-      const bool add = p.deterministic && pd.go && pd.rank > 0;
-      const rsrc_t lrs = make_rsrc(acc_blk, add ? 2 * DB * kBlkBytes : 0);
+    };
+    // Running sum so far (after the turn has come); the first contributor (and the
+    // atomic variant) reads through an empty descriptor, which returns zeros without
+    // touching memory.
+    auto reduce_load = [&](const Pending& pd, floatx16 (&ld)[C::NBLK]) __attribute__((always_inline)) {
+      const rsrc_t lrs = make_rsrc(pd.acc_blk, reduce_needs_turn(pd) ? 2 * DB * kBlkBytes : 0);
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
         const int soff = (w + NW * t2) * kBlkBytes;  // wave-uniform block offset
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_lane + 1024 * i, soff, kSC1);
+          // The previous contributor shares this XCD's L2 unless the chains cross XCDs.
+          const u32x4 v = cross ? __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_lane + 1024 * i, soff, kSC1)
+                                : __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_lane + 1024 * i, soff, kSC0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const unsigned u = v[e];
@@ -324,61 +341,72 @@ bwd_main_kernel(BwdParams p) {
           }
         }
       }
-      return pd;
     };
-    auto reduce_store = [&](const Pending& pd, int t2, const floatx16& v) __attribute__((always_inline)) {
+    // Stores part i (elements 4 i .. 4 i + 3, i.e. row group t = i) of dQ block t2.
+    auto reduce_store_part = [&](const Pending& pd, int t2, int i, const floatx16& v) __attribute__((always_inline)) {
       if (!pd.go) return;
-      if (!p.deterministic) {
-        // Rows past N exist (padding) and are never output.
-        float* dst = pd.acc_g + blk_base(t2);
+      const int qb = (w + NW * t2) / DB;
+      // Per-element row offsets go to the scalar offset operand and the instruction's
+      // immediate offset (compile-time constants), so that no per-element address has
+      // to stay in registers. Row of element (t, e): 32 qb + 16 (t / 2) + 2 (t % 2) + 4 e.
+      const int t = i;
+      if (!DET) {
+        // Row-major accumulator; rows past N exist (padding) and are never output.
+        const int vb = 4 * blk_base(t2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) atomicAdd(dst + row_const(t2, r), v[r]);
+        for (int e = 0; e < 4; ++e) {
+          const float x = v[4 * t + e];
+          __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+              x, pd.acc_rs, vb + 16 * (e & 1) * D, 4 * (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * (e & 2)) * D, 0);
+        }
       } else if (pd.last) {
+        // The last contributor writes bf16 dQ (rows past N are dropped by the descriptor).
         const int vb = 2 * blk_base(t2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bf16 hv = static_cast<bf16>(v[r] * p.scale);
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), pd.dq_rs,
-                                                vb + 2 * row_const(t2, r), 0, 0);
+        for (int e = 0; e < 4; ++e) {
+          const bf16 hv = static_cast<bf16>(v[4 * t + e] * p.scale);
+          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), pd.dq_rs, vb + 8 * e * D,
+                                                2 * (32 * qb + 16 * (t >> 1) + 2 * (t & 1)) * D, 0);
         }
       } else {
-        const int soff = (w + NW * t2) * kBlkBytes;
+        u32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            // Element copied to a scalar first: a bit-cast of a vector element lvalue
-            // reads the vector's first element.
-            const float f = v[4 * i + e];
-            x[e] = __builtin_bit_cast(unsigned, f);
-          }
-          __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_lane + 1024 * i, soff, 0);
+        for (int e = 0; e < 4; ++e) {
+          // Element copied to a scalar first: a bit-cast of a vector element lvalue
+          // reads the vector's first element.
+          const float f = v[4 * i + e];
+          x[e] = __builtin_bit_cast(unsigned, f);
         }
+        __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_lane + 1024 * i, (w + NW * t2) * kBlkBytes, 0);
       }
     };
-    // dQ blocks [t0, t1) of step ps (accumulated onto the loaded running sums) and
-    // their stores.
-    auto reduce_blocks = [&](int ps, const Pending& pd, floatx16 (&ld)[C::NBLK], int t0, int t1)
-        __attribute__((always_inline)) {
+    auto reduce_store = [&](const Pending& pd, int t2, const floatx16& v) __attribute__((always_inline)) {
 #pragma unroll
-      for (int t2 = t0; t2 < t1; ++t2) {
-        dq_block(ps, t2, ld[t2]);
-        reduce_store(pd, t2, ld[t2]);
-      }
+      for (int i = 0; i < 4; ++i) reduce_store_part(pd, t2, i, v);
     };
     // Call after wait_mem_done(): this wave's accumulator stores are in the L2.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
-      if (!p.deterministic || !pd.go || pd.last) return;
+      if (!DET || !pd.go || pd.last) return;
       if (cross) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       if (lane == 0) {
-        if (cross)
+        if (cross) {
           __hip_atomic_store(pd.sem, pd.rank + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        else
-          __hip_atomic_store(pd.sem, pd.rank + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          // Writer and reader share this XCD's L2, where the acknowledged stores already
+          // are: a plain store into the L2 suffices, and the next contributor's poll
+          // then hits in the L2 instead of going past it.
+          __builtin_amdgcn_raw_buffer_store_b32(static_cast<unsigned>(pd.rank + 1), make_rsrc(pd.sem, 4), 0, 0, 0);
+        }
       }
     };
 
+    // Reduction state carried from step to step: the previous step's contribution, its
+    // running sums (or dQ partials once the MFMAs have run) and whether their loads
+    // have been issued already.
+    Pending pd;
+    floatx16 ld[C::NBLK];
+    bool loaded = false;
+    constexpr int kBlkA = (C::NBLK + 1) / 2;  // dQ blocks reduced under the first S/dP block
     for (int s = 0; s < n_steps; ++s) {
       PROF_COUNT(kProfSteps);
       const int buf = s & 1;
@@ -386,14 +414,17 @@ bwd_main_kernel(BwdParams p) {
       const int j = task.y;
       const int q0 = j * BC + (s % SUBS) * BQ;
 
-      // Previous step's reduction, part 1: wait for the turn, issue the accumulator
-      // loads. The next step's copies go after them: waiting for those loads must not
-      // wait for the copies (the vector-memory counter is in order).
-      Pending pd;
-      floatx16 ld[C::NBLK];
+      // Previous step's reduction: if the poll of the last step found no turn, wait
+      // for it here and issue the running-sum loads now.
       const bool have_prev = s > 0;
-      if (have_prev) pd = reduce_begin(s - 1, ld);
-      constexpr int kBlkA = (C::NBLK + 1) / 2;  // dQ blocks reduced after the first S/dP block
+      if (have_prev && !loaded) {
+        PROF_MARK(kProfDq);
+        reduce_wait(pd);
+        PROF_MARK(kProfWait);
+        reduce_load(pd, ld);
+        PROF_COUNT(kProfLate);
+      }
+      PROF_MARK(kProfLoads);
 
       const LDS_AS char* sQ = smem + C::OFF_Q + buf * C::QT;
       const LDS_AS char* sdO = smem + C::OFF_DO + buf * C::QT;
@@ -412,6 +443,33 @@ bwd_main_kernel(BwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const int t = r >> 2, e = r & 3;
           if (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e < mask_thr) S[r] = -__builtin_inff();
+        }
+      };
+
+      // The next step's copies (Q, dO, -LSE*log2e, -D into buffer (s + 1) & 1, free since
+      // the last barrier), spread over the S/dP slots: copy op o is Q block o, dO block
+      // o - PER_WAVE, then -LSE*log2e (wave 0) and -D (wave 1).
+      const bool copy_next = s + 1 < n_steps;
+      const Quad task_n = load_quad(tasks, t_begin + (s + 1) / SUBS);
+      const int q0_n = task_n.y * BC + ((s + 1) % SUBS) * BQ;
+      const int64_t bh_n = static_cast<int64_t>(b) * H + task_n.x;
+      const bf16* q_n = p.q + bh_n * N * D;
+      const bf16* do_n = p.dO + bh_n * N * D;
+      LDS_AS char* const sQn = smem + C::OFF_Q + (buf ^ 1) * C::QT;
+      LDS_AS char* const sdOn = smem + C::OFF_DO + (buf ^ 1) * C::QT;
+      constexpr int kPW = TileCopy<D, BQ, NW>::PER_WAVE;
+      constexpr int kCopyOps = 2 * kPW + 2;
+      auto copy_op = [&](int o) __attribute__((always_inline)) {
+        if (!copy_next) return;
+        if (o < kPW) {
+          qcopy.issue_one(sQn, q_n, q0_n, N, w, o);
+        } else if (o < 2 * kPW) {
+          qcopy.issue_one(sdOn, do_n, q0_n, N, w, o - kPW);
+        } else if (o == 2 * kPW) {
+          // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
+          if (w == 0) dma4(p.nlse2 + bh_n * p.row_stride + q0_n, row_lane, smem + C::OFF_NL + (buf ^ 1) * 256);
+        } else {
+          if (w == 1) dma4(p.neg_delta + bh_n * p.row_stride + q0_n, row_lane, smem + C::OFF_DL + (buf ^ 1) * 256);
         }
       };
 
@@ -478,100 +536,198 @@ bwd_main_kernel(BwdParams p) {
         if ((slot & 1) && t + 1 < 4) nlr[(t + 1) & 1] = load_nl(qb, t + 1);
       };
 #define SLOT() __builtin_amdgcn_sched_barrier(0)
-      floatx16 S0 = {}, S1 = {};
+      // Operands are read from LDS kPF slots ahead of their MFMAs (rings of kPF + 1).
+      constexpr int kPF = 2, kRing = kPF + 1;
+      constexpr int NSD = 2 * DK;  // S/dP k-steps of the two 32-row blocks
+      constexpr int NIT = 2 * DB;  // dV/dK (hf, db) iterations of one block, 2 MFMAs each
+      constexpr int NDV = 2 * NIT;
+      static_assert(DK == 8 || DK == 4, "S/dP slots");
+      // The previous step's dQ MFMAs (dQ block t2, k-step kk: MFMA number t2 KK + kk) run
+      // inside the S/dP slots: blocks [0, kBlkA) under block 0's S/dP, the rest under
+      // block 1's, kQ1 / kQ2 of them per slot, their dS operands one slot ahead.
+      constexpr int kQ1 = kBlkA * KK / DK, kQ2 = (C::NBLK - kBlkA) * KK / DK;
+      static_assert(kQ1 * DK == kBlkA * KK && kQ2 * DK == (C::NBLK - kBlkA) * KK, "dQ MFMAs per slot");
+      constexpr int kQmax = kQ1 > kQ2 ? kQ1 : kQ2;
+      constexpr int kQRing = 2 * kQmax;
+      floatx16 S0, S1;
       floatx16 dP0 = load_negd(0), dP1;
       u32x4 P0[2], dS0[2], P1[2], dS1[2];
       floatx4 nlr[2];
-      bf16x8 aq[2], ad[2], bo[2], bq[2];
-      static_assert(DK == 8 || DK == 4, "S/dP slots");
-      constexpr int NIT = 2 * DB;  // dV/dK (hf, db) iterations, 2 MFMAs each
-      // Block 0: S/dP (A operands one k-step ahead).
-      aq[0] = lds_ld16(sQ, sdp_off(0, 0));
-      ad[0] = lds_ld16(sdO, sdp_off(0, 0));
+      bf16x8 aq[kRing], ad[kRing], bo[kRing], bq[kRing];
+      bf16x8 aqd[kQRing];
+      // S/dP k-step i = (block i / DK, k-step i % DK); dV/dK iteration j = (block j / NIT,
+      // (hf, db) = j % NIT).
+      auto sd_load = [&](int i) __attribute__((always_inline)) {
+        aq[i % kRing] = lds_ld16(sQ, sdp_off(i / DK, i % DK));
+        ad[i % kRing] = lds_ld16(sdO, sdp_off(i / DK, i % DK));
+      };
+      auto dv_load = [&](int j) __attribute__((always_inline)) {
+        load_bt(j / NIT, j % NIT, bo[j % kRing], bq[j % kRing]);
+      };
+      // Issued in S/dP slot i: operands kPF slots ahead, across into the dV/dK sequence.
+      auto sd_prefetch = [&](int i) __attribute__((always_inline)) {
+        if (i + kPF < NSD)
+          sd_load(i + kPF);
+        else
+          dv_load(i + kPF - NSD);
+      };
+      auto sd_mfma = [&](int i, floatx16& S, floatx16& dP) __attribute__((always_inline)) {
+        const int ks = i % DK;
+        if (ks == 0)
+          mfma32_vab_zero(S, aq[i % kRing], kreg[0]);
+        else
+          mfma32_vab(S, aq[i % kRing], kreg[ks]);
+        mfma32_vab(dP, ad[i % kRing], vreg[ks]);
+      };
+      // dQ MFMAs of S/dP slot i (previous step's dS^T, LDS buffer (s - 1) & 1; on an
+      // item's first step the MFMAs run on stale data and their results are dropped).
+      const LDS_AS char* sdSprev = smem + C::OFF_DS + ((s - 1) & 1) * C::DST;
+      auto dq_first = [&](int i) __attribute__((always_inline)) { return i < DK ? i * kQ1 : kBlkA * KK + (i - DK) * kQ2; };
+      auto dq_count = [&](int i) __attribute__((always_inline)) { return i < DK ? kQ1 : kQ2; };
+      auto dq_load = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < dq_count(i); ++n) {
+          const int m = dq_first(i) + n, t2 = m / KK, kk = m % KK;
+          const int off = ds_rd_lane + 16 * kk * kDsStride + 64 * ((w + NW * t2) / DB);
+          aqd[m % kQRing] = join(lds_tr(sdSprev, off), lds_tr(sdSprev, off + kDsStride));
+        }
+      };
+      auto dq_mfma = [&](int i) __attribute__((always_inline)) {
+#pragma unroll
+        for (int n = 0; n < dq_count(i); ++n) {
+          const int m = dq_first(i) + n, t2 = m / KK, kk = m % KK;
+          mfma32_vab(ld[t2], aqd[m % kQRing], kT[t2 % C::NKD][kk]);
+        }
+      };
+#pragma unroll
+      for (int i = 0; i < kPF; ++i) sd_load(i);
+      dq_load(0);
+      // Every running-sum load has landed before the first copy below is issued: the
+      // vector-memory counter is in order, and the compiler, which does not see the
+      // copies, would otherwise wait for them too.
+#pragma unroll
+      for (int t2 = 0; t2 < C::NBLK; ++t2) asm volatile("" : "+v"(ld[t2]));
       SLOT();
+      // Block 0: S/dP, with dQ blocks [0, kBlkA) of the previous step and the next
+      // step's copies.
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        if (ks + 1 < DK) {
-          aq[(ks + 1) & 1] = lds_ld16(sQ, sdp_off(0, ks + 1));
-          ad[(ks + 1) & 1] = lds_ld16(sdO, sdp_off(0, ks + 1));
-        } else {
-          aq[0] = lds_ld16(sQ, sdp_off(1, 0));
-          ad[0] = lds_ld16(sdO, sdp_off(1, 0));
-          nlr[0] = load_nl(0, 0);
-        }
+        sd_prefetch(ks);
+        if (ks + 1 < NSD) dq_load(ks + 1);
+        if (ks + 1 == DK) nlr[0] = load_nl(0, 0);
         if (ks == DK / 2) dP1 = load_negd(1);
-        S0 = mfma32(aq[ks & 1], kreg[ks], S0);
-        dP0 = mfma32(ad[ks & 1], vreg[ks], dP0);
+        sd_mfma(ks, S0, dP0);
+        dq_mfma(ks);
+#pragma unroll
+        for (int o = ks * kCopyOps / DK; o < (ks + 1) * kCopyOps / DK; ++o) copy_op(o);
         SLOT();
       }
-      // Previous step's reduction, part 2 (first blocks): the loads have had block 0's
-      // S/dP to arrive.
-      if (have_prev) reduce_blocks(s - 1, pd, ld, 0, kBlkA);
+      PROF_MARK(kProfSd0);
+      mfma_result_wait(S0, dP0);  // before the VALU reads them (and the stores read ld)
+#pragma unroll
+      for (int t2 = 0; t2 < kBlkA; ++t2) asm volatile("" : "+v"(ld[t2]));
       if (diag) mask_diag(0, S0);
+      PROF_MARK(kProfMid0);
       SLOT();
-      // Block 1: S/dP, with block 0's softmax (8 slots of 2 elements over the DK k-steps).
+      // Block 1: S/dP with block 0's softmax (8 slots of 2 elements over the DK k-steps)
+      // and the remaining dQ blocks.
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        if (ks + 1 < DK) {
-          aq[(ks + 1) & 1] = lds_ld16(sQ, sdp_off(1, ks + 1));
-          ad[(ks + 1) & 1] = lds_ld16(sdO, sdp_off(1, ks + 1));
-        } else {
-          load_bt(0, 0, bo[0], bq[0]);
-        }
-        S1 = mfma32(aq[ks & 1], kreg[ks], S1);
-        dP1 = mfma32(ad[ks & 1], vreg[ks], dP1);
+        sd_prefetch(DK + ks);
+        if (DK + ks + 1 < NSD) dq_load(DK + ks + 1);
+        sd_mfma(DK + ks, S1, dP1);
+        dq_mfma(DK + ks);
 #pragma unroll
         for (int sl = (8 / DK) * ks; sl < (8 / DK) * (ks + 1); ++sl) softmax_slot(0, sl, S0, dP0, nlr, P0, dS0);
         if (ks + 1 == DK) nlr[0] = load_nl(1, 0);
+        // Stores of the first dQ blocks (4 parts each) over these slots.
+        if (have_prev) {
+#pragma unroll
+          for (int x = ks * 4 * kBlkA / DK; x < (ks + 1) * 4 * kBlkA / DK; ++x) reduce_store_part(pd, x / 4, x % 4, ld[x / 4]);
+        }
         SLOT();
       }
-      if (have_prev) {
-        // Rest of the previous step's reduction; once its stores are acknowledged the
-        // turn is passed on, half a step earlier than the step's end.
-        reduce_blocks(s - 1, pd, ld, kBlkA, C::NBLK);
-        wait_mem_done();
-        reduce_signal(pd);
-      }
-      // The next step's copies: after every vector-memory load this step waits for.
-      if (s + 1 < n_steps) issue_step(s + 1);
+      PROF_MARK(kProfSd1);
+      mfma_result_wait(S1, dP1);
+#pragma unroll
+      for (int t2 = kBlkA; t2 < C::NBLK; ++t2) asm volatile("" : "+v"(ld[t2]));
       if (diag) mask_diag(1, S1);
+      PROF_MARK(kProfMid1);
       SLOT();
-      // Block 0: dV/dK (B operands one iteration ahead), with block 1's softmax.
+      // The reduction of the current step's partial, prepared during the last phase.
+      Pending pd_n;
+      int sem_now = 0;
+      // dV += P^T dO, dK += dS^T Q over both blocks; block 1's softmax under block 0's.
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        if (it + 1 < NIT)
-          load_bt(0, it + 1, bo[(it + 1) & 1], bq[(it + 1) & 1]);
-        else
-          load_bt(1, 0, bo[0], bq[0]);
+      for (int j = 0; j < NDV; ++j) {
+        if (j + kPF < NDV) dv_load(j + kPF);
+        const int qb = j / NIT, it = j % NIT;
         const int hf = it / DB, db = it % DB;
-        mfma32_acc(accV[db], as_bf16x8(P0[hf]), bo[it & 1]);
-        mfma32_acc(accK[db], as_bf16x8(dS0[hf]), bq[it & 1]);
+        mfma32_acc(accV[db], as_bf16x8(qb ? P1[hf] : P0[hf]), bo[j % kRing]);
+        mfma32_acc(accK[db], as_bf16x8(qb ? dS1[hf] : dS0[hf]), bq[j % kRing]);
+        if (qb == 0) {
 #pragma unroll
-        for (int sl = (8 / NIT) * it; sl < (8 / NIT) * (it + 1); ++sl) softmax_slot(1, sl, S1, dP1, nlr, P1, dS1);
-        SLOT();
-      }
-      // Block 1: dV/dK.
+          for (int sl = (8 / NIT) * it; sl < (8 / NIT) * (it + 1); ++sl) softmax_slot(1, sl, S1, dP1, nlr, P1, dS1);
+          // Stores of the other dQ blocks over the first half of these slots.
+          if (have_prev && 2 * it < NIT) {
+            constexpr int kB = C::NBLK - kBlkA, kH = NIT / 2;
 #pragma unroll
-      for (int it = 0; it < NIT; ++it) {
-        if (it + 1 < NIT) load_bt(1, it + 1, bo[(it + 1) & 1], bq[(it + 1) & 1]);
-        const int hf = it / DB, db = it % DB;
-        mfma32_acc(accV[db], as_bf16x8(P1[hf]), bo[it & 1]);
-        mfma32_acc(accK[db], as_bf16x8(dS1[hf]), bq[it & 1]);
+            for (int x = it * 4 * kB / kH; x < (it + 1) * 4 * kB / kH; ++x)
+              reduce_store_part(pd, kBlkA + x / 4, x % 4, ld[kBlkA + x / 4]);
+          }
+        }
+        if (j + 1 == NIT) {
+          PROF_MARK(kProfDv0);
+          // Stores and copies acknowledged (the copies were issued a phase earlier):
+          // the turn is passed on; the next step's tiles are in LDS.
+          wait_mem_done();
+          if (have_prev) reduce_signal(pd);
+          PROF_MARK(kProfReduce);
+        }
+        if (j == NIT) {
+          // This step's contribution: bookkeeping and a poll of its turn (a plain load,
+          // not waited for until half a phase later).
+          pd_n = reduce_prepare(s);
+          if (reduce_needs_turn(pd_n)) {
+            if (cross) {
+              sem_now = __hip_atomic_load(pd_n.sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+              const unsigned u = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(pd_n.sem, 4), 0, 0, kSC0);
+              sem_now = static_cast<int>(u);
+            }
+          }
+        }
+        if (j == NIT + NIT / 2) {
+          loaded = !reduce_needs_turn(pd_n) || __builtin_amdgcn_readfirstlane(sem_now) == pd_n.rank;
+          if (loaded) {
+            if (cross && reduce_needs_turn(pd_n)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            reduce_load(pd_n, ld);
+          }
+        }
         SLOT();
       }
 #undef SLOT
+      pd = pd_n;
       PROF_MARK(kProfBody);
-      wait_mem_done();  // next step's tiles have landed
-      PROF_MARK(kProfReduce);
-      __syncthreads();  // dS^T of all waves and the next step's tiles are visible
+      // dS^T of all waves is visible after the barrier (the copies were awaited above;
+      // the running-sum loads stay in flight across it).
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
       PROF_MARK(kProfBarrier);
     }
     // The item's last step: its dQ partial and reduction.
     {
-      floatx16 ld[C::NBLK];
-      const Pending pd = reduce_begin(n_steps - 1, ld);
-      reduce_blocks(n_steps - 1, pd, ld, 0, C::NBLK);
-      PROF_MARK(kProfDq);
+      if (!loaded) {
+        reduce_wait(pd);
+        reduce_load(pd, ld);
+      }
+#pragma unroll
+      for (int t2 = 0; t2 < C::NBLK; ++t2) {
+        dq_block(n_steps - 1, t2, ld[t2]);
+        reduce_store(pd, t2, ld[t2]);
+      }
+      PROF_MARK(kProfItem);
       wait_mem_done();
       reduce_signal(pd);
       PROF_MARK(kProfReduce);
@@ -609,7 +765,7 @@ static hipError_t launch_main_t(const BwdParams& prm, int grid, hipStream_t stre
   using C = BwdCfg<D, NW>;
   // At least 81 KiB of LDS so that exactly one workgroup fits on a CU.
   const int shmem = C::BYTES > 83 * 1024 ? C::BYTES : 83 * 1024;
-  auto fn = bwd_main_kernel<D, NW>;
+  auto fn = prm.deterministic ? bwd_main_kernel<D, NW, true> : bwd_main_kernel<D, NW, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;

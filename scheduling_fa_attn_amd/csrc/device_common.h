@@ -62,11 +62,24 @@ __device__ __forceinline__ void mfma32_acc(floatx16& acc, bf16x8 a, bf16x8 b) {
 __device__ __forceinline__ void mfma32_vab(floatx16& acc, bf16x8 a, const bf16x8& b) {
   asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
+// Moves an operand that only AGPR-operand MFMAs read into AGPRs once, so that the
+// register allocator keeps it there (instead of a VGPR copy moved over per use).
+__device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
+  asm volatile("" : "+a"(v));
+  return v;
+}
+// The same starting from a zero accumulator.
+__device__ __forceinline__ void mfma32_vab_zero(floatx16& acc, bf16x8 a, const bf16x8& b) {
+  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+}
 // Wait states between an inline-assembly MFMA writing `acc` (VGPRs) and memory or VALU
 // instructions reading it (12 for a store, 13 for VALU; 16 given). Ties the value to
 // the wait so that no reader is scheduled before it.
 __device__ __forceinline__ void mfma_result_wait(floatx16& acc) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+__device__ __forceinline__ void mfma_result_wait(floatx16& x, floatx16& y) {
+  asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
 // Wait states between the last MFMA writing an AGPR accumulator and VALU reads of it
 // (v_accvgpr_read): more than the 16-pass pipeline depth.
@@ -194,7 +207,11 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
 }
-constexpr int kSC1 = 16;  // buffer cache policy: device scope (skips the CU's L1)
+// Buffer cache policies. SC0 alone: the load misses the CU's L1 and reads the XCD's L2,
+// the coherence point of CUs on one XCD. SC1: device scope, past the XCD's L2 (needed
+// when writer and reader may sit on different XCDs).
+constexpr int kSC0 = 1;
+constexpr int kSC1 = 16;
 // (The raw buffer load/store builtins move 32-bit patterns as unsigned int: float
 // data is bit-cast, never converted.)
 
@@ -283,20 +300,35 @@ struct TileCopy {
   // (finite values; the kernel masks them): then every offset is taken from row 0 of
   // the matrix with the row clamped in signed arithmetic, so no address leaves
   // [src, src + nrows * D).
+  // Instruction m (< PER_WAVE) of this wave's share of the copy below, alone; issues
+  // nothing where the wave has no block m.
+  __device__ __forceinline__ void issue_one(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w, int m) const {
+    if (!(m + 1 < PER_WAVE || w + NW * m < NI)) return;
+    if (r0 + ROWS <= nrows) {
+      dma16(src + static_cast<int64_t>(r0) * D, voff[m], dst + (w + NW * m) * 1024);
+    } else {
+      int r = r0 + static_cast<int>(voff[m] / (2 * D));
+      r = r < nrows - 1 ? r : nrows - 1;
+      dma16(src, static_cast<unsigned>(r) * (2 * D) + (voff[m] % (2 * D)), dst + (w + NW * m) * 1024);
+    }
+  }
   __device__ __forceinline__ void issue(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w) const {
-    const bool ragged = r0 + ROWS > nrows;
-    const bf16* base = ragged ? src : src + static_cast<int64_t>(r0) * D;
+    if (r0 + ROWS <= nrows) {  // wave-uniform: whole tile inside the matrix
+      const bf16* base = src + static_cast<int64_t>(r0) * D;
 #pragma unroll
-    for (int m = 0; m < PER_WAVE; ++m) {
-      const int blk = w + NW * m;
-      if (blk < NI) {
-        unsigned v = voff[m];
-        if (ragged) {
-          int r = r0 + static_cast<int>(v / (2 * D));
+      for (int m = 0; m < PER_WAVE; ++m) {
+        // Blocks of the first PER_WAVE - 1 rounds always exist: NW (PER_WAVE - 1) < NI.
+        if (m + 1 < PER_WAVE || w + NW * m < NI) dma16(base, voff[m], dst + (w + NW * m) * 1024);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < PER_WAVE; ++m) {
+        if (m + 1 < PER_WAVE || w + NW * m < NI) {
+          int r = r0 + static_cast<int>(voff[m] / (2 * D));
           r = r < nrows - 1 ? r : nrows - 1;
-          v = static_cast<unsigned>(r) * (2 * D) + (v % (2 * D));
+          const unsigned v = static_cast<unsigned>(r) * (2 * D) + (voff[m] % (2 * D));
+          dma16(src, v, dst + (w + NW * m) * 1024);
         }
-        dma16(base, v, dst + blk * 1024);
       }
     }
   }

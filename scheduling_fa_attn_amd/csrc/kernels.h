@@ -72,16 +72,24 @@ constexpr int kDqBlock = 32 * 32;
 
 // Phase counters of a profiling build, per wave: [grid][NW][kProfSlots] of 64-bit cycles
 // (s_memtime) or counts.
-constexpr int kProfSlots = 8;
+constexpr int kProfSlots = 16;
 enum ProfSlot {
-  kProfBody = 0,     // step body: copies issued, S/dP, softmax, dV/dK, dS^T store
-  kProfBarrier = 1,  // waiting for this wave's copies and the step barrier
-  kProfDq = 2,       // dQ = dS K
+  kProfBody = 0,     // dV/dK of the second block (the step's last MFMA phase)
+  kProfBarrier = 1,  // the step barrier
+  kProfDq = 2,       // dQ turn bookkeeping: task record and accumulator addresses
   kProfWait = 3,     // waiting for the dQ turn (semaphore)
-  kProfReduce = 4,   // dQ read-add-write (or atomics) and passing the turn on
+  kProfReduce = 4,   // waiting for this wave's copies at the step's end
   kProfItem = 5,     // item prologue and epilogue
   kProfSteps = 6,    // number of steps
-  kProfTotal = 7     // whole kernel
+  kProfTotal = 7,    // whole kernel
+  kProfSd0 = 8,      // S/dP of the first block (with dQ MFMAs), from the accumulator loads on
+  kProfMid0 = 9,     // stores of the first dQ blocks, mask
+  kProfSd1 = 10,     // S/dP of the second block with the first block's softmax
+  kProfMid1 = 11,    // stores of the other dQ blocks, their acknowledgement, turn passed on,
+                     // next step's copies issued
+  kProfDv0 = 12,     // dV/dK of the first block with the second block's softmax
+  kProfLoads = 13,   // accumulator loads issued at the step's start (after a late turn)
+  kProfLate = 14,    // number of steps whose turn had not come at the poll
 };
 
 // Main kernel for head dimension d and a workgroup of nw waves (one translation unit each).
