@@ -16,17 +16,19 @@ extern "C" {
 #endif
 
 /* Later dash_attn_bwd calls write the main kernel's per-wave phase counters into
- * `buf`: a device buffer owned by the caller of at least CUs * 4 * 16 uint64
- * ([CU slot][wave][16]; unused waves are not written). Per wave, in this order:
+ * `buf`: a device buffer owned by the caller of at least CUs * 4 * 20 uint64
+ * ([CU slot][wave][20]; unused waves are not written). Per wave, in this order:
  *   0 dV/dK of the second block                 1 step barrier
  *   2 dQ turn bookkeeping (task record, addresses)   3 waiting for the dQ turn
- *   4 waiting for the step's copies              5 item prologue/epilogue
+ *   4 waiting for the step's copies              5 (unused)
  *   6 number of steps                            7 whole kernel
  *   8 S/dP of the first block (with dQ MFMAs)    9 stores of the first dQ blocks
  *  10 S/dP of the second block + first softmax  11 other dQ stores, acknowledgement, turn
  *                                                  passed on, next step's copies issued
  *  12 dV/dK of the first block + second softmax 13 accumulator loads issued late
  *  14 number of steps whose dQ turn had not come at the poll
+ *  15 reading the polled turn word (within 0)  16 item prologue
+ *  17 the item's last reduction                 18 item epilogue (dK, dV stores)
  * `buf` = null detaches. The buffer must stay allocated while attached. Returns 0. */
 int dash_profile_attach(void* buf);
 

@@ -153,49 +153,76 @@ bwd_main_kernel(BwdParams p) {
   qcopy.init(w, lane);
   const unsigned row_lane = static_cast<unsigned>(pi16(lane) * 4);  // LDS slot m <- row pi(m)
 
+  // Copies of an item's tiles, issued while the previous item finishes (its last step
+  // and its last reduction), so that an item starts with its data in LDS:
+  //  - K (BC x D) -> the K tile; it is read only by the item's prologue;
+  //  - V (BC x D) -> the Q and dO areas of the buffer its step 0 does not use (rows
+  //    64 h .. 64 h + 63 in area h), free from the end of the previous item's last step
+  //    until the item's step 0 issues step 1's copies;
+  //  - the first step's Q, dO, -LSE*log2e, -D -> the buffer of its step 0 (with the
+  //    previous item's last step copies, below).
+  // Buffers alternate by step across items: an item's step s uses buffer (par0 + s) & 1.
+  auto issue_kv = [&](int it2, int par0) __attribute__((always_inline)) {
+    const Quad item2 = load_quad(items, it2);
+    const int64_t bg2 = static_cast<int64_t>(item2.x) * Hkv + item2.y;
+    const int kv02 = item2.z * BC;
+    TileCopy<D, BC, NW> kcopy;  // plan computed in place
+    kcopy.init(w, lane);
+    kcopy.issue(sK, p.k + bg2 * N * D, kv02, N, w);
+#pragma unroll
+    for (int hh = 0; hh < BC / BQ; ++hh)
+      qcopy.issue(smem + (hh == 0 ? C::OFF_Q : C::OFF_DO) + (par0 ^ 1) * C::QT, p.v + bg2 * N * D, kv02 + BQ * hh, N,
+                  w);
+  };
+  auto issue_first_step = [&](int it2, int par0) __attribute__((always_inline)) {
+    const Quad item2 = load_quad(items, it2);
+    const Quad task = load_quad(tasks, item2.w);
+    const int q0 = task.y * BC;
+    const int64_t bh = static_cast<int64_t>(item2.x) * H + task.x;
+    qcopy.issue(smem + C::OFF_Q + par0 * C::QT, p.q + bh * N * D, q0, N, w);
+    qcopy.issue(smem + C::OFF_DO + par0 * C::QT, p.dO + bh * N * D, q0, N, w);
+    // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
+    if (w == 0) dma4(p.nlse2 + bh * p.row_stride + q0, row_lane, smem + C::OFF_NL + par0 * 256);
+    if (w == 1) dma4(p.neg_delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + par0 * 256);
+  };
+  int par0 = 0;  // buffer of the current item's step 0
+  if (it_begin < it_end) {
+    issue_kv(it_begin, par0);
+    issue_first_step(it_begin, par0);
+  }
+
   for (int it = it_begin; it < it_end; ++it) {
     const Quad item = load_quad(items, it);
-    const int b = item.x, g = item.y, kv_tile = item.z;
+    const int b = item.x, kv_tile = item.z;
     const int t_begin = item.w, t_end = load_quad(items, it + 1).w;
     const int n_steps = (t_end - t_begin) * SUBS;
     const int kv0 = kv_tile * BC;
-    const int64_t bg = static_cast<int64_t>(b) * Hkv + g;
-    const bf16* Kg = p.k + bg * N * D;
-    const bf16* Vg = p.v + bg * N * D;
+    const int64_t bg = static_cast<int64_t>(b) * Hkv + item.y;
+    const bool has_next = it + 1 < it_end;
 
-    // Issues the global->LDS copies of step s (Q, dO, -LSE*log2e, -D) into buffer s & 1.
-    auto issue_step = [&](int s) __attribute__((always_inline)) {
-      const Quad task = load_quad(tasks, t_begin + s / SUBS);
-      const int q0 = task.y * BC + (s % SUBS) * BQ;
-      const int64_t bh = static_cast<int64_t>(b) * H + task.x;
-      const int buf = s & 1;
-      qcopy.issue(smem + C::OFF_Q + buf * C::QT, p.q + bh * N * D, q0, N, w);
-      qcopy.issue(smem + C::OFF_DO + buf * C::QT, p.dO + bh * N * D, q0, N, w);
-      // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
-      if (w == 0) dma4(p.nlse2 + bh * p.row_stride + q0, row_lane, smem + C::OFF_NL + buf * 256);
-      if (w == 1) dma4(p.neg_delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + buf * 256);
-    };
-
-    // Item prologue: K tile to LDS, first step's tiles, K/V rows of this wave to registers.
-    {
-      TileCopy<D, BC, NW> kcopy;  // once per item: plan computed in place
-      kcopy.init(w, lane);
-      kcopy.issue(sK, Kg, kv0, N, w);
+    // Item prologue: the item's tiles (issued before) have landed; K and V rows of this
+    // wave to AGPRs, dK and dV accumulators zeroed.
+    wait_mem_done();
+    __syncthreads();
+    if (kv0 + BC > N) {
+      // Ragged KV tile: K rows past N become zero in LDS, so that the (unmasked,
+      // finite) dS of those columns adds nothing to dQ. Their dK/dV rows are never
+      // stored; their K/V operands (copies of row N - 1) only feed those rows.
+      const int r0 = N - kv0;
+      LDS_AS floatx4* z = reinterpret_cast<LDS_AS floatx4*>(sK + r0 * ST);
+      for (int x = tid; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
     }
-    issue_step(0);
     bf16x8 kreg[DK], vreg[DK];
     {
-      const int kvr = kv0 + 32 * w + l32;
-      const bool ok = kvr < N;
+      // Row 32 w + l32 of the tile; the B operand of k-step ks holds its d columns
+      // 16 ks + 8 hi .. + 7.
+      const int r = 32 * w + l32;
+      const LDS_AS char* vrow = smem + (r < BQ ? C::OFF_Q : C::OFF_DO) + (par0 ^ 1) * C::QT + (r % BQ) * ST;
 #pragma unroll
       for (int ks = 0; ks < DK; ++ks) {
-        bf16x8 kz = {}, vz = {};
-        if (ok) {
-          kz = *reinterpret_cast<const bf16x8*>(Kg + static_cast<int64_t>(kvr) * D + ks * 16 + 8 * hi);
-          vz = *reinterpret_cast<const bf16x8*>(Vg + static_cast<int64_t>(kvr) * D + ks * 16 + 8 * hi);
-        }
-        kreg[ks] = to_agpr(kz);
-        vreg[ks] = to_agpr(vz);
+        kreg[ks] = to_agpr(lds_ld16(sK, r * ST + 32 * ks + 16 * hi));
+        vreg[ks] = to_agpr(lds_ld16(vrow, 32 * ks + 16 * hi));
       }
     }
     floatx16 accK[DB], accV[DB];
@@ -203,17 +230,6 @@ bwd_main_kernel(BwdParams p) {
     for (int db = 0; db < DB; ++db) {
       accK[db] = floatx16{};
       accV[db] = floatx16{};
-    }
-    wait_mem_done();
-    __syncthreads();
-    if (kv0 + BC > N) {
-      // Ragged KV tile: K rows past N become zero in LDS, so that the (unmasked,
-      // finite) dS of those columns adds nothing to dQ. Their K/V registers are zero
-      // already and their dK/dV rows are never stored.
-      const int r0 = N - kv0;
-      LDS_AS floatx4* z = reinterpret_cast<LDS_AS floatx4*>(sK + r0 * ST);
-      for (int x = tid; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
-      __syncthreads();
     }
     const int kvcol = kv0 + 32 * w + l32;  // this lane's KV row in S, P, dP, dS
     // B operands of this wave's dQ blocks for the whole item: K^T of d block db_k(kd)
@@ -229,13 +245,15 @@ bwd_main_kernel(BwdParams p) {
         kT[kd][kk] = to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST)));
       }
     }
-    PROF_MARK(kProfItem);
+    // Every wave has its V rows before step 0 issues step 1's copies into buffer 1.
+    __syncthreads();
+    PROF_MARK(kProfPro);
 
     // Block t2 of this wave's dQ partial of step `ps` (its dS^T is in LDS buffer
-    // ps & 1) = init + dS K, accumulated in place; accumulator row m of block qb is Q
+    // (par0 + ps) & 1) = init + dS K, accumulated in place; accumulator row m of block qb is Q
     // row q0 + pi(32 qb + m). Block t2 uses d block db_k(t2 % NKD).
     auto dq_block = [&](int ps, int t2, floatx16& acc) __attribute__((always_inline)) {
-      const LDS_AS char* sdSp = smem + C::OFF_DS + (ps & 1) * C::DST;
+      const LDS_AS char* sdSp = smem + C::OFF_DS + ((par0 + ps) & 1) * C::DST;
       const int qb = (w + NW * t2) / DB;
       const int kd = t2 % C::NKD;
       // A operand of k-step kk = dS (transpose reads of dS^T), loaded one k-step ahead.
@@ -409,7 +427,7 @@ bwd_main_kernel(BwdParams p) {
     constexpr int kBlkA = (C::NBLK + 1) / 2;  // dQ blocks reduced under the first S/dP block
     for (int s = 0; s < n_steps; ++s) {
       PROF_COUNT(kProfSteps);
-      const int buf = s & 1;
+      const int buf = (par0 + s) & 1;
       const Quad task = load_quad(tasks, t_begin + s / SUBS);
       const int j = task.y;
       const int q0 = j * BC + (s % SUBS) * BQ;
@@ -449,10 +467,13 @@ bwd_main_kernel(BwdParams p) {
       // The next step's copies (Q, dO, -LSE*log2e, -D into buffer (s + 1) & 1, free since
       // the last barrier), spread over the S/dP slots: copy op o is Q block o, dO block
       // o - PER_WAVE, then -LSE*log2e (wave 0) and -D (wave 1).
-      const bool copy_next = s + 1 < n_steps;
-      const Quad task_n = load_quad(tasks, t_begin + (s + 1) / SUBS);
+      // (At the item's last step: the next item's first step.)
+      const bool last_step = s + 1 == n_steps;
+      const bool copy_next = !last_step || has_next;
+      const Quad item_n = load_quad(items, it + 1);
+      const Quad task_n = load_quad(tasks, last_step ? item_n.w : t_begin + (s + 1) / SUBS);
       const int q0_n = task_n.y * BC + ((s + 1) % SUBS) * BQ;
-      const int64_t bh_n = static_cast<int64_t>(b) * H + task_n.x;
+      const int64_t bh_n = static_cast<int64_t>(last_step ? item_n.x : b) * H + task_n.x;
       const bf16* q_n = p.q + bh_n * N * D;
       const bf16* do_n = p.dO + bh_n * N * D;
       LDS_AS char* const sQn = smem + C::OFF_Q + (buf ^ 1) * C::QT;
@@ -579,9 +600,9 @@ bwd_main_kernel(BwdParams p) {
           mfma32_vab(S, aq[i % kRing], kreg[ks]);
         mfma32_vab(dP, ad[i % kRing], vreg[ks]);
       };
-      // dQ MFMAs of S/dP slot i (previous step's dS^T, LDS buffer (s - 1) & 1; on an
+      // dQ MFMAs of S/dP slot i (previous step's dS^T, LDS buffer buf ^ 1; on an
       // item's first step the MFMAs run on stale data and their results are dropped).
-      const LDS_AS char* sdSprev = smem + C::OFF_DS + ((s - 1) & 1) * C::DST;
+      const LDS_AS char* sdSprev = smem + C::OFF_DS + (buf ^ 1) * C::DST;
       auto dq_first = [&](int i) __attribute__((always_inline)) { return i < DK ? i * kQ1 : kBlkA * KK + (i - DK) * kQ2; };
       auto dq_count = [&](int i) __attribute__((always_inline)) { return i < DK ? kQ1 : kQ2; };
       auto dq_load = [&](int i) __attribute__((always_inline)) {
@@ -698,7 +719,9 @@ bwd_main_kernel(BwdParams p) {
           }
         }
         if (j == NIT + NIT / 2) {
+          PROF_MARK(kProfBody);
           loaded = !reduce_needs_turn(pd_n) || __builtin_amdgcn_readfirstlane(sem_now) == pd_n.rank;
+          PROF_MARK(kProfPoll);
           if (loaded) {
             if (cross && reduce_needs_turn(pd_n)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             reduce_load(pd_n, ld);
@@ -727,11 +750,16 @@ bwd_main_kernel(BwdParams p) {
         dq_block(n_steps - 1, t2, ld[t2]);
         reduce_store(pd, t2, ld[t2]);
       }
-      PROF_MARK(kProfItem);
+      PROF_MARK(kProfFlush);
       wait_mem_done();
       reduce_signal(pd);
       PROF_MARK(kProfReduce);
     }
+    // The next item's K and V tiles (the last step's barrier has passed: no wave reads
+    // the K tile or the last step's buffer any more). Its step 0 uses the buffer the last
+    // step's copies went to.
+    par0 = (par0 + n_steps) & 1;
+    if (has_next) issue_kv(it + 1, par0);
 
     // Epilogue: dK = s dK, dV; bf16 stores of this wave's 32 KV rows.
     mfma_drain();
@@ -749,10 +777,8 @@ bwd_main_kernel(BwdParams p) {
         }
       }
     }
-    // Every wave is done with this item's LDS (K tile, last step's buffers) before
-    // the next item's copies overwrite it.
-    __syncthreads();
-    PROF_MARK(kProfItem);
+    // (No barrier here: the next item's prologue waits for its tiles and synchronises.)
+    PROF_MARK(kProfEpi);
   }
   PROF_STORE(p, w, NW);
 }

@@ -72,14 +72,14 @@ constexpr int kDqBlock = 32 * 32;
 
 // Phase counters of a profiling build, per wave: [grid][NW][kProfSlots] of 64-bit cycles
 // (s_memtime) or counts.
-constexpr int kProfSlots = 16;
+constexpr int kProfSlots = 20;
 enum ProfSlot {
   kProfBody = 0,     // dV/dK of the second block (the step's last MFMA phase)
   kProfBarrier = 1,  // the step barrier
   kProfDq = 2,       // dQ turn bookkeeping: task record and accumulator addresses
   kProfWait = 3,     // waiting for the dQ turn (semaphore)
   kProfReduce = 4,   // waiting for this wave's copies at the step's end
-  kProfItem = 5,     // item prologue and epilogue
+  kProfItem = 5,     // (unused)
   kProfSteps = 6,    // number of steps
   kProfTotal = 7,    // whole kernel
   kProfSd0 = 8,      // S/dP of the first block (with dQ MFMAs), from the accumulator loads on
@@ -90,6 +90,10 @@ enum ProfSlot {
   kProfDv0 = 12,     // dV/dK of the first block with the second block's softmax
   kProfLoads = 13,   // accumulator loads issued at the step's start (after a late turn)
   kProfLate = 14,    // number of steps whose turn had not come at the poll
+  kProfPoll = 15,    // reading the polled turn word
+  kProfPro = 16,     // item prologue (K, V, first tiles, K^T operands)
+  kProfFlush = 17,   // the item's last reduction
+  kProfEpi = 18,     // item epilogue (dK, dV stores)
 };
 
 // Main kernel for head dimension d and a workgroup of nw waves (one translation unit each).
