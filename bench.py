@@ -106,6 +106,54 @@ def time_schedule(dev, shape, causal, schedule, deterministic, steps, warmup, wo
     return total_ms / steps, main_ms, (dq, dk, dv)
 
 
+def time_cold(dev, shape, causal, schedule, steps, warmup, workspace, flush_mib=512):
+    """Whole-call timings (preprocess + main kernel) with the L2 and the memory-side cache
+    flushed before every call by writing a flush_mib MiB buffer: per-call HIP events on the
+    call's stream, returns (median ms, min ms, median main-kernel ms)."""
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    B, H, Hkv, N, d = shape
+    dq = torch.empty_like(dev["q"])
+    dk = torch.empty_like(dev["k"])
+    dv = torch.empty_like(dev["v"])
+    scale = 1.0 / math.sqrt(d)
+    mask = "causal" if causal else "full"
+    stream = torch.cuda.current_stream()
+    flush = torch.empty(flush_mib * (1 << 20) // 4, dtype=torch.float32, device="cuda")
+    calls = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(steps)]
+    for evs in calls:  # materialise the HIP events (the library records the main-kernel pair)
+        for e in evs:
+            e.record()
+
+    def call(evs=None):
+        st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], dq, dk, dv,
+                                scale, mask, schedule, 1, workspace, stream=stream.cuda_stream,
+                                main_start=None if evs is None else evs[2].cuda_event,
+                                main_stop=None if evs is None else evs[3].cuda_event)
+        if st != dash.DASH_OK:
+            raise dash.DashError(st, "dash_attn_bwd")
+
+    for _ in range(warmup):
+        flush.fill_(1.0)
+        call()
+    torch.cuda.synchronize()
+    for evs in calls:
+        flush.fill_(1.0)
+        evs[0].record()
+        call(evs)
+        evs[1].record()
+    torch.cuda.synchronize()
+    err = dash.dash_last_kernel_error()
+    if err != dash.DASH_OK:
+        raise dash.DashError(err, "kernel")
+    whole = sorted(e[0].elapsed_time(e[1]) for e in calls)
+    main = sorted(e[2].elapsed_time(e[3]) for e in calls)
+    del flush
+    return whole[len(whole) // 2], whole[0], main[len(main) // 2]
+
+
 def cpu_baseline(shape, causal, seed, budget_s):
     """The fp64 oracle backward on the host cores, on whole heads of the same workload."""
     import numpy as np
@@ -220,6 +268,8 @@ def main():
     ap.add_argument("--no-compare", action="store_true", help="skip the other schedules and the atomic variant")
     ap.add_argument("--only", action="store_true", help="measure only --workload (not the other configurations)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache timing (L2 and memory-side cache flushed before every call)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference for the "
@@ -257,7 +307,7 @@ def main():
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
-    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}>"
+    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true>"
     result = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 3),
@@ -281,6 +331,20 @@ def main():
                      "traffic": traffic_bytes(args.workload, kernel),
                      "kernel": kernel, "main_kernel_ms": round(main_ms, 4)},
     }
+    if not args.no_cold:
+        import torch
+
+        from scheduling_fa_attn_amd import dash
+
+        dev = make_inputs(B, H, Hkv, N, d, causal, 1000 + cfg_index)
+        ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+        med, mn, main_med = time_cold(dev, (B, H, Hkv, N, d), causal, main_res["schedule"], args.steps,
+                                      min(args.warmup, 5), ws)
+        result["cold_cache"] = {"flush": "512 MiB written before every call", "median_ms": round(med, 4),
+                                "min_ms": round(mn, 4), "main_kernel_median_ms": round(main_med, 4),
+                                "tflops_median": round(fl / (med * 1e-3) / 1e12, 2)}
+        log(f"  cold cache: median {med:.3f} ms (min {mn:.3f}), main kernel median {main_med:.3f} ms")
+        del dev, ws
     if others:
         result["other_workloads"] = others
     if not args.no_cpu_baseline:
