@@ -68,8 +68,11 @@ typedef enum {
 } dash_schedule;
 
 /* Bytes of caller-provided device workspace dash_attn_bwd needs for this shape:
- * an fp32 dQ accumulator [B,H,N,d], the fp32 row terms D = rowsum(dO*O) [B,H,N]
- * and the int32 ordering semaphores. Returns 0 for invalid sizes. */
+ * an fp32 dQ accumulator of B*H*R*d floats and two fp32 row-term arrays of B*H*R
+ * floats (-D with D = rowsum(dO*O), and -LSE*log2(e)), where R is N rounded up to the
+ * tile (dash_tile_size), plus the int32 ordering semaphores and XCD slot counters.
+ * The contents are the library's own between calls (the accumulator is kept in the
+ * matrix-core accumulator order, not row-major). Returns 0 for invalid sizes. */
 size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
 
 /* The backward pass (DASH, section 2.1; the schedules of section 3).
