@@ -12,6 +12,9 @@ LIB_PATH = os.path.join(HERE, LIB_NAME)
 # Profiling build (-DDASH_PROFILE): the main kernel also records per-wave phase cycle
 # counters, exported through dash_profile_attach. Not used by the default path.
 PROF_LIB_PATH = os.path.join(HERE, "libdash_mi355x_prof.so")
+# Replay build (-DDASH_REPLAY): every ordered dQ partial is dumped (dash_replay_attach),
+# for the exact check of the reduction order. Not used by the default path.
+REPLAY_LIB_PATH = os.path.join(HERE, "libdash_mi355x_replay.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
@@ -49,13 +52,15 @@ def _run(cmd, verbose):
     return res
 
 
-def build(verbose: bool = False, resource_usage: bool = False, profile: bool = False) -> str:
-    """Compile every source and link LIB_PATH (PROF_LIB_PATH with profile=True; always
-    recompiles); returns the library path."""
-    out = PROF_LIB_PATH if profile else LIB_PATH
-    tag = "prof" if profile else "rel"
+def build(verbose: bool = False, resource_usage: bool = False, profile: bool = False, replay: bool = False) -> str:
+    """Compile every source and link LIB_PATH (PROF_LIB_PATH with profile=True,
+    REPLAY_LIB_PATH with replay=True; always recompiles); returns the library path."""
+    assert not (profile and replay)
+    out = PROF_LIB_PATH if profile else (REPLAY_LIB_PATH if replay else LIB_PATH)
+    tag = "prof" if profile else ("replay" if replay else "rel")
     os.makedirs(BUILD_DIR, exist_ok=True)
-    extra = (["-DDASH_PROFILE"] if profile else []) + (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else [])
+    extra = (["-DDASH_PROFILE"] if profile else []) + (["-DDASH_REPLAY"] if replay else []) + \
+        (["-Rpass-analysis=kernel-resource-usage"] if resource_usage else [])
     objs = []
     for src, flags, obj in UNITS:
         o = os.path.join(BUILD_DIR, tag + "_" + obj)
@@ -71,4 +76,5 @@ def build(verbose: bool = False, resource_usage: bool = False, profile: bool = F
 
 
 if __name__ == "__main__":
-    build(verbose=True, resource_usage="--resource-usage" in sys.argv, profile="--profile" in sys.argv)
+    build(verbose=True, resource_usage="--resource-usage" in sys.argv, profile="--profile" in sys.argv,
+          replay="--replay" in sys.argv)

@@ -306,6 +306,9 @@ bwd_main_kernel(BwdParams p) {
                       // q0 .. q0 + 63 of the row-major accumulator)
       rsrc_t dq_rs;   // bf16 dQ rows [q0, N) of (b, h)
       bool go;
+#ifdef DASH_REPLAY
+      float* dump;    // replay builds: dump slot of the step's first block at this rank
+#endif
     };
     auto reduce_prepare = [&](int ps) __attribute__((always_inline)) -> Pending {
       const Quad task = load_quad(tasks, t_begin + ps / SUBS);
@@ -322,6 +325,12 @@ bwd_main_kernel(BwdParams p) {
       pd.dq_rs = make_rsrc(p.dq + bh * N * D + static_cast<int64_t>(q0s) * D, rows > 0 ? rows * D * 2 : 0);
       pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
       pd.go = !failed;
+#ifdef DASH_REPLAY
+      // Dump layout: [b*H + h][64-row step][dQ block (2 DB)][rank][kDqBlock floats].
+      pd.dump = p.replay ? p.replay + (((bh * (p.row_stride / BQ) + q0s / BQ) * (2 * DB)) * p.replay_ranks + pd.rank) *
+                                          static_cast<int64_t>(kDqBlock)
+                         : nullptr;
+#endif
       return pd;
     };
     // Does this contribution have to wait for its turn at all?
@@ -361,8 +370,44 @@ bwd_main_kernel(BwdParams p) {
       }
     };
     // Stores part i (elements 4 i .. 4 i + 3, i.e. row group t = i) of dQ block t2.
-    auto reduce_store_part = [&](const Pending& pd, int t2, int i, const floatx16& v) __attribute__((always_inline)) {
+#ifdef DASH_REPLAY
+    // Replay builds: the dQ MFMAs start from zero; the running sum loaded for the step
+    // is kept here and added to the partial with one fp32 add per element, and every
+    // partial is dumped, so that a CPU replay in rank order reproduces the sums bit for bit.
+    floatx16 run[C::NBLK];
+#endif
+    auto reduce_store_part = [&](const Pending& pd, int t2, int i, const floatx16& v_in) __attribute__((always_inline)) {
       if (!pd.go) return;
+#ifdef DASH_REPLAY
+      floatx16 v = v_in;
+      if (DET) {
+        if (pd.dump) {
+          u32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float f = v_in[4 * i + e];
+            x[e] = __builtin_bit_cast(unsigned, f);
+          }
+          const int blk = w + NW * t2;
+          float* dst = pd.dump + static_cast<int64_t>(blk) * p.replay_ranks * kDqBlock + 256 * i + 4 * lane;
+          *reinterpret_cast<u32x4*>(dst) = x;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * i + e] = run[t2][4 * i + e] + v_in[4 * i + e];
+        if (pd.last) {
+          // The final fp32 sum is kept in the accumulator too (read by the replay check).
+          u32x4 x;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float f = v[4 * i + e];
+            x[e] = __builtin_bit_cast(unsigned, f);
+          }
+          __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_lane + 1024 * i, (w + NW * t2) * kBlkBytes, 0);
+        }
+      }
+#else
+      const floatx16& v = v_in;
+#endif
       const int qb = (w + NW * t2) / DB;
       // Per-element row offsets go to the scalar offset operand and the instruction's
       // immediate offset (compile-time constants), so that no per-element address has
@@ -628,6 +673,13 @@ bwd_main_kernel(BwdParams p) {
       // copies, would otherwise wait for them too.
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) asm volatile("" : "+v"(ld[t2]));
+#ifdef DASH_REPLAY
+#pragma unroll
+      for (int t2 = 0; t2 < C::NBLK; ++t2) {
+        run[t2] = ld[t2];
+        ld[t2] = floatx16{};
+      }
+#endif
       SLOT();
       // Block 0: S/dP, with dQ blocks [0, kBlkA) of the previous step and the next
       // step's copies.
@@ -747,6 +799,10 @@ bwd_main_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
+#ifdef DASH_REPLAY
+        run[t2] = ld[t2];
+        ld[t2] = floatx16{};
+#endif
         dq_block(n_steps - 1, t2, ld[t2]);
         reduce_store(pd, t2, ld[t2]);
       }

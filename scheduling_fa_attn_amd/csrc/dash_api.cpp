@@ -1,6 +1,7 @@
 // Host side of the C ABI declared in include/dash.h: argument checks, per-device state
 // (measured XCD topology, device error word, schedule-table cache) and kernel launches.
 #include "dash.h"
+#include "dash_replay.h"
 
 #include <hip/hip_runtime.h>
 
@@ -95,6 +96,8 @@ struct DeviceState {
 std::mutex g_mu;
 std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
+float* g_replay = nullptr;              // replay builds: dump of the ordered dQ partials
+size_t g_replay_bytes = 0;
 
 // Measures which XCD each workgroup of a one-per-CU grid lands on. A clean
 // round-robin split (every XCD id present with the same count) gives the table
@@ -298,6 +301,18 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.cus_per_xcd = st->cus_per_xcd;
   bp.timeout_ticks = st->ticks_per_second * 5;  // 5 seconds per wait
   bp.prof = g_prof;
+  bp.replay = nullptr;
+  bp.replay_ranks = 0;
+#ifdef DASH_REPLAY
+  if (g_replay && deterministic) {
+    const int tile = tile_for(N);
+    const int ranks = static_cast<int>(cdiv(N, tile));
+    const size_t need = size_t(B) * H * (L.row_stride / 64) * (2 * (d / 32)) * ranks * 1024 * sizeof(float);
+    if (g_replay_bytes < need) return DASH_ERR_WORKSPACE;
+    bp.replay = g_replay;
+    bp.replay_ranks = ranks;
+  }
+#endif
   if (ev_start && hipEventRecord(static_cast<hipEvent_t>(ev_start), stream) != hipSuccess) return DASH_ERR_HIP;
   hipError_t e = dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream);
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
@@ -371,6 +386,17 @@ int dash_tile_size(int N) { return tile_for(N); }
 int dash_profile_attach(void* buf) {
   std::lock_guard<std::mutex> lock(g_mu);
   g_prof = static_cast<unsigned long long*>(buf);
+  return DASH_OK;
+}
+#endif
+
+#ifdef DASH_REPLAY
+// Replay builds only: later deterministic calls dump every dQ partial (see dash_replay.h);
+// null detaches.
+int dash_replay_attach(void* buf, size_t bytes) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_replay = static_cast<float*>(buf);
+  g_replay_bytes = buf ? bytes : 0;
   return DASH_OK;
 }
 #endif

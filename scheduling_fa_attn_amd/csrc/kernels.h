@@ -56,6 +56,8 @@ struct BwdParams {
   int cus_per_xcd;
   long long timeout_ticks;  // wall-clock ticks before a wait gives up
   unsigned long long* prof; // profiling builds (DASH_PROFILE): per-wave phase cycle counters, or null
+  float* replay;            // replay builds (DASH_REPLAY): dump of every ordered dQ partial, or null
+  int replay_ranks;         // replay builds: rank slots per dQ block in the dump (KV tiles per head)
 };
 
 // fp32 dQ accumulator layouts (rows per (b, h) padded to row_stride).

@@ -50,6 +50,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     global _lib
     if _lib is not None:
         return _lib
+    _lib = open_library(path)
+    return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Load a build of the library at `path` (the release build, or the profiling or
+    replay build beside it) with the C signatures declared; independent of load()."""
     if not os.path.exists(path):
         raise RuntimeError(f"HIP library {path} is not built; run scheduling_fa_attn_amd/build.py "
                            "or __graft_entry__.build()")
@@ -71,7 +78,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dash_schedule_table.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), ctypes.c_longlong,
                                         ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
     lib.dash_schedule_table.restype = i
-    _lib = lib
+    if hasattr(lib, "dash_profile_attach"):
+        lib.dash_profile_attach.argtypes = [vp]
+        lib.dash_profile_attach.restype = i
+    if hasattr(lib, "dash_replay_attach"):
+        lib.dash_replay_attach.argtypes = [vp, sz]
+        lib.dash_replay_attach.restype = i
     return lib
 
 
@@ -87,8 +99,8 @@ def dash_tile_size(N: int) -> int:
     return int(load().dash_tile_size(N))
 
 
-def dash_last_kernel_error() -> int:
-    return int(load().dash_last_kernel_error())
+def dash_last_kernel_error(lib=None) -> int:
+    return int((lib or load()).dash_last_kernel_error())
 
 
 def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):
@@ -116,16 +128,17 @@ def _ptr(t):
 
 
 def dash_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, softmax_scale, mask, schedule, deterministic, workspace,
-                  stream=None, main_start=None, main_stop=None) -> int:
+                  stream=None, main_start=None, main_stop=None, lib=None) -> int:
     """Call dash_attn_bwd (or dash_attn_bwd_timed when events are given) on torch device tensors.
 
     q, o, dO, dq: [B, H, N, d] bf16; k, v, dk, dv: [B, Hkv, N, d] bf16; lse: [B, H, N] fp32;
     workspace: a uint8 device tensor of at least dash_attn_bwd_workspace_size bytes.
     Returns the status code (0 = success); nothing is checked here beyond marshalling.
+    `lib`: another build opened with open_library (default: the release build).
     """
     import torch
 
-    lib = load()
+    lib = lib or load()
     B, H, N, d = q.shape
     Hkv = k.shape[1]
     if stream is None:

@@ -44,6 +44,23 @@ def test_profiling_build_exports():
         assert hasattr(prof, name), name
 
 
+def test_replay_build_exports():
+    """The replay build (-DDASH_REPLAY) exports dash.h plus dash_replay.h; the release
+    build exports nothing of dash_replay.h."""
+    from scheduling_fa_attn_amd.build import REPLAY_LIB_PATH
+
+    extra = header_functions(os.path.join(INCLUDE, "dash_replay.h"))
+    assert extra == ["dash_replay_attach"]
+    rel = ctypes.CDLL(dash.load()._name)
+    for name in extra:
+        assert not hasattr(rel, name), name
+    if not os.path.exists(REPLAY_LIB_PATH):
+        pytest.skip("replay library not built")
+    lib = ctypes.CDLL(REPLAY_LIB_PATH)
+    for name in header_functions() + extra:
+        assert hasattr(lib, name), name
+
+
 def test_status_strings():
     for code in range(0, -8, -1):
         assert dash.dash_status_string(code) != "unknown status"
