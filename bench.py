@@ -214,6 +214,17 @@ def measure_workload(name, schedule, steps, warmup, compare):
             ms_s, _, _ = time_schedule(dev, shape, causal, s, 1, steps, warmup, ws)
             extra[s] = round(fl / (ms_s * 1e-3) / 1e12, 2)
             log(f"  {s} det: {ms_s:.3f} ms/step ({extra[s]:.1f} TFLOPS)")
+        lanes = (-(-N // 128)) // (2 if schedule == "sym_shift" else 1)
+        if lanes > 32:
+            # Groups larger than one XCD: the paper's n-SM layout (chains across XCDs) beside
+            # the default aggregation on one XCD.
+            dash.dash_set_placement("spread")
+            try:
+                ms_sp, _, _ = time_schedule(dev, shape, causal, schedule, 1, steps, warmup, ws)
+            finally:
+                dash.dash_set_placement("aggregate")
+            extra[schedule + "_spread"] = round(fl / (ms_sp * 1e-3) / 1e12, 2)
+            log(f"  {schedule} det, spread placement: {ms_sp:.3f} ms/step ({extra[schedule + '_spread']:.1f} TFLOPS)")
         ms_a, _, _ = time_schedule(dev, shape, causal, schedule, 0, steps, warmup, ws)
         extra["atomic_" + schedule] = round(fl / (ms_a * 1e-3) / 1e12, 2)
         ratio = ms_a / ms

@@ -67,6 +67,20 @@ typedef enum {
   DASH_SCHED_SYM_SHIFT = 3
 } dash_schedule;
 
+/* CU-group placement (DASH paper, section 3: "n KV tiles = n SMs; otherwise refine or
+ * aggregate heads"). A KV head's group has one lane per KV tile (one per tile pair for
+ * the symmetric shift); when it has more lanes than one XCD has CUs:
+ *   DASH_PLACEMENT_AGGREGATE (default): the group stays on one XCD and each CU runs
+ *     several lanes one after another, so every dQ chain stays in one L2;
+ *   DASH_PLACEMENT_SPREAD: the group spans as many XCDs as it needs, one lane per CU
+ *     (the paper's n-SM layout); dQ chains then cross XCDs and use device-scope
+ *     ordering. Smaller groups are placed the same way under both. */
+typedef enum { DASH_PLACEMENT_AGGREGATE = 0, DASH_PLACEMENT_SPREAD = 1 } dash_placement;
+
+/* Sets the placement used by later calls (library-wide, thread-safe; tables are cached
+ * per placement). Returns DASH_OK, or DASH_ERR_INVALID_ARG for another value. */
+int dash_set_placement(int placement);
+
 /* Bytes of caller-provided device workspace dash_attn_bwd needs for this shape:
  * an fp32 dQ accumulator of B*H*R*d floats and two fp32 row-term arrays of B*H*R
  * floats (-D with D = rowsum(dO*O), and -LSE*log2(e)), where R is N rounded up to the

@@ -90,12 +90,13 @@ struct DeviceState {
   int cus_per_xcd = 1;
   int* err = nullptr;
   long long ticks_per_second = 100000000LL;
-  std::map<std::tuple<int, int, int, int, int, int, int>, DevTable> tables;
+  std::map<std::tuple<int, int, int, int, int, int, int, int>, DevTable> tables;
 };
 
 std::mutex g_mu;
 std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
+int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
 float* g_replay = nullptr;              // replay builds: dump of the ordered dQ partials
 size_t g_replay_bytes = 0;
 
@@ -167,7 +168,7 @@ int get_device(DeviceState** out) {
 
 int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int schedule, const DevTable** out) {
   const int tile = tile_for(N);
-  auto key = std::make_tuple(B, H, Hkv, N, tile, causal ? 1 : 0, schedule);
+  auto key = std::make_tuple(B, H, Hkv, N, tile, causal ? 1 : 0, schedule, g_placement);
   auto found = st->tables.find(key);
   if (found != st->tables.end()) {
     *out = &found->second;
@@ -183,6 +184,7 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   sp.kind = static_cast<Sched>(schedule);
   sp.num_xcd = st->num_xcd;
   sp.cus_per_xcd = st->cus_per_xcd;
+  sp.spread = g_placement == DASH_PLACEMENT_SPREAD;
   dash::Table t;
   std::string err;
   const int s = dash::build_table(sp, &t, &err);
@@ -401,6 +403,13 @@ int dash_replay_attach(void* buf, size_t bytes) {
 }
 #endif
 
+int dash_set_placement(int placement) {
+  if (placement != DASH_PLACEMENT_AGGREGATE && placement != DASH_PLACEMENT_SPREAD) return DASH_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_placement = placement;
+  return DASH_OK;
+}
+
 int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local) {
   int s = check_sizes(B, H, Hkv, N, 64, mask, schedule);
@@ -416,6 +425,10 @@ int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, in
   sp.kind = static_cast<Sched>(schedule);
   sp.num_xcd = num_xcd;
   sp.cus_per_xcd = cus_per_xcd;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    sp.spread = g_placement == DASH_PLACEMENT_SPREAD;
+  }
   dash::Table t;
   std::string err;
   s = dash::build_table(sp, &t, &err);

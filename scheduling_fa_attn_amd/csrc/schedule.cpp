@@ -71,17 +71,24 @@ int build_table(const SchedParams& p, Table* out, std::string* err) {
   const int U = p.B * p.Hkv;  // units: (batch, KV head)
   if (U > 0 && n > 0) {
     const int L = (p.kind == Sched::SymShift) ? n / 2 : n;
-    int C, per_xcd;
-    if (L <= S) {
+    // A group that spreads spans `span` whole domains (lane c on domain c / S, CU c % S);
+    // otherwise it sits on one domain.
+    const int span = (p.spread && L > S && L % S == 0 && X % (L / S) == 0) ? L / S : 1;
+    int C, NG;
+    if (span > 1) {
       C = L;
-      per_xcd = S / C;
+      NG = X / span;
+    } else if (L <= S) {
+      C = L;
+      NG = X * (S / C);
     } else {
       C = S;
-      per_xcd = 1;
+      NG = X;
     }
-    const int NG = X * per_xcd;
-    // group gamma -> XCD gamma % X, CU slots [(gamma / X) * C, + C)
+    // group gamma -> one domain: XCD gamma % X, CU slots [(gamma / X) * C, + C);
+    // spread: domains [gamma * span, + span), lane c on domain gamma * span + c / S.
     auto worker_of = [&](int gamma, int c) {
+      if (span > 1) return (gamma * span + c / S) * S + c % S;
       const int xcd = gamma % X;
       const int slot = (gamma / X) * C + c;
       return xcd * S + slot;

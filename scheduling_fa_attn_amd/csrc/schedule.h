@@ -21,6 +21,11 @@ struct SchedParams {
   Sched kind = Sched::Naive;
   int num_xcd = 1;     // L2 domains
   int cus_per_xcd = 1; // compute units per L2 domain
+  // Groups with more lanes than one L2 domain has CUs: false = aggregate them on one
+  // domain (a CU runs several lanes one after another); true = spread them over as many
+  // domains as they need, one lane per CU (the paper's n-SM layout; dQ chains then cross
+  // L2 domains).
+  bool spread = false;
 };
 
 // One task: query head h, Q tile j, place `rank` in dQ tile (b, h, j)'s reduction

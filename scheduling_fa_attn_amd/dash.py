@@ -34,6 +34,7 @@ EXPORTED = (
     "dash_status_string",
     "dash_tile_size",
     "dash_schedule_table",
+    "dash_set_placement",
 )
 
 _lib = None
@@ -78,6 +79,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_schedule_table.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), ctypes.c_longlong,
                                         ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
     lib.dash_schedule_table.restype = i
+    lib.dash_set_placement.argtypes = [i]
+    lib.dash_set_placement.restype = i
     if hasattr(lib, "dash_profile_attach"):
         lib.dash_profile_attach.argtypes = [vp]
         lib.dash_profile_attach.restype = i
@@ -101,6 +104,15 @@ def dash_tile_size(N: int) -> int:
 
 def dash_last_kernel_error(lib=None) -> int:
     return int((lib or load()).dash_last_kernel_error())
+
+
+PLACEMENTS = {"aggregate": 0, "spread": 1}
+
+
+def dash_set_placement(placement, lib=None) -> int:
+    """Placement of CU groups larger than one XCD for later calls: "aggregate" (default)
+    or "spread" (the paper's n-SM layout; chains cross XCDs)."""
+    return int((lib or load()).dash_set_placement(PLACEMENTS.get(placement, placement)))
 
 
 def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):

@@ -142,3 +142,26 @@ def test_atomic_run_to_run_deviation(workload):
         print(f"[{w['name']}] schedule={best} det={det} max run-to-run deviation {dev_max:.3g}", flush=True)
         if det:
             assert dev_max == 0.0
+
+
+def test_spread_placement_parity_and_determinism(workload):
+    """The long causal head (n = 128 KV tiles, 64 lanes for the symmetric shift) with the
+    spread placement: the group spans XCDs and its dQ chains cross L2 domains (device-
+    scope ordering). Same bars: parity on the sampled heads, bitwise repeats."""
+    w = workload
+    if w["name"] != "causal-d128-N16384":
+        pytest.skip("only this workload has groups larger than one XCD")
+    assert dash.dash_set_placement("spread") == 0
+    try:
+        for sched in ("sym_shift", "naive"):
+            print(f"[{w['name']}] spread placement, schedule={sched}", flush=True)
+            first = [t.clone() for t in _run(w, sched, 1)]
+            for (b, g, hs), (rq, rk, rv) in w["refs"]:
+                errs = (_rel(first[0][b, hs], rq), _rel(first[1][b, g], rk), _rel(first[2][b, g], rv))
+                assert max(errs) <= TOL, (sched, b, g, errs)
+            for rep in range(2):
+                out = _run(w, sched, 1)
+                for a, b_ in zip(first, out):
+                    assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), (sched, rep)
+    finally:
+        assert dash.dash_set_placement("aggregate") == 0

@@ -114,3 +114,39 @@ def test_ragged_and_empty():
     osch.validate(to_table(rec, 2, 4, 2, 1000, "causal", "descending", 256))
     rec, _ = dash.dash_schedule_table(0, 4, 2, 1000, "full", "shift", 8, 32)
     assert len(rec) == 0
+
+
+@pytest.mark.parametrize("schedule,lanes", [("sym_shift", 64), ("naive", 128), ("descending", 128)])
+def test_spread_placement_of_the_long_causal_head(schedule, lanes):
+    """C4 (n = 128 KV tiles per head): with the spread placement a head's group takes one
+    CU per lane over several XCDs (the paper's n-SM layout), its chains cross XCDs, and
+    the table stays valid; the symmetric shift still reaches the work bound (each CU then
+    runs its single lane for every unit of its group: 16 units over 4 groups of 64 CUs).
+    The default (aggregate) placement keeps every chain on one XCD."""
+    B, H, Hkv, N, mask, _ = WORKLOADS["causal-d128-N16384"]
+    assert dash.dash_set_placement("spread") == 0
+    try:
+        rec, local = dash.dash_schedule_table(B, H, Hkv, N, mask, schedule, 8, 32)
+    finally:
+        assert dash.dash_set_placement("aggregate") == 0
+    table = to_table(rec, B, H, Hkv, N, mask, schedule, 256)
+    osch.validate(table)
+    assert not local
+    # one lane per CU: every CU that works has the KV tiles of one lane of each unit
+    workers = np.unique(rec[:, 0])
+    assert len(workers) == 256
+    per_unit = {}
+    for w, b, h, g, i, j, rank in rec.tolist():
+        per_unit.setdefault((w, b, g), set()).add(i)
+    assert max(len(v) for v in per_unit.values()) == (2 if schedule == "sym_shift" else 1)
+    if schedule == "sym_shift":
+        work = _lane_work(table)
+        assert work == 516
+        assert osch.simulate(table, 3.0, 1.0) == pytest.approx(work * 4.0)
+    rec2, local2 = dash.dash_schedule_table(B, H, Hkv, N, mask, schedule, 8, 32)
+    assert local2
+
+
+def test_placement_argument_errors():
+    assert dash.dash_set_placement(2) == dash.DASH_ERR_INVALID_ARG
+    assert dash.dash_set_placement(-1) == dash.DASH_ERR_INVALID_ARG
