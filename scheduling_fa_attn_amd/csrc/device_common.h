@@ -45,22 +45,26 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// dK/dV accumulation with the accumulator pinned in AGPRs: these 32x32 fp32 blocks
-// are touched only by MFMAs for a whole KV item, so keeping them out of the VGPRs
-// leaves the VGPRs to the softmax and to operands in flight. Written as inline
-// assembly (the compiler's MFMA form is one per function); the compiler's hazard
-// checks do not look inside it, so the s_nop covers the wait states a VALU write of
-// an A/B operand needs before an MFMA reads it. Dependent MFMAs on the same
+// MFMAs written as inline assembly, for operands or accumulators held in AGPRs (the
+// compiler's MFMA form is one register file per function). The compiler's hazard checks
+// do not look inside inline assembly: an MFMA must not read a VGPR that a VALU
+// instruction wrote less than 2 wait states before it. The S/dP and dQ MFMAs
+// (mfma32_vab*) read only LDS loads and AGPRs, so they carry no wait; the dV/dK MFMAs
+// read the packed P and dS, which the compiler may convert right before their first use,
+// so they start with s_nop 1. tests/test_asm_hazards.py checks the compiled kernels for
+// every violation. Back-to-back MFMAs accumulating into the same registers need no
+// wait states; reads of a VGPR result by other instructions need mfma_result_wait().
+//
+// dK/dV accumulation with the accumulator pinned in AGPRs: these 32x32 fp32 blocks are
+// touched only by MFMAs for a whole KV item, so keeping them out of the VGPRs leaves
+// the VGPRs to the softmax and to operands in flight. Dependent MFMAs on the same
 // accumulator are at least 7 MFMAs apart here.
 __device__ __forceinline__ void mfma32_acc(floatx16& acc, bf16x8 a, bf16x8 b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
 }
-// MFMA with the accumulator in VGPRs and the B operand in AGPRs (an operand held in
-// AGPRs for a whole KV item). Back-to-back MFMAs accumulating into the same registers
-// need no wait states; reads of the result by other instructions need
-// mfma_result_wait() first.
+// Accumulator in VGPRs, B operand in AGPRs (an operand held for a whole KV item).
 __device__ __forceinline__ void mfma32_vab(floatx16& acc, bf16x8 a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "a"(b));
 }
 // Moves an operand that only AGPR-operand MFMAs read into AGPRs once, so that the
 // register allocator keeps it there (instead of a VGPR copy moved over per use).
@@ -70,7 +74,7 @@ __device__ __forceinline__ bf16x8 to_agpr(bf16x8 v) {
 }
 // The same starting from a zero accumulator.
 __device__ __forceinline__ void mfma32_vab_zero(floatx16& acc, bf16x8 a, const bf16x8& b) {
-  asm("s_nop 2\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "a"(b));
 }
 // Wait states between an inline-assembly MFMA writing `acc` (VGPRs) and memory or VALU
 // instructions reading it (12 for a store, 13 for VALU; 16 given). Ties the value to
