@@ -1,7 +1,7 @@
 """Benchmark of the deterministic attention backward on one MI355X.
 
 One step = one dash_attn_bwd call (preprocess + persistent backward kernel with the
-ordered dQ reduction, dQ written by the last contributor) over one batch of
+ordered dQ reduction + dQ cast of the final fp32 sums) over one batch of
 synthetic bf16 inputs resident in HBM. The headline workload is the full-mask
 configuration the metric is quoted on (B=8, H=Hkv=16, N=2048, d=128, 16 384
 tokens, hidden 2048) with the shift schedule; the naive ordered schedule and the
@@ -318,7 +318,7 @@ def main():
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
-    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true>"
+    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false>"
     result = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 3),

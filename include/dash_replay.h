@@ -27,9 +27,9 @@ extern "C" {
  * with R = N rounded up to the tile (dash_tile_size) and n_kv = R / tile; a block's 1024
  * floats are in the accumulator order of the workspace (element 4i+e of lane l at
  * 256 i + 4 l + e; row 16(i/2) + 2(i%2) + l/32 + 4e, column l%32 of the block). Rank
- * slots past a tile's contributor count stay untouched. The last contributor also
- * leaves the final fp32 sum in the workspace accumulator (offset 0 of the workspace,
- * B*H*R*d floats in the same block order). A deterministic call whose dump would not
+ * slots past a tile's contributor count stay untouched. The final fp32 sums stay in the
+ * workspace accumulator (offset 0 of the workspace, B*H*R*d floats in the same block
+ * order), from which the dQ cast writes bf16 dQ. A deterministic call whose dump would not
  * fit in `bytes` returns DASH_ERR_WORKSPACE before launching. `buf` = null detaches.
  * Returns 0. */
 int dash_replay_attach(void* buf, size_t bytes);

@@ -1,6 +1,6 @@
 // Auxiliary HIP kernels of the attention backward for gfx950: the preprocess
-// (D = rowsum(dO * O), -LSE*log2(e), clearing), the dQ cast of the atomic variant and
-// the XCD topology probe.
+// (D = rowsum(dO * O), -LSE*log2(e), clearing), the dQ casts of the ordered and the
+// atomic variant and the XCD topology probe.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,9 +58,52 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   }
 }
 
-// dQ = bf16(s * dQacc), for the atomic variant (the ordered variant writes dQ from
-// the last contributor of each tile); the accumulator is row-major with row_stride
-// rows per head, of which the first N are output.
+// dQ = bf16(s * dQacc), for the ordered variant: the accumulator holds the final fp32
+// sums in the block layout described at kDqBlock. One workgroup per 32-row block row
+// of one head reads its D / 32 blocks with 16-byte loads, rounds them, puts them in row
+// order in LDS and writes rows < N in 16-byte chunks. (The last contributor of a tile
+// could write bf16 itself, but its step would then be slower than every other step,
+// and in the shift schedules every step of one CU holds up the steps that wait for it.)
+template <int D>
+__global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
+                                                             int N, int row_stride, float scale) {
+  constexpr int DB = D / 32;
+  constexpr int LROW = D + 8;  // bf16 per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) bf16 tile[32 * LROW];
+  const int rbs = row_stride / 32;  // block rows per head
+  const int64_t g = blockIdx.x;     // (head, block row)
+  const int64_t bh = g / rbs;
+  const int qblk = static_cast<int>(g % rbs);
+  const floatx4* src = reinterpret_cast<const floatx4*>(acc + g * DB * kDqBlock);
+#pragma unroll
+  for (int k = 0; k < DB; ++k) {
+    // float4 x of the block row: block db = x / 256; floats 4 l + 256 i .. + 3 of block db
+    // are elements 4 i .. 4 i + 3 of lane l: rows 16 (i / 2) + 2 (i % 2) + l / 32 + 4 e,
+    // column 32 db + l % 32.
+    const int x = threadIdx.x + 256 * k;
+    const int db = x >> 8, i = (x >> 6) & 3, l = x & 63;
+    const floatx4 v = src[x];
+    const int row0 = 16 * (i >> 1) + 2 * (i & 1) + (l >> 5);
+    const int col = 32 * db + (l & 31);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) tile[(row0 + 4 * e) * LROW + col] = static_cast<bf16>(v[e] * scale);
+  }
+  __syncthreads();
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const int r_end = N - 32 * qblk < 32 ? N - 32 * qblk : 32;
+#pragma unroll
+  for (int k = 0; k < 32 * CPR / 256; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    const int r = c / CPR, ch = c % CPR;
+    if (r < r_end) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&tile[r * LROW + 8 * ch]);
+      *reinterpret_cast<u32x4*>(dq + (bh * N + 32 * qblk + r) * D + 8 * ch) = v;
+    }
+  }
+}
+
+// dQ = bf16(s * dQacc), for the atomic variant; the accumulator is row-major with
+// row_stride rows per head, of which the first N are output.
 __global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
                                                       int64_t quads, int N, int row_stride, int d, float scale) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
@@ -102,6 +145,23 @@ hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int 
   grid = grid < 1 ? 1 : (grid > 8192 ? 8192 : grid);
   hipLaunchKernelGGL(dq_cast_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
                      reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
+                                 hipStream_t stream) {
+  const int64_t grid = heads * (row_stride / 32);
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (d == 64) {
+    hipLaunchKernelGGL(dq_cast_blocks_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
+                       reinterpret_cast<bf16*>(dq), N, row_stride, scale);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(dq_cast_blocks_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
+                       reinterpret_cast<bf16*>(dq), N, row_stride, scale);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -88,8 +88,11 @@ struct BwdCfg {
 };
 
 // DET: ordered reduction (p.deterministic != 0) or float atomics; one kernel each, so
-// that neither carries the other's code and registers.
-template <int D, int NW, bool DET>
+// that neither carries the other's code and registers. CROSS (ordered reduction only):
+// the contributors of one dQ tile may sit on different XCDs, whose L2s are not coherent
+// with each other, so the running sums and turns go through device-scope accesses and
+// fences; otherwise every chain stays inside one XCD's L2.
+template <int D, int NW, bool DET, bool CROSS>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_main_kernel(BwdParams p) {
   using C = BwdCfg<D, NW>;
@@ -123,7 +126,8 @@ bwd_main_kernel(BwdParams p) {
 
   PROF_DECL
   const int H = p.H, Hkv = p.Hkv, N = p.N;
-  const bool cross = !p.xcd_local;
+  constexpr bool cross = CROSS;
+  static_assert(DET || !CROSS, "device-scope chains exist only in the ordered reduction");
   bool failed = false;  // this wave gave up waiting (error reported); it keeps going without reducing
   // The schedule table is read-only for the whole launch: reading it through the
   // constant address space turns its uniform loads into scalar loads, which are
@@ -282,13 +286,12 @@ bwd_main_kernel(BwdParams p) {
       const int blk = w + NW * t2;
       return hi * D + (blk % DB) * 32 + l32;
     };
-    auto row_const = [&](int t2, int r) __attribute__((always_inline)) {
-      const int qb = (w + NW * t2) / DB;  // wave-uniform
-      const int t = r >> 2, e = r & 3;
-      return (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e) * D;
-    };
-    const int acc_lane = lane * 16;  // byte offset of this lane's first 4 floats in a block
     constexpr int kBlkBytes = kDqBlock * 4;
+    // Ordered variant: byte offset of this lane's first 4 floats in block w + NW t2 of a
+    // step's 2 DB accumulator blocks; part i (floats 256 i ..) adds the immediate 1024 i.
+    int acc_off[C::NBLK];
+#pragma unroll
+    for (int t2 = 0; t2 < C::NBLK; ++t2) acc_off[t2] = lane * 16 + (w + NW * t2) * kBlkBytes;
 
     // Ordered reduction of step ps's dQ partial (DASH paper, section 3.1: contributions
     // to one dQ tile are added in the order the schedule table ranks them). Its parts
@@ -298,13 +301,17 @@ bwd_main_kernel(BwdParams p) {
     // blocking wait), (3) the dQ MFMAs, which start from the loaded running sum, inside
     // the S/dP slots of step ps + 1, (4) the stores, spread over the following slots,
     // (5) after the stores are acknowledged, the turn is passed on.
+    // Every contributor, the last one included, stores its running sum (the final sums are
+    // cast to bf16 dQ by a separate kernel), so that every step runs the same code. Stores
+    // that must not happen (a contribution whose wait failed, step 0's missing previous
+    // partial) go through an empty descriptor, which drops them: the stores spread over
+    // the step's slots need no branch.
     struct Pending {
       int rank, last;
       int* sem;
       float* acc_blk; // the step's first fp32 accumulator block
-      rsrc_t acc_rs;  // the step's 2 DB fp32 accumulator blocks (atomic variant: its rows
-                      // q0 .. q0 + 63 of the row-major accumulator)
-      rsrc_t dq_rs;   // bf16 dQ rows [q0, N) of (b, h)
+      rsrc_t acc_rs;  // fp32 stores: the step's 2 DB accumulator blocks (atomic variant: its
+                      // rows q0 .. q0 + 63 of the row-major accumulator); empty if none
       bool go;
 #ifdef DASH_REPLAY
       float* dump;    // replay builds: dump slot of the step's first block at this rank
@@ -317,14 +324,12 @@ bwd_main_kernel(BwdParams p) {
       pd.last = task.w;
       const int q0s = task.y * BC + (ps % SUBS) * BQ;
       const int64_t bh = static_cast<int64_t>(b) * H + task.x;
-      const int rows = N - q0s;  // may be <= 0 for a step past N
       // Accumulator rows are padded to the tile, so the step's blocks always exist.
       pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
-      pd.acc_rs = DET ? make_rsrc(pd.acc_blk, 2 * DB * kBlkBytes)
-                      : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, 64 * D * 4);
-      pd.dq_rs = make_rsrc(p.dq + bh * N * D + static_cast<int64_t>(q0s) * D, rows > 0 ? rows * D * 2 : 0);
-      pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
       pd.go = !failed;
+      pd.acc_rs = DET ? make_rsrc(pd.acc_blk, pd.go ? 2 * DB * kBlkBytes : 0)
+                      : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, pd.go ? 64 * D * 4 : 0);
+      pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
 #ifdef DASH_REPLAY
       // Dump layout: [b*H + h][64-row step][dQ block (2 DB)][rank][kDqBlock floats].
       pd.dump = p.replay ? p.replay + (((bh * (p.row_stride / BQ) + q0s / BQ) * (2 * DB)) * p.replay_ranks + pd.rank) *
@@ -346,6 +351,7 @@ bwd_main_kernel(BwdParams p) {
           pd.go = wait_turn_local(pd.sem, pd.rank, p.err, p.timeout_ticks);
         }
         failed = !pd.go;
+        if (failed) pd.acc_rs = make_rsrc(pd.acc_blk, 0);
       }
     };
     // Running sum so far (after the turn has come); the first contributor (and the
@@ -355,12 +361,10 @@ bwd_main_kernel(BwdParams p) {
       const rsrc_t lrs = make_rsrc(pd.acc_blk, reduce_needs_turn(pd) ? 2 * DB * kBlkBytes : 0);
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
-        const int soff = (w + NW * t2) * kBlkBytes;  // wave-uniform block offset
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           // The previous contributor shares this XCD's L2 unless the chains cross XCDs.
-          const u32x4 v = cross ? __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_lane + 1024 * i, soff, kSC1)
-                                : __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_lane + 1024 * i, soff, kSC0);
+          const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(lrs, acc_off[t2] + 1024 * i, 0, cross ? kSC1 : kSC0);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const unsigned u = v[e];
@@ -377,8 +381,8 @@ bwd_main_kernel(BwdParams p) {
     floatx16 run[C::NBLK];
 #endif
     auto reduce_store_part = [&](const Pending& pd, int t2, int i, const floatx16& v_in) __attribute__((always_inline)) {
-      if (!pd.go) return;
 #ifdef DASH_REPLAY
+      if (!pd.go) return;
       floatx16 v = v_in;
       if (DET) {
         if (pd.dump) {
@@ -394,42 +398,22 @@ bwd_main_kernel(BwdParams p) {
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[4 * i + e] = run[t2][4 * i + e] + v_in[4 * i + e];
-        if (pd.last) {
-          // The final fp32 sum is kept in the accumulator too (read by the replay check).
-          u32x4 x;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float f = v[4 * i + e];
-            x[e] = __builtin_bit_cast(unsigned, f);
-          }
-          __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_lane + 1024 * i, (w + NW * t2) * kBlkBytes, 0);
-        }
       }
 #else
       const floatx16& v = v_in;
 #endif
-      const int qb = (w + NW * t2) / DB;
-      // Per-element row offsets go to the scalar offset operand and the instruction's
-      // immediate offset (compile-time constants), so that no per-element address has
-      // to stay in registers. Row of element (t, e): 32 qb + 16 (t / 2) + 2 (t % 2) + 4 e.
-      const int t = i;
       if (!DET) {
-        // Row-major accumulator; rows past N exist (padding) and are never output.
+        // Row-major accumulator; rows past N exist (padding) and are never output. Row
+        // of element (t, e), t = i: 32 qb + 16 (t / 2) + 2 (t % 2) + 4 e; the wave-uniform
+        // part goes to the scalar offset operand.
+        const int qb = (w + NW * t2) / DB;
+        const int t = i;
         const int vb = 4 * blk_base(t2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float x = v[4 * t + e];
           __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
               x, pd.acc_rs, vb + 16 * (e & 1) * D, 4 * (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * (e & 2)) * D, 0);
-        }
-      } else if (pd.last) {
-        // The last contributor writes bf16 dQ (rows past N are dropped by the descriptor).
-        const int vb = 2 * blk_base(t2);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bf16 hv = static_cast<bf16>(v[4 * t + e] * p.scale);
-          __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, hv), pd.dq_rs, vb + 8 * e * D,
-                                                2 * (32 * qb + 16 * (t >> 1) + 2 * (t & 1)) * D, 0);
         }
       } else {
         u32x4 x;
@@ -440,7 +424,7 @@ bwd_main_kernel(BwdParams p) {
           const float f = v[4 * i + e];
           x[e] = __builtin_bit_cast(unsigned, f);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_lane + 1024 * i, (w + NW * t2) * kBlkBytes, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_off[t2] + 1024 * i, 0, 0);
       }
     };
     auto reduce_store = [&](const Pending& pd, int t2, const floatx16& v) __attribute__((always_inline)) {
@@ -466,7 +450,18 @@ bwd_main_kernel(BwdParams p) {
     // Reduction state carried from step to step: the previous step's contribution, its
     // running sums (or dQ partials once the MFMAs have run) and whether their loads
     // have been issued already.
+    // Step 0 has no previous partial: its stores go to a contribution with empty
+    // descriptors, which drops them.
     Pending pd;
+    pd.rank = 0;
+    pd.last = 0;
+    pd.sem = p.sem;
+    pd.acc_blk = p.dqacc;
+    pd.acc_rs = make_rsrc(p.dqacc, 0);
+    pd.go = false;
+#ifdef DASH_REPLAY
+    pd.dump = nullptr;
+#endif
     floatx16 ld[C::NBLK];
     bool loaded = false;
     constexpr int kBlkA = (C::NBLK + 1) / 2;  // dQ blocks reduced under the first S/dP block
@@ -511,31 +506,31 @@ bwd_main_kernel(BwdParams p) {
 
       // The next step's copies (Q, dO, -LSE*log2e, -D into buffer (s + 1) & 1, free since
       // the last barrier), spread over the S/dP slots: copy op o is Q block o, dO block
-      // o - PER_WAVE, then -LSE*log2e (wave 0) and -D (wave 1).
-      // (At the item's last step: the next item's first step.)
+      // o - PER_WAVE, then -LSE*log2e (even waves) or -D (odd waves).
+      // At the item's last step: the next item's first step. At the worker's last step
+      // (no next item) the current task is copied again, so that the copies need no
+      // branch: nothing reads that buffer any more.
       const bool last_step = s + 1 == n_steps;
-      const bool copy_next = !last_step || has_next;
       const Quad item_n = load_quad(items, it + 1);
-      const Quad task_n = load_quad(tasks, last_step ? item_n.w : t_begin + (s + 1) / SUBS);
+      const Quad task_n = load_quad(tasks, last_step ? (has_next ? item_n.w : t_begin) : t_begin + (s + 1) / SUBS);
       const int q0_n = task_n.y * BC + ((s + 1) % SUBS) * BQ;
-      const int64_t bh_n = static_cast<int64_t>(last_step ? item_n.x : b) * H + task_n.x;
+      const int64_t bh_n = static_cast<int64_t>(last_step && has_next ? item_n.x : b) * H + task_n.x;
       const bf16* q_n = p.q + bh_n * N * D;
       const bf16* do_n = p.dO + bh_n * N * D;
       LDS_AS char* const sQn = smem + C::OFF_Q + (buf ^ 1) * C::QT;
       LDS_AS char* const sdOn = smem + C::OFF_DO + (buf ^ 1) * C::QT;
       constexpr int kPW = TileCopy<D, BQ, NW>::PER_WAVE;
-      constexpr int kCopyOps = 2 * kPW + 2;
+      constexpr int kCopyOps = 2 * kPW + 1;
       auto copy_op = [&](int o) __attribute__((always_inline)) {
-        if (!copy_next) return;
         if (o < kPW) {
-          qcopy.issue_one(sQn, q_n, q0_n, N, w, o);
+          qcopy.issue_one_clamped(sQn, q_n, q0_n, N, w, o);
         } else if (o < 2 * kPW) {
-          qcopy.issue_one(sdOn, do_n, q0_n, N, w, o - kPW);
-        } else if (o == 2 * kPW) {
-          // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
-          if (w == 0) dma4(p.nlse2 + bh_n * p.row_stride + q0_n, row_lane, smem + C::OFF_NL + (buf ^ 1) * 256);
+          qcopy.issue_one_clamped(sdOn, do_n, q0_n, N, w, o - kPW);
         } else {
-          if (w == 1) dma4(p.neg_delta + bh_n * p.row_stride + q0_n, row_lane, smem + C::OFF_DL + (buf ^ 1) * 256);
+          // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist. Waves of
+          // one parity write the same values to the same LDS slots.
+          const float* row_src = (w & 1) ? p.neg_delta : p.nlse2;
+          dma4(row_src + bh_n * p.row_stride + q0_n, row_lane, smem + ((w & 1) ? C::OFF_DL : C::OFF_NL) + (buf ^ 1) * 256);
         }
       };
 
@@ -714,10 +709,8 @@ bwd_main_kernel(BwdParams p) {
         for (int sl = (8 / DK) * ks; sl < (8 / DK) * (ks + 1); ++sl) softmax_slot(0, sl, S0, dP0, nlr, P0, dS0);
         if (ks + 1 == DK) nlr[0] = load_nl(1, 0);
         // Stores of the first dQ blocks (4 parts each) over these slots.
-        if (have_prev) {
 #pragma unroll
-          for (int x = ks * 4 * kBlkA / DK; x < (ks + 1) * 4 * kBlkA / DK; ++x) reduce_store_part(pd, x / 4, x % 4, ld[x / 4]);
-        }
+        for (int x = ks * 4 * kBlkA / DK; x < (ks + 1) * 4 * kBlkA / DK; ++x) reduce_store_part(pd, x / 4, x % 4, ld[x / 4]);
         SLOT();
       }
       PROF_MARK(kProfSd1);
@@ -742,7 +735,7 @@ bwd_main_kernel(BwdParams p) {
 #pragma unroll
           for (int sl = (8 / NIT) * it; sl < (8 / NIT) * (it + 1); ++sl) softmax_slot(1, sl, S1, dP1, nlr, P1, dS1);
           // Stores of the other dQ blocks over the first half of these slots.
-          if (have_prev && 2 * it < NIT) {
+          if (2 * it < NIT) {
             constexpr int kB = C::NBLK - kBlkA, kH = NIT / 2;
 #pragma unroll
             for (int x = it * 4 * kB / kH; x < (it + 1) * 4 * kB / kH; ++x)
@@ -847,7 +840,9 @@ static hipError_t launch_main_t(const BwdParams& prm, int grid, hipStream_t stre
   using C = BwdCfg<D, NW>;
   // At least 81 KiB of LDS so that exactly one workgroup fits on a CU.
   const int shmem = C::BYTES > 83 * 1024 ? C::BYTES : 83 * 1024;
-  auto fn = prm.deterministic ? bwd_main_kernel<D, NW, true> : bwd_main_kernel<D, NW, false>;
+  auto fn = !prm.deterministic ? bwd_main_kernel<D, NW, false, false>
+            : prm.xcd_local      ? bwd_main_kernel<D, NW, true, false>
+                                 : bwd_main_kernel<D, NW, true, true>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;

@@ -278,7 +278,6 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.dO = static_cast<const __bf16*>(dO);
   bp.nlse2 = nlse2;
   bp.neg_delta = neg_delta;
-  bp.dq = static_cast<__bf16*>(dq);
   bp.dk = static_cast<__bf16*>(dk);
   bp.dv = static_cast<__bf16*>(dv);
   bp.dqacc = dqacc;
@@ -320,10 +319,10 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
   if (e != hipSuccess) return DASH_ERR_HIP;
   if (ev_stop && hipEventRecord(static_cast<hipEvent_t>(ev_stop), stream) != hipSuccess) return DASH_ERR_HIP;
-  if (!deterministic) {
-    if (dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream) != hipSuccess)
-      return DASH_ERR_HIP;
-  }
+  const hipError_t ec = deterministic
+                           ? dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream)
+                           : dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream);
+  if (ec != hipSuccess) return DASH_ERR_HIP;
   return DASH_OK;
 }
 

@@ -316,6 +316,15 @@ struct TileCopy {
       dma16(src, static_cast<unsigned>(r) * (2 * D) + (voff[m] % (2 * D)), dst + (w + NW * m) * 1024);
     }
   }
+  // The same without a branch on raggedness: the clamped addressing above always (three
+  // VALU instructions per copy).
+  __device__ __forceinline__ void issue_one_clamped(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w,
+                                                    int m) const {
+    if (!(m + 1 < PER_WAVE || w + NW * m < NI)) return;
+    int r = r0 + static_cast<int>(voff[m] / (2 * D));
+    r = r < nrows - 1 ? r : nrows - 1;
+    dma16(src, static_cast<unsigned>(r) * (2 * D) + (voff[m] % (2 * D)), dst + (w + NW * m) * 1024);
+  }
   __device__ __forceinline__ void issue(LDS_AS char* dst, const bf16* src, int r0, int nrows, int w) const {
     if (r0 + ROWS <= nrows) {  // wave-uniform: whole tile inside the matrix
       const bf16* base = src + static_cast<int64_t>(r0) * D;

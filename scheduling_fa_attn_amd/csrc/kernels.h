@@ -34,7 +34,6 @@ struct BwdParams {
   const __bf16* dO;
   const float* nlse2;  // [B*H][row_stride] -LSE * log2(e); -inf past N
   const float* neg_delta;  // [B*H][row_stride] -D = -rowsum(dO * O); 0 past N
-  __bf16* dq;
   __bf16* dk;
   __bf16* dv;
   float* dqacc;        // fp32 dQ accumulator (layouts described at kDqBlock)
@@ -111,6 +110,9 @@ inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hip
   return hipErrorInvalidValue;
 }
 hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t stream);
+// dQ = bf16(scale * dqacc) for rows < N, from the ordered variant's block layout.
+hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
+                                 hipStream_t stream);
 // dQ = bf16(scale * dqacc) for rows < N, from the atomic variant's row-major layout.
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
                           hipStream_t stream);

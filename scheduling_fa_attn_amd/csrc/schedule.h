@@ -29,7 +29,7 @@ struct SchedParams {
 };
 
 // One task: query head h, Q tile j, place `rank` in dQ tile (b, h, j)'s reduction
-// order; `last` = 1 when rank is the final place (that task writes the bf16 dQ).
+// order; `last` = 1 when rank is the final place (that task passes no turn on).
 struct Task {
   int32_t h, j, rank, last;
 };

@@ -182,12 +182,13 @@ def kernel_asm(tmp_path_factory):
     return texts
 
 
-VARIANTS = [(d, nw, det) for (d, nw) in sorted(dash_build.MAIN_FLAGS) for det in (1, 0)]
+# (ordered reduction, cross-XCD chains): the three instantiations of each (d, nw).
+VARIANTS = [(d, nw, det, cross) for (d, nw) in sorted(dash_build.MAIN_FLAGS) for det, cross in ((1, 0), (1, 1), (0, 0))]
 
 
-@pytest.mark.parametrize("d,nw,det", VARIANTS, ids=[f"d{v[0]}-nw{v[1]}-det{v[2]}" for v in VARIANTS])
-def test_inline_mfma_wait_states(kernel_asm, d, nw, det):
-    symbol = f"_ZN4dash15bwd_main_kernelILi{d}ELi{nw}ELb{det}EEEvNS_9BwdParamsE"
+@pytest.mark.parametrize("d,nw,det,cross", VARIANTS, ids=[f"d{v[0]}-nw{v[1]}-det{v[2]}-cross{v[3]}" for v in VARIANTS])
+def test_inline_mfma_wait_states(kernel_asm, d, nw, det, cross):
+    symbol = f"_ZN4dash15bwd_main_kernelILi{d}ELi{nw}ELb{det}ELb{cross}EEEvNS_9BwdParamsE"
     insts, labels = parse_kernel(kernel_asm[(d, nw)], symbol)
     n_mfma = sum(1 for i in insts if i.mfma and i.asm)
     assert n_mfma >= 48, n_mfma

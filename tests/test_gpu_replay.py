@@ -8,14 +8,14 @@ contribution at its rank and adds it to the running sum with one fp32 addition. 
 the CPU adds the dumped partials of every 32x32 dQ block in rank order, in float32 from
 +0, and requires:
   - the sums equal the final fp32 accumulator of the workspace bitwise;
-  - the bf16 dQ the last contributor wrote equals bf16_RNE(scale * sum) bitwise;
+  - the bf16 dQ the cast wrote equals bf16_RNE(scale * sum) bitwise;
   - every rank slot up to the tile's contributor count was written (the dump starts as
     NaN, so a lost contribution cannot pass as a zero), and none past it.
 The contributor count of query tile j is n (full mask) or j + 1 (causal), the KV tiles
 that see it; ranks are the table's order of those contributions (the schedules of the
 paper's section 3). The release build's fused arithmetic is checked by the tolerance
 tests; this test pins the ordering, the turn-passing, the accumulator addressing and
-the bf16 write-out.
+the bf16 cast.
 """
 import math
 import os
