@@ -190,18 +190,27 @@ bwd_main_kernel(BwdParams p) {
     if (w == 1) dma4(p.neg_delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + par0 * 256);
   };
   int par0 = 0;  // buffer of the current item's step 0
+  // Step records (p.steps: {b * H + h, first Q row, rank, last} per 64-row step) of the
+  // current and the next step, carried across steps and items (a worker's steps are
+  // contiguous in the stream); the record two steps ahead is read during a step and
+  // taken over at its end, so no step waits for a table read.
+  const CONST_AS Quad* steps = (const CONST_AS Quad*)p.steps;
+  Quad rec_cur = {0, 0, 0, 0}, rec_nxt = {0, 0, 0, 0};
   if (it_begin < it_end) {
     issue_kv(it_begin, par0);
     issue_first_step(it_begin, par0);
+    const int gs0 = load_quad(items, it_begin).w * SUBS;
+    rec_cur = load_quad(steps, gs0);
+    rec_nxt = load_quad(steps, gs0 + 1);
   }
 
   for (int it = it_begin; it < it_end; ++it) {
     const Quad item = load_quad(items, it);
-    const int b = item.x, kv_tile = item.z;
+    const int kv_tile = item.z;
     const int t_begin = item.w, t_end = load_quad(items, it + 1).w;
     const int n_steps = (t_end - t_begin) * SUBS;
     const int kv0 = kv_tile * BC;
-    const int64_t bg = static_cast<int64_t>(b) * Hkv + item.y;
+    const int64_t bg = static_cast<int64_t>(item.x) * Hkv + item.y;
     const bool has_next = it + 1 < it_end;
 
     // Item prologue: the item's tiles (issued before) have landed; K and V rows of this
@@ -317,19 +326,19 @@ bwd_main_kernel(BwdParams p) {
       float* dump;    // replay builds: dump slot of the step's first block at this rank
 #endif
     };
-    auto reduce_prepare = [&](int ps) __attribute__((always_inline)) -> Pending {
-      const Quad task = load_quad(tasks, t_begin + ps / SUBS);
+    // `rec` is the step's record: {b * H + h, first Q row, rank, last}.
+    auto reduce_prepare = [&](const Quad& rec) __attribute__((always_inline)) -> Pending {
       Pending pd;
-      pd.rank = task.z;
-      pd.last = task.w;
-      const int q0s = task.y * BC + (ps % SUBS) * BQ;
-      const int64_t bh = static_cast<int64_t>(b) * H + task.x;
+      pd.rank = rec.z;
+      pd.last = rec.w;
+      const int q0s = rec.y;
+      const int64_t bh = rec.x;
       // Accumulator rows are padded to the tile, so the step's blocks always exist.
       pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
       pd.go = !failed;
       pd.acc_rs = DET ? make_rsrc(pd.acc_blk, pd.go ? 2 * DB * kBlkBytes : 0)
                       : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, pd.go ? 64 * D * 4 : 0);
-      pd.sem = p.sem + bh * p.sem_stride + (task.y * SUBS + ps % SUBS) * 4 + w;
+      pd.sem = p.sem + bh * p.sem_stride + (q0s / BQ) * 4 + w;
 #ifdef DASH_REPLAY
       // Dump layout: [b*H + h][64-row step][dQ block (2 DB)][rank][kDqBlock floats].
       pd.dump = p.replay ? p.replay + (((bh * (p.row_stride / BQ) + q0s / BQ) * (2 * DB)) * p.replay_ranks + pd.rank) *
@@ -468,9 +477,9 @@ bwd_main_kernel(BwdParams p) {
     for (int s = 0; s < n_steps; ++s) {
       PROF_COUNT(kProfSteps);
       const int buf = (par0 + s) & 1;
-      const Quad task = load_quad(tasks, t_begin + s / SUBS);
-      const int j = task.y;
-      const int q0 = j * BC + (s % SUBS) * BQ;
+      const int q0 = rec_cur.y;
+      const int j = q0 / BC;
+      const Quad rec_nn = load_quad(steps, t_begin * SUBS + s + 2);  // taken over at the step's end
 
       // Previous step's reduction: if the poll of the last step found no turn, wait
       // for it here and issue the running-sum loads now.
@@ -508,13 +517,10 @@ bwd_main_kernel(BwdParams p) {
       // the last barrier), spread over the S/dP slots: copy op o is Q block o, dO block
       // o - PER_WAVE, then -LSE*log2e (even waves) or -D (odd waves).
       // At the item's last step: the next item's first step. At the worker's last step
-      // (no next item) the current task is copied again, so that the copies need no
-      // branch: nothing reads that buffer any more.
-      const bool last_step = s + 1 == n_steps;
-      const Quad item_n = load_quad(items, it + 1);
-      const Quad task_n = load_quad(tasks, last_step ? (has_next ? item_n.w : t_begin) : t_begin + (s + 1) / SUBS);
-      const int q0_n = task_n.y * BC + ((s + 1) % SUBS) * BQ;
-      const int64_t bh_n = static_cast<int64_t>(last_step && has_next ? item_n.x : b) * H + task_n.x;
+      // the next record belongs to another worker (or is a zero record): copied all the
+      // same, so that the copies need no branch; nothing reads that buffer any more.
+      const int q0_n = rec_nxt.y;
+      const int64_t bh_n = rec_nxt.x;
       const bf16* q_n = p.q + bh_n * N * D;
       const bf16* do_n = p.dO + bh_n * N * D;
       LDS_AS char* const sQn = smem + C::OFF_Q + (buf ^ 1) * C::QT;
@@ -668,6 +674,7 @@ bwd_main_kernel(BwdParams p) {
       // copies, would otherwise wait for them too.
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) asm volatile("" : "+v"(ld[t2]));
+      PROF_MARK(kProfItem);
 #ifdef DASH_REPLAY
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
@@ -753,19 +760,18 @@ bwd_main_kernel(BwdParams p) {
         if (j == NIT) {
           // This step's contribution: bookkeeping and a poll of its turn (a plain load,
           // not waited for until half a phase later).
-          pd_n = reduce_prepare(s);
-          if (reduce_needs_turn(pd_n)) {
-            if (cross) {
-              sem_now = __hip_atomic_load(pd_n.sem, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            } else {
-              const unsigned u = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(pd_n.sem, 4), 0, 0, kSC0);
-              sem_now = static_cast<int>(u);
-            }
-          }
+          // The load is issued and its value read on every step (through an empty
+          // descriptor, which returns 0, when no turn is needed): a load into a register
+          // that some path leaves unread makes the compiler wait for all vector memory
+          // (the running-sum loads included) before the register is reused.
+          pd_n = reduce_prepare(rec_cur);
+          const rsrc_t srs = make_rsrc(pd_n.sem, reduce_needs_turn(pd_n) ? 4 : 0);
+          sem_now = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(srs, 0, 0, cross ? kSC1 : kSC0));
         }
         if (j == NIT + NIT / 2) {
           PROF_MARK(kProfBody);
-          loaded = !reduce_needs_turn(pd_n) || __builtin_amdgcn_readfirstlane(sem_now) == pd_n.rank;
+          const int sem_seen = __builtin_amdgcn_readfirstlane(sem_now);
+          loaded = !reduce_needs_turn(pd_n) || sem_seen == pd_n.rank;
           PROF_MARK(kProfPoll);
           if (loaded) {
             if (cross && reduce_needs_turn(pd_n)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -778,10 +784,14 @@ bwd_main_kernel(BwdParams p) {
       pd = pd_n;
       PROF_MARK(kProfBody);
       // dS^T of all waves is visible after the barrier (the copies were awaited above;
-      // the running-sum loads stay in flight across it).
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // the running-sum loads stay in flight across it). The wait is the compiler's own
+      // s_waitcnt, so that it also counts as the wait for the step record read ahead.
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      rec_cur = rec_nxt;
+      rec_nxt = rec_nn;
       PROF_MARK(kProfBarrier);
     }
     // The item's last step: its dQ partial and reduction.

@@ -73,10 +73,11 @@ int check_sizes(int B, int H, int Hkv, int N, int d, int mask, int schedule) {
 }
 
 struct DevTable {
-  void* buf = nullptr;  // worker_begin | items | tasks
+  void* buf = nullptr;  // worker_begin | items | tasks | steps
   const int* worker_begin = nullptr;
   const int4* items = nullptr;
   const int4* tasks = nullptr;
+  const int4* steps = nullptr;
   int workers = 0;
   int tile = 0;
   bool xcd_local = true;
@@ -192,11 +193,28 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   const size_t wb_bytes = align256(sizeof(int32_t) * t.worker_begin.size());
   const size_t it_bytes = align256(sizeof(dash::Item) * t.items.size());
   const size_t tk_bytes = align256(sizeof(dash::Task) * (t.tasks.size() + 1));
-  std::vector<char> host(wb_bytes + it_bytes + tk_bytes, 0);
+  // The kernel's step stream: one record {b * H + h, first Q row, rank, last} per 64-row
+  // step, in task order (each worker's steps are contiguous, across its items), so that a
+  // step's bookkeeping is one record read ahead of time. Two zero records follow, for
+  // the read-ahead past a worker's last step (a valid head 0, row 0).
+  const int subs = tile / 64;
+  std::vector<int4> steps;
+  steps.reserve(t.tasks.size() * subs + 2);
+  for (size_t k = 0; k < t.tasks.size(); ++k) {
+    const dash::Task& tk = t.tasks[k];
+    const dash::Item& it = t.items[t.task_item[k]];
+    for (int sub = 0; sub < subs; ++sub)
+      steps.push_back(int4{it.b * H + tk.h, tk.j * tile + sub * 64, tk.rank, tk.last});
+  }
+  steps.push_back(int4{0, 0, 0, 0});
+  steps.push_back(int4{0, 0, 0, 0});
+  const size_t st_bytes = align256(sizeof(int4) * steps.size());
+  std::vector<char> host(wb_bytes + it_bytes + tk_bytes + st_bytes, 0);
   std::memcpy(host.data(), t.worker_begin.data(), sizeof(int32_t) * t.worker_begin.size());
   std::memcpy(host.data() + wb_bytes, t.items.data(), sizeof(dash::Item) * t.items.size());
   if (!t.tasks.empty())
     std::memcpy(host.data() + wb_bytes + it_bytes, t.tasks.data(), sizeof(dash::Task) * t.tasks.size());
+  std::memcpy(host.data() + wb_bytes + it_bytes + tk_bytes, steps.data(), sizeof(int4) * steps.size());
   DevTable dt;
   if (hipMalloc(&dt.buf, host.size()) != hipSuccess) return DASH_ERR_HIP;
   if (hipMemcpy(dt.buf, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
@@ -207,6 +225,7 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   dt.worker_begin = reinterpret_cast<const int*>(base);
   dt.items = reinterpret_cast<const int4*>(base + wb_bytes);
   dt.tasks = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes);
+  dt.steps = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes + tk_bytes);
   dt.workers = t.workers;
   dt.tile = tile;
   dt.xcd_local = t.xcd_local;
@@ -287,6 +306,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.worker_begin = tab->worker_begin;
   bp.items = tab->items;
   bp.tasks = tab->tasks;
+  bp.steps = tab->steps;
   bp.B = B;
   bp.H = H;
   bp.Hkv = Hkv;

@@ -112,6 +112,10 @@ __device__ __forceinline__ void raise_error(int* err, int code) {
                                        __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+// s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8) that waits for LDS and scalar-memory operations only: lgkmcnt(0).
+constexpr int kWaitLgkm0 = 0xC07F;
+
 // Waits until every memory operation this wave issued has completed: global stores
 // acknowledged by the L2, global->LDS copies landed. The signal fences keep the
 // compiler from moving memory operations across it.

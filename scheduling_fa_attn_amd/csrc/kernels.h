@@ -43,6 +43,7 @@ struct BwdParams {
   const int* worker_begin;
   const int4* items;
   const int4* tasks;
+  const int4* steps;   // per 64-row step in task order: {b * H + h, first Q row, rank, last}; 2 zero records follow
   int B, H, Hkv, N;
   int sem_stride;      // semaphores per (b, h): 4 per 64-row Q step (one per wave), padded
   int row_stride;      // rows per (b, h) of nlse2, neg_delta and dqacc: N rounded up to the tile
@@ -80,7 +81,7 @@ enum ProfSlot {
   kProfDq = 2,       // dQ turn bookkeeping: task record and accumulator addresses
   kProfWait = 3,     // waiting for the dQ turn (semaphore)
   kProfReduce = 4,   // waiting for this wave's copies at the step's end
-  kProfItem = 5,     // (unused)
+  kProfItem = 5,     // the step's first LDS reads issued and its running sums landed
   kProfSteps = 6,    // number of steps
   kProfTotal = 7,    // whole kernel
   kProfSd0 = 8,      // S/dP of the first block (with dQ MFMAs), from the accumulator loads on
