@@ -262,6 +262,21 @@ bwd_main_kernel(BwdParams p) {
     __syncthreads();
     PROF_MARK(kProfPro);
 
+    // The dQ MFMAs start from the loaded running sum, except in the atomic variant and in
+    // replay builds, which start from zero: then the first k-step uses a literal 0 as its
+    // accumulator input, so that no VALU instruction writes the accumulator right before
+    // an inline MFMA reads it.
+#ifdef DASH_REPLAY
+    constexpr bool kZeroStart = true;
+#else
+    constexpr bool kZeroStart = !DET;
+#endif
+    auto dq_mma = [&](floatx16& acc, int kk, const bf16x8& a, const bf16x8& b) __attribute__((always_inline)) {
+      if (kZeroStart && kk == 0)
+        mfma32_vab_zero(acc, a, b);
+      else
+        mfma32_vab(acc, a, b);
+    };
     // Block t2 of this wave's dQ partial of step `ps` (its dS^T is in LDS buffer
     // (par0 + ps) & 1) = init + dS K, accumulated in place; accumulator row m of block qb is Q
     // row q0 + pi(32 qb + m). Block t2 uses d block db_k(t2 % NKD).
@@ -280,7 +295,7 @@ bwd_main_kernel(BwdParams p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         if (kk + 1 < KK) a[(kk + 1) & 1] = load(kk + 1);
-        mfma32_vab(acc, a[kk & 1], kT[kd][kk]);
+        dq_mma(acc, kk, a[kk & 1], kT[kd][kk]);
         __builtin_amdgcn_sched_barrier(0);
       }
       mfma_result_wait(acc);
@@ -367,6 +382,12 @@ bwd_main_kernel(BwdParams p) {
     // atomic variant) reads through an empty descriptor, which returns zeros without
     // touching memory.
     auto reduce_load = [&](const Pending& pd, floatx16 (&ld)[C::NBLK]) __attribute__((always_inline)) {
+      if (!DET) {
+        // The atomic variant adds partials from zero (kZeroStart) and issues no load: a
+        // load would make the next wait for it also wait for every float atomic issued
+        // before it.
+        return;
+      }
       const rsrc_t lrs = make_rsrc(pd.acc_blk, reduce_needs_turn(pd) ? 2 * DB * kBlkBytes : 0);
 #pragma unroll
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
@@ -595,12 +616,14 @@ bwd_main_kernel(BwdParams p) {
         return x;
       };
       // Softmax of block qb spread over 8 slots (2 elements each); the row terms of
-      // group t are loaded one slot before its first element (ring of 2).
+      // group t + 1 are loaded at the first slot of group t, two slots before they are
+      // used (ring of 2), so that their LDS latency is hidden even where the scheduler
+      // puts the softmax first in its slot.
       auto softmax_slot = [&](int qb, int slot, const floatx16& S, const floatx16& dP, floatx4 (&nlr)[2],
                               u32x4 (&Pw)[2], u32x4 (&dSw)[2]) __attribute__((always_inline)) {
         const int t = slot >> 1;
+        if (!(slot & 1) && t + 1 < 4) nlr[(t + 1) & 1] = load_nl(qb, t + 1);
         softmax2(qb, 2 * slot, S, dP, nlr[t & 1], Pw, dSw);
-        if ((slot & 1) && t + 1 < 4) nlr[(t + 1) & 1] = load_nl(qb, t + 1);
       };
 #define SLOT() __builtin_amdgcn_sched_barrier(0)
       // Operands are read from LDS kPF slots ahead of their MFMAs (rings of kPF + 1).
@@ -663,7 +686,7 @@ bwd_main_kernel(BwdParams p) {
 #pragma unroll
         for (int n = 0; n < dq_count(i); ++n) {
           const int m = dq_first(i) + n, t2 = m / KK, kk = m % KK;
-          mfma32_vab(ld[t2], aqd[m % kQRing], kT[t2 % C::NKD][kk]);
+          dq_mma(ld[t2], kk, aqd[m % kQRing], kT[t2 % C::NKD][kk]);
         }
       };
 #pragma unroll
@@ -677,10 +700,7 @@ bwd_main_kernel(BwdParams p) {
       PROF_MARK(kProfItem);
 #ifdef DASH_REPLAY
 #pragma unroll
-      for (int t2 = 0; t2 < C::NBLK; ++t2) {
-        run[t2] = ld[t2];
-        ld[t2] = floatx16{};
-      }
+      for (int t2 = 0; t2 < C::NBLK; ++t2) run[t2] = ld[t2];
 #endif
       SLOT();
       // Block 0: S/dP, with dQ blocks [0, kBlkA) of the previous step and the next
@@ -689,7 +709,7 @@ bwd_main_kernel(BwdParams p) {
       for (int ks = 0; ks < DK; ++ks) {
         sd_prefetch(ks);
         if (ks + 1 < NSD) dq_load(ks + 1);
-        if (ks + 1 == DK) nlr[0] = load_nl(0, 0);
+        if (ks == DK / 2) nlr[0] = load_nl(0, 0);
         if (ks == DK / 2) dP1 = load_negd(1);
         sd_mfma(ks, S0, dP0);
         dq_mfma(ks);
@@ -714,7 +734,7 @@ bwd_main_kernel(BwdParams p) {
         dq_mfma(DK + ks);
 #pragma unroll
         for (int sl = (8 / DK) * ks; sl < (8 / DK) * (ks + 1); ++sl) softmax_slot(0, sl, S0, dP0, nlr, P0, dS0);
-        if (ks + 1 == DK) nlr[0] = load_nl(1, 0);
+        if (ks == (6 * DK) / 8) nlr[0] = load_nl(1, 0);  // after group 2 of block 0 (slots 4, 5)
         // Stores of the first dQ blocks (4 parts each) over these slots.
 #pragma unroll
         for (int x = ks * 4 * kBlkA / DK; x < (ks + 1) * 4 * kBlkA / DK; ++x) reduce_store_part(pd, x / 4, x % 4, ld[x / 4]);
@@ -752,8 +772,18 @@ bwd_main_kernel(BwdParams p) {
         if (j + 1 == NIT) {
           PROF_MARK(kProfDv0);
           // Stores and copies acknowledged (the copies were issued a phase earlier):
-          // the turn is passed on; the next step's tiles are in LDS.
-          wait_mem_done();
+          // the turn is passed on; the next step's tiles are in LDS. The atomic variant
+          // passes no turn: it waits for the copies only, and its float atomics, all
+          // issued after the copies, stay in flight (the vector-memory counter drains in
+          // issue order).
+          if (DET) {
+            wait_mem_done();
+          } else {
+            constexpr int kAtomics = 16 * C::NBLK < 63 ? 16 * C::NBLK : 63;
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(kAtomics));
+            __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          }
           if (have_prev) reduce_signal(pd);
           PROF_MARK(kProfReduce);
         }
@@ -765,8 +795,10 @@ bwd_main_kernel(BwdParams p) {
           // that some path leaves unread makes the compiler wait for all vector memory
           // (the running-sum loads included) before the register is reused.
           pd_n = reduce_prepare(rec_cur);
-          const rsrc_t srs = make_rsrc(pd_n.sem, reduce_needs_turn(pd_n) ? 4 : 0);
-          sem_now = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(srs, 0, 0, cross ? kSC1 : kSC0));
+          if (DET) {
+            const rsrc_t srs = make_rsrc(pd_n.sem, reduce_needs_turn(pd_n) ? 4 : 0);
+            sem_now = static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(srs, 0, 0, cross ? kSC1 : kSC0));
+          }
         }
         if (j == NIT + NIT / 2) {
           PROF_MARK(kProfBody);
@@ -804,7 +836,6 @@ bwd_main_kernel(BwdParams p) {
       for (int t2 = 0; t2 < C::NBLK; ++t2) {
 #ifdef DASH_REPLAY
         run[t2] = ld[t2];
-        ld[t2] = floatx16{};
 #endif
         dq_block(n_steps - 1, t2, ld[t2]);
         reduce_store(pd, t2, ld[t2]);

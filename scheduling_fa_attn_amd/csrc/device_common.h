@@ -115,6 +115,9 @@ __device__ __forceinline__ void raise_error(int* err, int code) {
 // s_waitcnt immediate (gfx9 encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
 // 11:8) that waits for LDS and scalar-memory operations only: lgkmcnt(0).
 constexpr int kWaitLgkm0 = 0xC07F;
+// s_waitcnt immediate that waits until at most n (0..63) vector-memory operations of
+// this wave are outstanding: vmcnt(n).
+constexpr int wait_vmcnt(int n) { return (n & 15) | ((n >> 4) << 14) | 0x70 | 0xF00; }
 
 // Waits until every memory operation this wave issued has completed: global stores
 // acknowledged by the L2, global->LDS copies landed. The signal fences keep the

@@ -157,10 +157,15 @@ def find_hazards(insts, labels):
     return found
 
 
-def _compile_asm(d, nw, out):
+# Library flavours that run on the GPU: release, profiling (-DDASH_PROFILE), replay
+# (-DDASH_REPLAY).
+FLAVOURS = {"release": [], "profile": ["-DDASH_PROFILE"], "replay": ["-DDASH_REPLAY"]}
+
+
+def _compile_asm(d, nw, flavour, out):
     cmd = [dash_build.HIPCC] + dash_build.COMMON + [f"-DDASH_MAIN_D={d}", f"-DDASH_MAIN_NW={nw}"] + \
-        dash_build.MAIN_FLAGS[(d, nw)] + ["--cuda-device-only", "-S", "-x", "hip",
-                                          os.path.join(dash_build.HERE, "csrc", "bwd_main.hip"), "-o", out]
+        dash_build.MAIN_FLAGS[(d, nw)] + FLAVOURS[flavour] + \
+        ["--cuda-device-only", "-S", "-x", "hip", os.path.join(dash_build.HERE, "csrc", "bwd_main.hip"), "-o", out]
     return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
 
 
@@ -170,9 +175,10 @@ def kernel_asm(tmp_path_factory):
         pytest.skip("hipcc not available")
     tmp = tmp_path_factory.mktemp("asm")
     procs = {}
-    for key in dash_build.MAIN_FLAGS:
-        out = str(tmp / f"bwd_main_d{key[0]}_nw{key[1]}.s")
-        procs[key] = (out, _compile_asm(key[0], key[1], out))
+    for (d, nw) in dash_build.MAIN_FLAGS:
+        for flavour in FLAVOURS:
+            out = str(tmp / f"bwd_main_d{d}_nw{nw}_{flavour}.s")
+            procs[(d, nw, flavour)] = (out, _compile_asm(d, nw, flavour, out))
     texts = {}
     for key, (out, proc) in procs.items():
         _, err = proc.communicate(timeout=600)
@@ -182,14 +188,17 @@ def kernel_asm(tmp_path_factory):
     return texts
 
 
-# (ordered reduction, cross-XCD chains): the three instantiations of each (d, nw).
-VARIANTS = [(d, nw, det, cross) for (d, nw) in sorted(dash_build.MAIN_FLAGS) for det, cross in ((1, 0), (1, 1), (0, 0))]
+# (ordered reduction, cross-XCD chains): the three instantiations of each (d, nw), in
+# every flavour.
+VARIANTS = [(d, nw, det, cross, fl) for (d, nw) in sorted(dash_build.MAIN_FLAGS)
+            for det, cross in ((1, 0), (1, 1), (0, 0)) for fl in FLAVOURS]
 
 
-@pytest.mark.parametrize("d,nw,det,cross", VARIANTS, ids=[f"d{v[0]}-nw{v[1]}-det{v[2]}-cross{v[3]}" for v in VARIANTS])
-def test_inline_mfma_wait_states(kernel_asm, d, nw, det, cross):
+@pytest.mark.parametrize("d,nw,det,cross,flavour", VARIANTS,
+                         ids=[f"d{v[0]}-nw{v[1]}-det{v[2]}-cross{v[3]}-{v[4]}" for v in VARIANTS])
+def test_inline_mfma_wait_states(kernel_asm, d, nw, det, cross, flavour):
     symbol = f"_ZN4dash15bwd_main_kernelILi{d}ELi{nw}ELb{det}ELb{cross}EEEvNS_9BwdParamsE"
-    insts, labels = parse_kernel(kernel_asm[(d, nw)], symbol)
+    insts, labels = parse_kernel(kernel_asm[(d, nw, flavour)], symbol)
     n_mfma = sum(1 for i in insts if i.mfma and i.asm)
     assert n_mfma >= 48, n_mfma
     hazards = find_hazards(insts, labels)
