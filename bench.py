@@ -238,6 +238,49 @@ def measure_workload(name, schedule, steps, warmup, compare):
             "roofline_frac": round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+# The DASH paper's benchmark grid (section 4.1): 16 384 tokens in total and hidden size
+# 2048, so B = 16384 / N and H = Hkv = 2048 / d, for each sequence length, head size and
+# mask.
+SWEEP_N = (512, 1024, 2048, 4096, 8192, 16384)
+SWEEP_SCHEDULES = {False: ("naive", "descending", "shift"), True: ("naive", "descending", "sym_shift")}
+
+
+def sweep(steps, warmup):
+    """Every deterministic schedule and the atomic variant (of the best schedule) over the
+    paper's grid; returns one record per (N, d, mask)."""
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    out = []
+    idx = 0
+    for d in (64, 128):
+        for causal in (False, True):
+            for N in SWEEP_N:
+                B, H = 16384 // N, 2048 // d
+                shape = (B, H, H, N, d)
+                seed = 2000 + idx
+                idx += 1
+                dev = make_inputs(B, H, H, N, d, causal, seed)
+                ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, H, N, d), dtype=torch.uint8, device="cuda")
+                fl = flops_bwd(B, H, N, d, causal)
+                rec = {"N": N, "d": d, "B": B, "H": H, "mask": "causal" if causal else "full", "seed": seed,
+                       "tflops": {}}
+                best = SWEEP_SCHEDULES[causal][-1]
+                for s in SWEEP_SCHEDULES[causal]:
+                    ms, main_ms, _ = time_schedule(dev, shape, causal, s, 1, steps, warmup, ws)
+                    rec["tflops"][s] = round(fl / (ms * 1e-3) / 1e12, 1)
+                    if s == best:
+                        rec["main_kernel_frac"] = round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                ms_a, _, _ = time_schedule(dev, shape, causal, best, 0, steps, warmup, ws)
+                rec["tflops"]["atomic_" + best] = round(fl / (ms_a * 1e-3) / 1e12, 1)
+                log(f"sweep N={N} d={d} {rec['mask']}: " + ", ".join(f"{k} {v}" for k, v in rec["tflops"].items()))
+                out.append(rec)
+                del dev, ws
+                torch.cuda.empty_cache()
+    return out
+
+
 # Sources of the main kernel: the HBM-traffic figures in profiles/ hold for the kernel
 # these hashed to when the counters were taken.
 KERNEL_SOURCES = ("scheduling_fa_attn_amd/csrc/bwd_main.hip", "scheduling_fa_attn_amd/csrc/device_common.h",
@@ -282,6 +325,9 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing (L2 and memory-side cache flushed before every call)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time every schedule and the atomic variant over the paper's grid (16 384 tokens, "
+                         "hidden 2048, N = 512 .. 16384, d = 64 and 128, both masks) and print one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scale factor) and exit")
@@ -306,6 +352,10 @@ def main():
         return
 
     torch.cuda.set_device(0)
+    if args.sweep:
+        print(json.dumps({"sweep": sweep(args.steps, args.warmup), "unit": "TFLOPS", "steps": args.steps,
+                          "warmup": args.warmup, "data": "synthetic"}), flush=True)
+        return
     main_res = measure_workload(args.workload, args.schedule, args.steps, args.warmup, not args.no_compare)
     B, H, Hkv, N, d, causal, _, _, cfg_index = WORKLOADS[args.workload]
     others = {}
