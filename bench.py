@@ -44,6 +44,38 @@ def flops_bwd(B, H, N, d, causal):
     return f / 2.0 if causal else f
 
 
+def flops_fwd(B, H, N, d, causal):
+    f = 4.0 * N * N * d * B * H
+    return f / 2.0 if causal else f
+
+
+def time_forward(dev, d, causal, steps, warmup):
+    """dash_attn_fwd on the workload's Q, K, V (outputs to scratch tensors): ms per call."""
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    o = torch.empty_like(dev["q"])
+    lse = torch.empty(dev["q"].shape[:3], dtype=torch.float32, device="cuda")
+    mask = "causal" if causal else "full"
+
+    def call():
+        st = dash.dash_attn_fwd(dev["q"], dev["k"], dev["v"], o, lse, 1.0 / math.sqrt(d), mask)
+        if st != dash.DASH_OK:
+            raise dash.DashError(st, "dash_attn_fwd")
+
+    for _ in range(warmup):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(steps):
+        call()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
 def make_inputs(B, H, Hkv, N, d, causal, seed):
     import numpy as np
     import torch
@@ -230,12 +262,17 @@ def measure_workload(name, schedule, steps, warmup, compare):
         ratio = ms_a / ms
         log(f"  {schedule} atomic: {ms_a:.3f} ms/step ({extra['atomic_' + schedule]:.1f} TFLOPS); "
             f"det/non-det throughput ratio {ratio:.3f}")
+    ms_f = time_forward(dev, d, causal, steps, warmup)
+    fl_f = flops_fwd(B, H, N, d, causal)
+    fwd = {"ms": round(ms_f, 4), "tflops": round(fl_f / (ms_f * 1e-3) / 1e12, 2),
+           "roofline_frac": round(fl_f / (ms_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    log(f"  forward (dash_attn_fwd): {ms_f:.3f} ms ({fwd['tflops']:.1f} TFLOPS)")
     del dev, ws
     torch.cuda.empty_cache()
     return {"schedule": schedule, "tflops": round(tflops, 2), "ms_per_step": round(ms, 4),
             "main_kernel_ms": round(main_ms, 4), "det_nondet_ratio": None if ratio is None else round(ratio, 4),
             "schedules_tflops": extra,
-            "roofline_frac": round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            "roofline_frac": round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "forward": fwd}
 
 
 # The DASH paper's benchmark grid (section 4.1): 16 384 tokens in total and hidden size
@@ -364,7 +401,8 @@ def main():
             if name != args.workload:
                 r = measure_workload(name, None, args.steps, args.warmup, not args.no_compare)
                 others[name] = {k: r[k] for k in ("schedule", "tflops", "ms_per_step", "main_kernel_ms",
-                                                  "det_nondet_ratio", "schedules_tflops", "roofline_frac")}
+                                                  "det_nondet_ratio", "schedules_tflops", "roofline_frac",
+                                                  "forward")}
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
@@ -387,6 +425,7 @@ def main():
                    "deterministic": True, "seed": 1000 + cfg_index},
         "det_nondet_ratio": main_res["det_nondet_ratio"],
         "schedules_tflops": main_res["schedules_tflops"],
+        "forward": main_res["forward"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.workload, kernel),

@@ -117,6 +117,18 @@ int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream,
                         void* main_start, void* main_stop);
 
+/* The forward pass ("Writing an Attention Kernel", Steps 1 and 2): O = softmax(s Q K^T) V
+ * and lse = the natural-log log-sum-exp of each query row's scaled scores s q.k, i.e.
+ * the o and lse that dash_attn_bwd takes. Key tiles are visited in ascending order with
+ * an online softmax (running maximum and sum per row); the result is deterministic.
+ * q: [B, H, N, d], k, v: [B, Hkv, N, d] bf16 (read); o: [B, H, N, d] bf16 and
+ * lse: [B, H, N] float32 (written). Device pointers owned by the caller; q, k, v, o
+ * 16-byte aligned, lse 4-byte aligned. Same size, mask and scale rules as dash_attn_bwd;
+ * no workspace and no schedule. B == 0 or N == 0 is a no-op that returns DASH_OK.
+ * Errors (before anything is enqueued): DASH_ERR_INVALID_ARG, _UNSUPPORTED; DASH_ERR_HIP
+ * if the launch fails. */
+int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Hkv, int N, int d, float softmax_scale, int mask, void* stream);
 /* Synchronizes the current device, returns the device error word left by the
  * kernels since the last call (DASH_OK, DASH_ERR_TIMEOUT or DASH_ERR_PLACEMENT)
  * and clears it. Returns DASH_ERR_HIP if the synchronization itself fails. */

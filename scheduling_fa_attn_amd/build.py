@@ -37,6 +37,7 @@ UNITS = [
     for (d, nw), fl in MAIN_FLAGS.items()
 ] + [
     ("aux_kernels.hip", [], "aux_kernels.o"),
+    ("fwd_main.hip", [], "fwd_main.o"),
     ("dash_api.cpp", [], "dash_api.o"),
     ("schedule.cpp", [], "schedule.o"),
 ]

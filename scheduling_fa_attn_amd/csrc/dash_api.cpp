@@ -356,6 +356,37 @@ size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d) {
   return ws_layout(B, H, N, d).total;
 }
 
+int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
+                  int d, float softmax_scale, int mask, void* stream) {
+  if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return DASH_ERR_INVALID_ARG;
+  if (N > (1 << 22) || int64_t(B) * H > (int64_t(1) << 24)) return DASH_ERR_INVALID_ARG;
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return DASH_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return DASH_ERR_UNSUPPORTED;
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale)) return DASH_ERR_INVALID_ARG;
+  if (B == 0 || N == 0) return DASH_OK;
+  const void* ptrs[] = {q, k, v, o};
+  for (const void* ptr : ptrs)
+    if (ptr == nullptr || !aligned(ptr, 16)) return DASH_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return DASH_ERR_INVALID_ARG;
+  const int64_t n_qt = cdiv(N, 128);
+  if (int64_t(B) * H * n_qt > 0x7fffffff) return DASH_ERR_INVALID_ARG;
+  dash::FwdParams fp;
+  fp.q = static_cast<const __bf16*>(q);
+  fp.k = static_cast<const __bf16*>(k);
+  fp.v = static_cast<const __bf16*>(v);
+  fp.o = static_cast<__bf16*>(o);
+  fp.lse = lse;
+  fp.B = B;
+  fp.H = H;
+  fp.Hkv = Hkv;
+  fp.N = N;
+  fp.n_qt = static_cast<int>(n_qt);
+  fp.causal = mask == DASH_MASK_CAUSAL ? 1 : 0;
+  fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  if (dash::launch_fwd(fp, d, static_cast<hipStream_t>(stream)) != hipSuccess) return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
 int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,
                   void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d, float softmax_scale, int mask,
                   int schedule, int deterministic, void* workspace, size_t workspace_bytes, void* stream) {

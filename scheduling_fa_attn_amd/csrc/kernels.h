@@ -60,6 +60,19 @@ struct BwdParams {
   int replay_ranks;         // replay builds: rank slots per dQ block in the dump (KV tiles per head)
 };
 
+// Forward kernel (O and the natural-log LSE from Q, K, V).
+struct FwdParams {
+  const __bf16* q;   // [B, H, N, d]
+  const __bf16* k;   // [B, Hkv, N, d]
+  const __bf16* v;   // [B, Hkv, N, d]
+  __bf16* o;         // [B, H, N, d]
+  float* lse;        // [B, H, N]
+  int B, H, Hkv, N;
+  int n_qt;          // 128-row Q tiles per head
+  int causal;
+  float scale_log2;  // softmax scale * log2(e)
+};
+
 // fp32 dQ accumulator layouts (rows per (b, h) padded to row_stride).
 // - Ordered variant, block layout: the rows are cut into 32-row blocks and the d
 //   columns into 32-column blocks; block (qblk, db) is kDqBlock floats at
@@ -118,5 +131,6 @@ hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int 
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
                           hipStream_t stream);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
+hipError_t launch_fwd(const FwdParams& prm, int d, hipStream_t stream);
 
 }  // namespace dash

@@ -35,6 +35,7 @@ EXPORTED = (
     "dash_tile_size",
     "dash_schedule_table",
     "dash_set_placement",
+    "dash_attn_fwd",
 )
 
 _lib = None
@@ -81,6 +82,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_schedule_table.restype = i
     lib.dash_set_placement.argtypes = [i]
     lib.dash_set_placement.restype = i
+    lib.dash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
+    lib.dash_attn_fwd.restype = i
     if hasattr(lib, "dash_profile_attach"):
         lib.dash_profile_attach.argtypes = [vp]
         lib.dash_profile_attach.restype = i
@@ -137,6 +140,20 @@ def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):
 
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def dash_attn_fwd(q, k, v, o, lse, softmax_scale, mask, stream=None, lib=None) -> int:
+    """Call dash_attn_fwd on torch device tensors: q [B, H, N, d], k, v [B, Hkv, N, d] bf16
+    (read); o [B, H, N, d] bf16 and lse [B, H, N] fp32 (written). Returns the status code."""
+    import torch
+
+    lib = lib or load()
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    return int(lib.dash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Hkv, N, d,
+                                 float(softmax_scale), MASKS.get(mask, mask), ctypes.c_void_p(stream)))
 
 
 def dash_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, softmax_scale, mask, schedule, deterministic, workspace,
