@@ -257,6 +257,10 @@ def measure_workload(name, schedule, steps, warmup, compare):
                 dash.dash_set_placement("aggregate")
             extra[schedule + "_spread"] = round(fl / (ms_sp * 1e-3) / 1e12, 2)
             log(f"  {schedule} det, spread placement: {ms_sp:.3f} ms/step ({extra[schedule + '_spread']:.1f} TFLOPS)")
+        ms_t, _, _ = time_schedule(dev, shape, causal, schedule, 2, steps, warmup, ws)
+        extra["two_pass_" + schedule] = round(fl / (ms_t * 1e-3) / 1e12, 2)
+        log(f"  {schedule} two-pass (dK/dV pass + separate dQ pass): {ms_t:.3f} ms/step "
+            f"({extra['two_pass_' + schedule]:.1f} TFLOPS)")
         ms_a, _, _ = time_schedule(dev, shape, causal, schedule, 0, steps, warmup, ws)
         extra["atomic_" + schedule] = round(fl / (ms_a * 1e-3) / 1e12, 2)
         ratio = ms_a / ms
@@ -309,6 +313,8 @@ def sweep(steps, warmup):
                     rec["tflops"][s] = round(fl / (ms * 1e-3) / 1e12, 1)
                     if s == best:
                         rec["main_kernel_frac"] = round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+                ms_t, _, _ = time_schedule(dev, shape, causal, best, 2, steps, warmup, ws)
+                rec["tflops"]["two_pass_" + best] = round(fl / (ms_t * 1e-3) / 1e12, 1)
                 ms_a, _, _ = time_schedule(dev, shape, causal, best, 0, steps, warmup, ws)
                 rec["tflops"]["atomic_" + best] = round(fl / (ms_a * 1e-3) / 1e12, 1)
                 log(f"sweep N={N} d={d} {rec['mask']}: " + ", ".join(f"{k} {v}" for k, v in rec["tflops"].items()))

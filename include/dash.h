@@ -95,6 +95,11 @@ size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
  * deterministic = 0: dQ partial sums are added with floating-point atomics
  *   (completion order, not reproducible; kept for comparison, section 1). The
  *   schedule still sets the tile order.
+ * deterministic = 2: two-pass variant, the alternative the paper contrasts with its
+ *   design (section 5): the main kernel computes dK and dV only, and a second kernel
+ *   walks all key tiles for each query tile, recomputing S and dP, with dQ kept in
+ *   registers (deterministic, no cross-CU reduction). The schedule sets the tile
+ *   order of the dK/dV pass.
  * softmax_scale must be finite and > 0 (1/sqrt(d) for standard attention).
  * B == 0 or N == 0 is a no-op that returns DASH_OK.
  * Errors: DASH_ERR_INVALID_ARG, _UNSUPPORTED, _WORKSPACE, _NOT_CORESIDENT, _HIP.

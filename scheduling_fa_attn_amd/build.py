@@ -38,6 +38,7 @@ UNITS = [
 ] + [
     ("aux_kernels.hip", [], "aux_kernels.o"),
     ("fwd_main.hip", [], "fwd_main.o"),
+    ("dq_pass.hip", [], "dq_pass.o"),
     ("dash_api.cpp", [], "dash_api.o"),
     ("schedule.cpp", [], "schedule.o"),
 ]

@@ -91,8 +91,9 @@ struct BwdCfg {
 // that neither carries the other's code and registers. CROSS (ordered reduction only):
 // the contributors of one dQ tile may sit on different XCDs, whose L2s are not coherent
 // with each other, so the running sums and turns go through device-scope accesses and
-// fences; otherwise every chain stays inside one XCD's L2.
-template <int D, int NW, bool DET, bool CROSS>
+// fences; otherwise every chain stays inside one XCD's L2. NODQ (with !DET): dK and dV
+// only, no dQ work at all (the two-pass variant computes dQ in a separate kernel).
+template <int D, int NW, bool DET, bool CROSS, bool NODQ>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_main_kernel(BwdParams p) {
   using C = BwdCfg<D, NW>;
@@ -128,6 +129,7 @@ bwd_main_kernel(BwdParams p) {
   const int H = p.H, Hkv = p.Hkv, N = p.N;
   constexpr bool cross = CROSS;
   static_assert(DET || !CROSS, "device-scope chains exist only in the ordered reduction");
+  static_assert(!(DET && NODQ), "the ordered reduction reduces dQ");
   bool failed = false;  // this wave gave up waiting (error reported); it keeps going without reducing
   // The schedule table is read-only for the whole launch: reading it through the
   // constant address space turns its uniform loads into scalar loads, which are
@@ -255,7 +257,7 @@ bwd_main_kernel(BwdParams p) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const int koff = kd_lane + 16 * kk * ST + 64 * db_k(kd);
-        kT[kd][kk] = to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST)));
+        kT[kd][kk] = NODQ ? bf16x8{} : to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST)));
       }
     }
     // Every wave has its V rows before step 0 issues step 1's copies into buffer 1.
@@ -281,6 +283,7 @@ bwd_main_kernel(BwdParams p) {
     // (par0 + ps) & 1) = init + dS K, accumulated in place; accumulator row m of block qb is Q
     // row q0 + pi(32 qb + m). Block t2 uses d block db_k(t2 % NKD).
     auto dq_block = [&](int ps, int t2, floatx16& acc) __attribute__((always_inline)) {
+      if (NODQ) return;
       const LDS_AS char* sdSp = smem + C::OFF_DS + ((par0 + ps) & 1) * C::DST;
       const int qb = (w + NW * t2) / DB;
       const int kd = t2 % C::NKD;
@@ -411,6 +414,7 @@ bwd_main_kernel(BwdParams p) {
     floatx16 run[C::NBLK];
 #endif
     auto reduce_store_part = [&](const Pending& pd, int t2, int i, const floatx16& v_in) __attribute__((always_inline)) {
+      if (NODQ) return;
 #ifdef DASH_REPLAY
       if (!pd.go) return;
       floatx16 v = v_in;
@@ -591,7 +595,7 @@ bwd_main_kernel(BwdParams p) {
         const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r0 + 1], p.scale_log2, nl[e0 + 1]));
         Pw[r0 >> 3][(r0 & 7) >> 1] = pack_bf16(p0, p1);
         dSw[r0 >> 3][(r0 & 7) >> 1] = pack_bf16(p0 * dP[r0], p1 * dP[r0 + 1]);
-        if ((r0 & 3) == 2) {
+        if (!NODQ && (r0 & 3) == 2) {
           const int t = r0 >> 2;
           u32x2 v2;
           v2[0] = dSw[t >> 1][2 * (t & 1)];
@@ -675,6 +679,7 @@ bwd_main_kernel(BwdParams p) {
       auto dq_first = [&](int i) __attribute__((always_inline)) { return i < DK ? i * kQ1 : kBlkA * KK + (i - DK) * kQ2; };
       auto dq_count = [&](int i) __attribute__((always_inline)) { return i < DK ? kQ1 : kQ2; };
       auto dq_load = [&](int i) __attribute__((always_inline)) {
+        if (NODQ) return;
 #pragma unroll
         for (int n = 0; n < dq_count(i); ++n) {
           const int m = dq_first(i) + n, t2 = m / KK, kk = m % KK;
@@ -683,6 +688,7 @@ bwd_main_kernel(BwdParams p) {
         }
       };
       auto dq_mfma = [&](int i) __attribute__((always_inline)) {
+        if (NODQ) return;
 #pragma unroll
         for (int n = 0; n < dq_count(i); ++n) {
           const int m = dq_first(i) + n, t2 = m / KK, kk = m % KK;
@@ -696,7 +702,8 @@ bwd_main_kernel(BwdParams p) {
       // vector-memory counter is in order, and the compiler, which does not see the
       // copies, would otherwise wait for them too.
 #pragma unroll
-      for (int t2 = 0; t2 < C::NBLK; ++t2) asm volatile("" : "+v"(ld[t2]));
+      for (int t2 = 0; t2 < C::NBLK; ++t2)
+        if (!NODQ) asm volatile("" : "+v"(ld[t2]));
       PROF_MARK(kProfItem);
 #ifdef DASH_REPLAY
 #pragma unroll
@@ -720,7 +727,8 @@ bwd_main_kernel(BwdParams p) {
       PROF_MARK(kProfSd0);
       mfma_result_wait(S0, dP0);  // before the VALU reads them (and the stores read ld)
 #pragma unroll
-      for (int t2 = 0; t2 < kBlkA; ++t2) asm volatile("" : "+v"(ld[t2]));
+      for (int t2 = 0; t2 < kBlkA; ++t2)
+        if (!NODQ) asm volatile("" : "+v"(ld[t2]));
       if (diag) mask_diag(0, S0);
       PROF_MARK(kProfMid0);
       SLOT();
@@ -743,7 +751,8 @@ bwd_main_kernel(BwdParams p) {
       PROF_MARK(kProfSd1);
       mfma_result_wait(S1, dP1);
 #pragma unroll
-      for (int t2 = kBlkA; t2 < C::NBLK; ++t2) asm volatile("" : "+v"(ld[t2]));
+      for (int t2 = kBlkA; t2 < C::NBLK; ++t2)
+        if (!NODQ) asm volatile("" : "+v"(ld[t2]));
       if (diag) mask_diag(1, S1);
       PROF_MARK(kProfMid1);
       SLOT();
@@ -779,7 +788,7 @@ bwd_main_kernel(BwdParams p) {
           if (DET) {
             wait_mem_done();
           } else {
-            constexpr int kAtomics = 16 * C::NBLK < 63 ? 16 * C::NBLK : 63;
+            constexpr int kAtomics = NODQ ? 0 : (16 * C::NBLK < 63 ? 16 * C::NBLK : 63);
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
             __builtin_amdgcn_s_waitcnt(wait_vmcnt(kAtomics));
             __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -824,6 +833,11 @@ bwd_main_kernel(BwdParams p) {
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       rec_cur = rec_nxt;
       rec_nxt = rec_nn;
+      // The step's dV/dK MFMAs are done: wait for them before anything else can read the
+      // accumulators. On every step, at the end of the loop body, so that the wait also
+      // precedes the copies of the accumulators the compiler may place on the loop's exit
+      // edge (and reads in the epilogue).
+      mfma_settle(accK, accV);
       PROF_MARK(kProfBarrier);
     }
     // The item's last step: its dQ partial and reduction.
@@ -852,7 +866,6 @@ bwd_main_kernel(BwdParams p) {
     if (has_next) issue_kv(it + 1, par0);
 
     // Epilogue: dK = s dK, dV; bf16 stores of this wave's 32 KV rows.
-    mfma_drain();
     bf16* dKg = p.dk + bg * N * D;
     bf16* dVg = p.dv + bg * N * D;
 #pragma unroll
@@ -881,9 +894,10 @@ static hipError_t launch_main_t(const BwdParams& prm, int grid, hipStream_t stre
   using C = BwdCfg<D, NW>;
   // At least 81 KiB of LDS so that exactly one workgroup fits on a CU.
   const int shmem = C::BYTES > 83 * 1024 ? C::BYTES : 83 * 1024;
-  auto fn = !prm.deterministic ? bwd_main_kernel<D, NW, false, false>
-            : prm.xcd_local      ? bwd_main_kernel<D, NW, true, false>
-                                 : bwd_main_kernel<D, NW, true, true>;
+  auto fn = prm.deterministic == 2 ? bwd_main_kernel<D, NW, false, false, true>
+            : !prm.deterministic     ? bwd_main_kernel<D, NW, false, false, false>
+            : prm.xcd_local          ? bwd_main_kernel<D, NW, true, false, false>
+                                     : bwd_main_kernel<D, NW, true, true, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;

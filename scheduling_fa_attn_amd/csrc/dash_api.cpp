@@ -242,7 +242,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
             void* ev_stop) {
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
-  if (deterministic != 0 && deterministic != 1) return DASH_ERR_INVALID_ARG;
+  if (deterministic < 0 || deterministic > 2) return DASH_ERR_INVALID_ARG;
   if (!(scale > 0.f) || !std::isfinite(scale)) return DASH_ERR_INVALID_ARG;
   if (B == 0 || N == 0) return DASH_OK;
   const void* ptrs[] = {q, k, v, o, dO, dq, dk, dv};
@@ -284,7 +284,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   pp.sem_count = int64_t(B) * H * L.sem_stride;
   pp.ctr = ctr;
   pp.ctr_count = kCtrInts;
-  pp.dqacc_zero = deterministic ? nullptr : dqacc;
+  pp.dqacc_zero = deterministic == 0 ? dqacc : nullptr;
   pp.zero_count = int64_t(B) * H * L.row_stride * d;
   const int64_t pre_threads = pp.rows * (d / 8);
   const int pre_grid = static_cast<int>(std::min<int64_t>(std::max<int64_t>(cdiv(pre_threads, 256), 1), 4096));
@@ -339,9 +339,31 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
   if (e != hipSuccess) return DASH_ERR_HIP;
   if (ev_stop && hipEventRecord(static_cast<hipEvent_t>(ev_stop), stream) != hipSuccess) return DASH_ERR_HIP;
-  const hipError_t ec = deterministic
-                           ? dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream)
-                           : dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream);
+  hipError_t ec;
+  if (deterministic == 2) {
+    dash::DqParams dp;
+    dp.q = static_cast<const __bf16*>(q);
+    dp.k = static_cast<const __bf16*>(k);
+    dp.v = static_cast<const __bf16*>(v);
+    dp.dO = static_cast<const __bf16*>(dO);
+    dp.nlse2 = nlse2;
+    dp.neg_delta = neg_delta;
+    dp.dq = static_cast<__bf16*>(dq);
+    dp.B = B;
+    dp.H = H;
+    dp.Hkv = Hkv;
+    dp.N = N;
+    dp.row_stride = L.row_stride;
+    dp.n_qt = static_cast<int>(cdiv(N, 128));
+    dp.causal = causal ? 1 : 0;
+    dp.scale = scale;
+    dp.scale_log2 = scale * 1.4426950408889634f;
+    ec = dash::launch_dq_pass(dp, d, stream);
+  } else if (deterministic == 1) {
+    ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream);
+  } else {
+    ec = dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream);
+  }
   if (ec != hipSuccess) return DASH_ERR_HIP;
   return DASH_OK;
 }

@@ -85,10 +85,15 @@ __device__ __forceinline__ void mfma_result_wait(floatx16& acc) {
 __device__ __forceinline__ void mfma_result_wait(floatx16& x, floatx16& y) {
   asm volatile("s_nop 7\n\ts_nop 7" : "+v"(x), "+v"(y));
 }
-// Wait states between the last MFMA writing an AGPR accumulator and VALU reads of it
-// (v_accvgpr_read): more than the 16-pass pipeline depth.
-__device__ __forceinline__ void mfma_drain() {
-  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 7" ::: "memory");
+// Wait states between MFMAs writing AGPR accumulators and any other reader of them
+// (v_accvgpr_read, stores): 13, more than an 8-pass MFMA needs. The accumulators are tied
+// to the wait, so that no read of them is scheduled before it.
+__device__ __forceinline__ void mfma_settle(floatx16 (&a)[2], floatx16 (&b)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[0]), "+a"(a[1]), "+a"(b[0]), "+a"(b[1]));
+}
+__device__ __forceinline__ void mfma_settle(floatx16 (&a)[4], floatx16 (&b)[4]) {
+  asm volatile("s_nop 7\n\ts_nop 4"
+               : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]), "+a"(b[0]), "+a"(b[1]), "+a"(b[2]), "+a"(b[3]));
 }
 
 // Scheduling hints (__builtin_amdgcn_sched_group_barrier): the instructions of the

@@ -73,6 +73,23 @@ struct FwdParams {
   float scale_log2;  // softmax scale * log2(e)
 };
 
+// dQ pass of the two-pass variant.
+struct DqParams {
+  const __bf16* q;          // [B, H, N, d]
+  const __bf16* k;          // [B, Hkv, N, d]
+  const __bf16* v;          // [B, Hkv, N, d]
+  const __bf16* dO;         // [B, H, N, d]
+  const float* nlse2;       // [B*H][row_stride] -LSE * log2(e)
+  const float* neg_delta;   // [B*H][row_stride] -D
+  __bf16* dq;               // [B, H, N, d]
+  int B, H, Hkv, N;
+  int row_stride;
+  int n_qt;                 // 128-row Q tiles per head
+  int causal;
+  float scale;              // softmax scale s
+  float scale_log2;         // s * log2(e)
+};
+
 // fp32 dQ accumulator layouts (rows per (b, h) padded to row_stride).
 // - Ordered variant, block layout: the rows are cut into 32-row blocks and the d
 //   columns into 32-column blocks; block (qblk, db) is kDqBlock floats at
@@ -132,5 +149,6 @@ hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int 
                           hipStream_t stream);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& prm, int d, hipStream_t stream);
+hipError_t launch_dq_pass(const DqParams& prm, int d, hipStream_t stream);
 
 }  // namespace dash

@@ -94,7 +94,8 @@ def _call(**kw):
     (dict(schedule=4), dash.DASH_ERR_INVALID_ARG),
     (dict(mask=1, schedule=2), dash.DASH_ERR_UNSUPPORTED),
     (dict(mask=0, schedule=3), dash.DASH_ERR_UNSUPPORTED),
-    (dict(det=2), dash.DASH_ERR_INVALID_ARG),
+    (dict(det=3), dash.DASH_ERR_INVALID_ARG),
+    (dict(det=-1), dash.DASH_ERR_INVALID_ARG),
     (dict(scale=0.0), dash.DASH_ERR_INVALID_ARG),
     (dict(scale=float("inf")), dash.DASH_ERR_INVALID_ARG),
     (dict(q=None), dash.DASH_ERR_INVALID_ARG),
@@ -104,6 +105,31 @@ def _call(**kw):
 ])
 def test_argument_errors_before_any_launch(kw, status):
     assert _call(**kw) == status
+
+
+def _call_fwd(**kw):
+    lib = dash.load()
+    args = dict(q=1 << 12, k=1 << 12, v=1 << 12, o=1 << 12, lse=1 << 12, B=1, H=2, Hkv=2, N=256, d=64,
+                scale=0.125, mask=0, stream=None)
+    args.update(kw)
+    vp = ctypes.c_void_p
+    return lib.dash_attn_fwd(*(vp(args[k]) for k in ("q", "k", "v", "o", "lse")), args["B"], args["H"],
+                             args["Hkv"], args["N"], args["d"], args["scale"], args["mask"], vp(args["stream"]))
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d=96), dash.DASH_ERR_UNSUPPORTED),
+    (dict(H=3), dash.DASH_ERR_INVALID_ARG),
+    (dict(Hkv=0), dash.DASH_ERR_INVALID_ARG),
+    (dict(mask=2), dash.DASH_ERR_INVALID_ARG),
+    (dict(scale=-1.0), dash.DASH_ERR_INVALID_ARG),
+    (dict(q=None), dash.DASH_ERR_INVALID_ARG),
+    (dict(o=(1 << 12) + 8), dash.DASH_ERR_INVALID_ARG),
+    (dict(lse=(1 << 12) + 2), dash.DASH_ERR_INVALID_ARG),
+    (dict(B=0, q=None, o=None), dash.DASH_OK),
+])
+def test_forward_argument_errors_before_any_launch(kw, status):
+    assert _call_fwd(**kw) == status
 
 
 def test_empty_inputs_are_a_no_op():

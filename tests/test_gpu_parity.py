@@ -4,7 +4,9 @@ Bar (per tensor): max |GPU - oracle| / max |oracle| <= 1e-2, the tolerance the
 workload specification fixes for bf16 inputs/outputs with fp32 accumulation.
 Deterministic schedules must also give bitwise identical dQ/dK/dV on repeated runs.
 Cases span several KV tiles, ragged tails (N not a multiple of the tile), grouped
-query heads, both head dims, both masks, all four schedules and the atomic variant.
+query heads, both head dims, both masks, all four schedules, the atomic variant
+(deterministic = 0) and the two-pass variant (deterministic = 2: dK/dV pass plus a
+separate dQ pass).
 """
 import pytest
 
@@ -48,7 +50,7 @@ def test_parity_all_schedules(shape, causal):
     for sched in SCHEDS[causal]:
         if sched == "sym_shift" and n_tiles % 2:
             continue
-        for det in (1, 0):
+        for det in (1, 0, 2):
             print(f"case {_ids(shape)} causal={causal} schedule={sched} det={det}", flush=True)
             (dq, dk, dv), _ = run(case, dev, sched, det)
             errs = rel_errs((dq, dk, dv), (dq_r, dk_r, dv_r))
@@ -59,9 +61,9 @@ def test_parity_all_schedules(shape, causal):
 def test_repeat_runs_bitwise_identical(causal):
     case = make_case(2, 4, 2, 700, 128, causal, seed=77)
     dev = to_device(case)
-    for sched in SCHEDS[causal]:
-        ref, ws = run(case, dev, sched, 1)
+    for sched, det in [(s, 1) for s in SCHEDS[causal]] + [(SCHEDS[causal][-1], 2)]:
+        ref, ws = run(case, dev, sched, det)
         ref_bytes = [bf16_bytes(t) for t in ref]
         for rep in range(19):
-            out, ws = run(case, dev, sched, 1, workspace=ws)
-            assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, rep)
+            out, ws = run(case, dev, sched, det, workspace=ws)
+            assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, det, rep)
