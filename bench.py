@@ -412,7 +412,7 @@ def main():
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
-    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false>"
+    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false>"
     result = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 3),
