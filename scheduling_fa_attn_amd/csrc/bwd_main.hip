@@ -865,18 +865,37 @@ bwd_main_kernel(BwdParams p) {
     par0 = (par0 + n_steps) & 1;
     if (has_next) issue_kv(it + 1, par0);
 
-    // Epilogue: dK = s dK, dV; bf16 stores of this wave's 32 KV rows.
+    // Epilogue: dK = s dK, dV; bf16 stores of this wave's 32 KV rows. A lane holds one
+    // column of each 32x32 block, so the rows are put together in LDS first: in this
+    // wave's 32 rows of the dS^T buffer that the next item's step 0 writes (free since the
+    // last step's barrier, and the next item's prologue barrier comes before that step),
+    // 64 columns at a time; then every lane stores 16-byte row chunks.
+    LDS_AS char* stage = smem + C::OFF_DS + par0 * C::DST + 32 * w * kDsStride;
     bf16* dKg = p.dk + bg * N * D;
     bf16* dVg = p.dv + bg * N * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
+    for (int tns = 0; tns < 2; ++tns) {
+      const floatx16* acc = tns == 0 ? accK : accV;
+      const float mul = tns == 0 ? p.scale : 1.f;
+      bf16* g = tns == 0 ? dKg : dVg;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kvr = kv0 + 32 * w + 8 * (r >> 2) + 4 * hi + (r & 3);
-        if (kvr < N) {
-          const int off = kvr * D + db * 32 + l32;
-          dKg[off] = static_cast<bf16>(accK[db][r] * p.scale);
-          dVg[off] = static_cast<bf16>(accV[db][r]);
+      for (int half = 0; half < DB / 2; ++half) {
+        // Element r of block 2 half + e2: row 8 (r / 4) + 4 hi + r % 4, column 32 e2 + l32.
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = 8 * (r >> 2) + 4 * hi + (r & 3);
+            *reinterpret_cast<LDS_AS bf16*>(stage + row * kDsStride + 2 * (32 * e2 + l32)) =
+                static_cast<bf16>(acc[2 * half + e2][r] * mul);
+          }
+        // 32 rows x 128 bytes: chunk lane + 64 k is 16 bytes of row chunk / 8.
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int chunk = lane + 64 * k, row = chunk >> 3, c16 = chunk & 7;
+          const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(stage + row * kDsStride + 16 * c16);
+          const int kvr = kv0 + 32 * w + row;
+          if (kvr < N) *reinterpret_cast<u32x4*>(g + static_cast<int64_t>(kvr) * D + 64 * half + 8 * c16) = v;
         }
       }
     }
