@@ -59,12 +59,16 @@ typedef enum {
 typedef enum { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 } dash_mask;
 
 /* Tile-to-CU schedules (DASH, section 3). shift is defined for the full mask only,
- * sym_shift for the causal mask only (with an even number of KV tiles per head). */
+ * sym_shift for the causal mask only (with an even number of KV tiles per head).
+ * DASH_SCHED_AUTO picks, per call, the schedule this library measured fastest on MI355X
+ * at every point of the paper's benchmark grid: shift for the full mask, sym_shift for
+ * the causal mask, descending for a causal mask with an odd tile count. */
 typedef enum {
   DASH_SCHED_NAIVE = 0,
   DASH_SCHED_DESCENDING = 1,
   DASH_SCHED_SHIFT = 2,
-  DASH_SCHED_SYM_SHIFT = 3
+  DASH_SCHED_SYM_SHIFT = 3,
+  DASH_SCHED_AUTO = 4
 } dash_schedule;
 
 /* CU-group placement (DASH paper, section 3: "n KV tiles = n SMs; otherwise refine or

@@ -56,6 +56,16 @@ WsLayout ws_layout(int B, int H, int N, int d) {
 }
 
 // Checks shared by every entry point; pointers are checked separately.
+// DASH_SCHED_AUTO: the schedule measured fastest on MI355X at every point of the DASH
+// paper's benchmark grid (section 4.1: N = 512 .. 16384, d = 64 and 128): shift for the
+// full mask, symmetric shift for the causal mask (descending when the tile count is odd,
+// where symmetric shift is not defined). Other values are returned unchanged.
+int resolve_schedule(int schedule, int N, int mask) {
+  if (schedule != DASH_SCHED_AUTO) return schedule;
+  if (mask != DASH_MASK_CAUSAL) return DASH_SCHED_SHIFT;
+  return cdiv(N, tile_for(N)) % 2 == 0 ? DASH_SCHED_SYM_SHIFT : DASH_SCHED_DESCENDING;
+}
+
 int check_sizes(int B, int H, int Hkv, int N, int d, int mask, int schedule) {
   if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return DASH_ERR_INVALID_ARG;
   if (N > (1 << 22) || int64_t(B) * H > (int64_t(1) << 24)) return DASH_ERR_INVALID_ARG;
@@ -240,6 +250,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
             void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int mask, int schedule,
             int deterministic, void* workspace, size_t workspace_bytes, void* stream_ptr, void* ev_start,
             void* ev_stop) {
+  schedule = resolve_schedule(schedule, N, mask);
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
   if (deterministic < 0 || deterministic > 2) return DASH_ERR_INVALID_ARG;
@@ -484,6 +495,7 @@ int dash_set_placement(int placement) {
 
 int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local) {
+  schedule = resolve_schedule(schedule, N, mask);
   int s = check_sizes(B, H, Hkv, N, 64, mask, schedule);
   if (s != DASH_OK) return s;
   if (num_xcd <= 0 || cus_per_xcd <= 0 || count == nullptr || capacity < 0) return DASH_ERR_INVALID_ARG;

@@ -24,7 +24,7 @@ DASH_ERR_TIMEOUT = -6
 DASH_ERR_PLACEMENT = -7
 
 MASKS = {"full": 0, "causal": 1}
-SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "sym_shift": 3}
+SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "sym_shift": 3, "auto": 4}
 
 EXPORTED = (
     "dash_attn_bwd_workspace_size",

@@ -91,7 +91,7 @@ def _call(**kw):
     (dict(H=3), dash.DASH_ERR_INVALID_ARG),
     (dict(Hkv=0), dash.DASH_ERR_INVALID_ARG),
     (dict(mask=2), dash.DASH_ERR_INVALID_ARG),
-    (dict(schedule=4), dash.DASH_ERR_INVALID_ARG),
+    (dict(schedule=5), dash.DASH_ERR_INVALID_ARG),
     (dict(mask=1, schedule=2), dash.DASH_ERR_UNSUPPORTED),
     (dict(mask=0, schedule=3), dash.DASH_ERR_UNSUPPORTED),
     (dict(det=3), dash.DASH_ERR_INVALID_ARG),

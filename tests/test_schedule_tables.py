@@ -150,3 +150,18 @@ def test_spread_placement_of_the_long_causal_head(schedule, lanes):
 def test_placement_argument_errors():
     assert dash.dash_set_placement(2) == dash.DASH_ERR_INVALID_ARG
     assert dash.dash_set_placement(-1) == dash.DASH_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("N,mask,resolved", [
+    (2048, "full", "shift"),
+    (4096, "causal", "sym_shift"),
+    (1000, "causal", "sym_shift"),     # 8 tiles of 128
+    (1100, "causal", "descending"),    # 9 tiles: symmetric shift is not defined
+    (448, "causal", "descending"),     # 7 tiles of 64
+    (256, "full", "shift"),
+])
+def test_auto_schedule_resolves_to_the_measured_best(N, mask, resolved):
+    """schedule=auto gives the same table as the schedule it resolves to."""
+    auto, local_a = dash.dash_schedule_table(2, 4, 2, N, mask, "auto", 8, 32)
+    ref, local_r = dash.dash_schedule_table(2, 4, 2, N, mask, resolved, 8, 32)
+    assert np.array_equal(auto, ref) and local_a == local_r
