@@ -13,7 +13,9 @@
 // KV tile at a time and keeps its dK/dV in registers while it visits Q tiles; the
 // dQ partial sum of every visit goes to an fp32 accumulator in global memory,
 // added in the order the schedule table fixes (ordered reduction, section 1) or
-// with float atomics (the non-deterministic variant kept for comparison).
+// with float atomics (the non-deterministic variant kept for comparison). A separate
+// kernel casts the final sums to bf16 dQ. For the two-pass variant (the alternative
+// design of section 5) the dQ work is compiled out and dQ comes from its own pass.
 //
 // CDNA4 mapping of the main kernel
 // - One workgroup of NW waves per CU, persistent (one workgroup per CU, each reads
@@ -45,6 +47,11 @@
 //   wave), so the ordered reduction needs no workgroup barrier. The ordered variant's
 //   fp32 accumulator is kept in the MFMA accumulator's order (kDqBlock), so a wave
 //   reads and writes a block with four contiguous 1 KiB accesses at fixed offsets.
+// - The step is an explicit software pipeline (one wave per SIMD, so the wave itself
+//   must overlap MFMAs with LDS latency, softmax VALU and memory traffic); its hot path
+//   has no per-store or per-copy branches (empty buffer descriptors drop the stores
+//   that must not happen) and its bookkeeping comes from a per-step record read two
+//   steps ahead.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
