@@ -108,8 +108,10 @@ std::mutex g_mu;
 std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
+#ifdef DASH_REPLAY
 float* g_replay = nullptr;              // replay builds: dump of the ordered dQ partials
 size_t g_replay_bytes = 0;
+#endif
 
 // Measures which XCD each workgroup of a one-per-CU grid lands on. A clean
 // round-robin split (every XCD id present with the same count) gives the table
