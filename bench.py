@@ -368,6 +368,8 @@ def main():
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing (L2 and memory-side cache flushed before every call)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--kernel", default="auto", choices=["auto", "one_wave", "two_waves"],
+                    help="main backward kernel (dash_set_kernel); two_waves applies to d = 128")
     ap.add_argument("--sweep", action="store_true",
                     help="only time every schedule and the atomic variant over the paper's grid (16 384 tokens, "
                          "hidden 2048, N = 512 .. 16384, d = 64 and 128, both masks) and print one JSON line")
@@ -395,6 +397,9 @@ def main():
         return
 
     torch.cuda.set_device(0)
+    from scheduling_fa_attn_amd import dash
+    if dash.dash_set_kernel(args.kernel) != dash.DASH_OK:
+        raise SystemExit(f"dash_set_kernel({args.kernel}) failed")
     if args.sweep:
         print(json.dumps({"sweep": sweep(args.steps, args.warmup), "unit": "TFLOPS", "steps": args.steps,
                           "warmup": args.warmup, "data": "synthetic"}), flush=True)

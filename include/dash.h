@@ -85,6 +85,24 @@ typedef enum { DASH_PLACEMENT_AGGREGATE = 0, DASH_PLACEMENT_SPREAD = 1 } dash_pl
  * per placement). Returns DASH_OK, or DASH_ERR_INVALID_ARG for another value. */
 int dash_set_placement(int placement);
 
+/* Main backward kernel. The one-wave-per-SIMD kernel gives each of 4 waves per CU 32 KV
+ * rows and all five contractions. The two-waves-per-SIMD kernel gives the same 32 rows
+ * to a pair of waves that split the contractions by role (S, P, dV and dP, dS, dK; one
+ * dQ block each), so that two waves share every SIMD. The latter covers d = 128 with
+ * deterministic = 0 or 1 (dQ chains inside one XCD); other calls use the former under
+ * every setting. DASH_KERNEL_AUTO picks the one measured faster. Both give results
+ * within the same tolerance; their bits differ (dS is formed from the bf16 P in the
+ * two-waves kernel), and each is bitwise reproducible on its own. */
+typedef enum {
+  DASH_KERNEL_AUTO = 0,
+  DASH_KERNEL_ONE_WAVE_PER_SIMD = 1,
+  DASH_KERNEL_TWO_WAVES_PER_SIMD = 2
+} dash_kernel;
+
+/* Sets the main kernel used by later calls (library-wide, thread-safe). Returns DASH_OK,
+ * or DASH_ERR_INVALID_ARG for another value. */
+int dash_set_kernel(int kernel);
+
 /* Bytes of caller-provided device workspace dash_attn_bwd needs for this shape:
  * an fp32 dQ accumulator of B*H*R*d floats and two fp32 row-term arrays of B*H*R
  * floats (-D with D = rowsum(dO*O), and -LSE*log2(e)), where R is N rounded up to the

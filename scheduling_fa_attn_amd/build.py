@@ -32,10 +32,13 @@ COMMON = [
 VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
 # (source, extra flags, object name)
 MAIN_FLAGS = {(64, 4): VGPR_FORM, (128, 4): VGPR_FORM, (64, 2): [], (128, 2): []}
+# The two-waves-per-SIMD kernel (d = 128): MFMA results in VGPRs for the same reason.
+PAIR_FLAGS = VGPR_FORM
 UNITS = [
     ("bwd_main.hip", [f"-DDASH_MAIN_D={d}", f"-DDASH_MAIN_NW={nw}"] + fl, f"bwd_main_d{d}_nw{nw}.o")
     for (d, nw), fl in MAIN_FLAGS.items()
 ] + [
+    ("bwd_pair.hip", PAIR_FLAGS, "bwd_pair.o"),
     ("aux_kernels.hip", [], "aux_kernels.o"),
     ("fwd_main.hip", [], "fwd_main.o"),
     ("dq_pass.hip", [], "dq_pass.o"),

@@ -363,7 +363,7 @@ bwd_main_kernel(BwdParams p) {
       pd.go = !failed;
       pd.acc_rs = DET ? make_rsrc(pd.acc_blk, pd.go ? 2 * DB * kBlkBytes : 0)
                       : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, pd.go ? 64 * D * 4 : 0);
-      pd.sem = p.sem + bh * p.sem_stride + (q0s / BQ) * 4 + w;
+      pd.sem = p.sem + bh * p.sem_stride + (q0s / BQ) * kSemPerStep + w;
 #ifdef DASH_REPLAY
       // Dump layout: [b*H + h][64-row step][dQ block (2 DB)][rank][kDqBlock floats].
       pd.dump = p.replay ? p.replay + (((bh * (p.row_stride / BQ) + q0s / BQ) * (2 * DB)) * p.replay_ranks + pd.rank) *

@@ -38,10 +38,10 @@ struct WsLayout {
 
 WsLayout ws_layout(int B, int H, int N, int d) {
   WsLayout L;
-  // One semaphore per 64-row Q step and wave (4 at most), for every step of the
-  // ceil(N / tile) tiles of a head (the last tile's second step may lie past N).
+  // One semaphore per 64-row Q step and wave (dash::kSemPerStep at most), for every
+  // step of the ceil(N / tile) tiles of a head (the last tile's second step may lie past N).
   const int tile = tile_for(N);
-  L.sem_stride = static_cast<int>(cdiv(cdiv(N, tile) * (tile / 64) * 4, 32) * 32);
+  L.sem_stride = static_cast<int>(cdiv(cdiv(N, tile) * (tile / 64) * dash::kSemPerStep, 32) * 32);
   L.row_stride = static_cast<int>(cdiv(N, tile) * tile);
   const size_t dq_bytes = align256(size_t(B) * H * L.row_stride * d * sizeof(float));
   const size_t row_bytes = align256(size_t(B) * H * L.row_stride * sizeof(float));
@@ -108,6 +108,9 @@ std::mutex g_mu;
 std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
+int g_kernel = DASH_KERNEL_AUTO;  // main-kernel choice of later calls
+// What DASH_KERNEL_AUTO resolves to where the two-waves-per-SIMD kernel applies.
+constexpr bool kPairAuto = false;
 #ifdef DASH_REPLAY
 float* g_replay = nullptr;              // replay builds: dump of the ordered dQ partials
 size_t g_replay_bytes = 0;
@@ -348,7 +351,19 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   }
 #endif
   if (ev_start && hipEventRecord(static_cast<hipEvent_t>(ev_start), stream) != hipSuccess) return DASH_ERR_HIP;
-  hipError_t e = dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream);
+  // The two-waves-per-SIMD kernel covers d = 128 with 128-row tiles, the ordered
+  // reduction inside one XCD and the atomic variant; everything else (and the profiling
+  // build's phase counters) runs on the one-wave-per-SIMD kernel.
+  int kernel;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    kernel = g_kernel;
+  }
+  const bool pair_ok = d == 128 && tab->tile == 128 && deterministic != 2 && (deterministic == 0 || bp.xcd_local ||
+                       st->num_xcd == 1) && bp.prof == nullptr;
+  const bool use_pair = pair_ok && (kernel == DASH_KERNEL_TWO_WAVES_PER_SIMD || (kernel == DASH_KERNEL_AUTO && kPairAuto));
+  hipError_t e = use_pair ? dash::launch_pair_d128(bp, tab->workers, stream)
+                          : dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream);
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
   if (e != hipSuccess) return DASH_ERR_HIP;
   if (ev_stop && hipEventRecord(static_cast<hipEvent_t>(ev_stop), stream) != hipSuccess) return DASH_ERR_HIP;
@@ -487,6 +502,14 @@ int dash_replay_attach(void* buf, size_t bytes) {
   return DASH_OK;
 }
 #endif
+
+int dash_set_kernel(int kernel) {
+  if (kernel != DASH_KERNEL_AUTO && kernel != DASH_KERNEL_ONE_WAVE_PER_SIMD && kernel != DASH_KERNEL_TWO_WAVES_PER_SIMD)
+    return DASH_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_kernel = kernel;
+  return DASH_OK;
+}
 
 int dash_set_placement(int placement) {
   if (placement != DASH_PLACEMENT_AGGREGATE && placement != DASH_PLACEMENT_SPREAD) return DASH_ERR_INVALID_ARG;

@@ -45,7 +45,7 @@ struct BwdParams {
   const int4* tasks;
   const int4* steps;   // per 64-row step in task order: {b * H + h, first Q row, rank, last}; 2 zero records follow
   int B, H, Hkv, N;
-  int sem_stride;      // semaphores per (b, h): 4 per 64-row Q step (one per wave), padded
+  int sem_stride;      // semaphores per (b, h): kSemPerStep per 64-row Q step, padded
   int row_stride;      // rows per (b, h) of nlse2, neg_delta and dqacc: N rounded up to the tile
   float scale;         // softmax scale s
   float scale_log2;    // s * log2(e)
@@ -102,6 +102,10 @@ struct DqParams {
 //   of a wave hit whole cache lines.
 constexpr int kDqBlock = 32 * 32;
 
+// Ordering semaphores per 64-row Q step of a (b, h): one per wave of the largest
+// workgroup (each wave reduces its own dQ blocks and passes its own turn).
+constexpr int kSemPerStep = 8;
+
 // Phase counters of a profiling build, per wave: [grid][NW][kProfSlots] of 64-bit cycles
 // (s_memtime) or counts.
 constexpr int kProfSlots = 20;
@@ -133,6 +137,9 @@ hipError_t launch_main_d64_nw2(const BwdParams& prm, int grid, hipStream_t strea
 hipError_t launch_main_d64_nw4(const BwdParams& prm, int grid, hipStream_t stream);
 hipError_t launch_main_d128_nw2(const BwdParams& prm, int grid, hipStream_t stream);
 hipError_t launch_main_d128_nw4(const BwdParams& prm, int grid, hipStream_t stream);
+// Two-waves-per-SIMD main kernel (d = 128, 128-row tiles, ordered XCD-local or atomic
+// reduction; 8 waves per workgroup).
+hipError_t launch_pair_d128(const BwdParams& prm, int grid, hipStream_t stream);
 inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hipStream_t stream) {
   if (d == 64 && nw == 2) return launch_main_d64_nw2(prm, grid, stream);
   if (d == 64 && nw == 4) return launch_main_d64_nw4(prm, grid, stream);

@@ -35,6 +35,7 @@ EXPORTED = (
     "dash_tile_size",
     "dash_schedule_table",
     "dash_set_placement",
+    "dash_set_kernel",
     "dash_attn_fwd",
 )
 
@@ -82,6 +83,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_schedule_table.restype = i
     lib.dash_set_placement.argtypes = [i]
     lib.dash_set_placement.restype = i
+    lib.dash_set_kernel.argtypes = [i]
+    lib.dash_set_kernel.restype = i
     lib.dash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.dash_attn_fwd.restype = i
     if hasattr(lib, "dash_profile_attach"):
@@ -116,6 +119,16 @@ def dash_set_placement(placement, lib=None) -> int:
     """Placement of CU groups larger than one XCD for later calls: "aggregate" (default)
     or "spread" (the paper's n-SM layout; chains cross XCDs)."""
     return int((lib or load()).dash_set_placement(PLACEMENTS.get(placement, placement)))
+
+
+KERNELS = {"auto": 0, "one_wave": 1, "two_waves": 2}
+
+
+def dash_set_kernel(kernel, lib=None) -> int:
+    """Main backward kernel of later calls: "auto" (default), "one_wave" (one wave per
+    SIMD, every configuration) or "two_waves" (two waves per SIMD, d = 128 with the
+    ordered or atomic reduction; other calls keep the one-wave kernel)."""
+    return int((lib or load()).dash_set_kernel(KERNELS.get(kernel, kernel)))
 
 
 def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):

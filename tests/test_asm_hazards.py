@@ -205,6 +205,43 @@ def test_inline_mfma_wait_states(kernel_asm, d, nw, det, cross, nodq, flavour):
     assert not hazards, "\n".join(hazards[:20])
 
 
+def _compile_pair_asm(flavour, out):
+    cmd = [dash_build.HIPCC] + dash_build.COMMON + dash_build.PAIR_FLAGS + FLAVOURS[flavour] + \
+        ["--cuda-device-only", "-S", "-x", "hip", os.path.join(dash_build.HERE, "csrc", "bwd_pair.hip"), "-o", out]
+    return subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)
+
+
+@pytest.fixture(scope="module")
+def pair_asm(tmp_path_factory):
+    if not os.path.exists(dash_build.HIPCC):
+        pytest.skip("hipcc not available")
+    tmp = tmp_path_factory.mktemp("pair_asm")
+    procs = {fl: (str(tmp / f"bwd_pair_{fl}.s"), None) for fl in FLAVOURS}
+    procs = {fl: (out, _compile_pair_asm(fl, out)) for fl, (out, _) in procs.items()}
+    texts = {}
+    for fl, (out, proc) in procs.items():
+        _, err = proc.communicate(timeout=600)
+        assert proc.returncode == 0, err
+        with open(out) as f:
+            texts[fl] = f.read()
+    return texts
+
+
+# The two-waves-per-SIMD kernel (d = 128): ordered and atomic instantiations, every flavour.
+PAIR_VARIANTS = [(det, fl) for det in (1, 0) for fl in FLAVOURS]
+
+
+@pytest.mark.parametrize("det,flavour", PAIR_VARIANTS, ids=[f"pair-d128-det{v[0]}-{v[1]}" for v in PAIR_VARIANTS])
+def test_pair_kernel_inline_mfma_wait_states(pair_asm, det, flavour):
+    symbol = f"_ZN4dash15bwd_pair_kernelILi128ELb{det}EEEvNS_9BwdParamsE"
+    insts, labels = parse_kernel(pair_asm[flavour], symbol)
+    # Both roles' bodies: 16 + 16 + 8 per step and 8 for an item's last dQ block, each.
+    n_mfma = sum(1 for i in insts if i.mfma and i.asm)
+    assert n_mfma >= 96, n_mfma
+    hazards = find_hazards(insts, labels)
+    assert not hazards, "\n".join(hazards[:20])
+
+
 def _synthetic(lines):
     text = "k:\n" + "\n".join(lines) + "\n.Lfunc_end0:\n"
     return parse_kernel(text, "k")
