@@ -28,17 +28,20 @@
 // dQ contraction needs it anyway.
 //
 // Step of 64 Q rows (two barriers):
-//   A: S MFMAs; softmax; P -> LDS                          | barrier X |
-//      dV MFMAs with the previous step's dQ block (8 MFMAs), its stores, its turn passed
-//      on; this step's turn polled and running sum loaded   | barrier Y |
-//   B: next step's global->LDS copies; dP MFMAs with the previous step's dQ block; its
-//      stores                                               | barrier X |
-//      P from LDS; dS -> registers and dS^T -> LDS; dK MFMAs; the previous step's turn
-//      passed on; this step's turn polled and running sum loaded | barrier Y |
-// Only B waves issue global->LDS copies: the compiler does not see those (inline
-// assembly), so a wave that has copies in flight must wait for its running-sum loads
-// before issuing them (the vector-memory counter is in order); A waves load their
-// running sums a whole phase before they use them and never wait for copies.
+//   A: S MFMAs of Q block 0, then of block 1 with block 0's softmax and the next step's
+//      Q-tile copies between them; block 1's softmax; P -> LDS      | barrier X |
+//      dV MFMAs with the previous step's dQ block (8 MFMAs) in their second half, its
+//      stores, its turn passed on; this step's turn polled and running sum loaded
+//                                                                   | barrier Y |
+//   B: dP MFMAs with the next step's dO-tile copies and the previous step's dQ block;
+//      its stores                                                   | barrier X |
+//      P from LDS; dS of block 0 (registers, and transposed to LDS); dK MFMAs of
+//      block 0 with block 1's dS between them; dK MFMAs of block 1; the previous step's
+//      turn passed on; this step's turn polled and running sum loaded | barrier Y |
+// A waves copy the next step's Q tile (after their S MFMAs), B waves its dO tile (during
+// their dP MFMAs). The compiler does not see these copies (inline assembly), so a wave
+// waits for its running-sum loads before issuing them (the vector-memory counter is in
+// order) and for the copies themselves before the step-end barrier.
 // Operand layouts, the padded and row-permuted LDS tiles, the fp32 accumulator's block
 // layout, the step records and the turn protocol are those of bwd_main.hip.
 #include <hip/hip_runtime.h>
@@ -47,6 +50,9 @@
 #include "device_common.h"
 #include "kernels.h"
 
+// Depth of the LDS operand rings (reads issued DASH_PAIR_RING - 1 MFMAs ahead). Depths
+// 3 and 4 measured no faster than 2 (two waves per SIMD cover the LDS latency that a
+// deeper ring would) and spill a few registers.
 #ifndef DASH_PAIR_RING
 #define DASH_PAIR_RING 2
 #endif
@@ -97,6 +103,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
   const int hi = lane >> 5;
   const int L16 = lane & 15;
   const int nb = (lane >> 4) & 1;
+  PROF_DECL
   const int H = p.H, Hkv = p.Hkv, N = p.N;
   bool failed = false;  // this wave gave up waiting (error reported); it keeps going without reducing
   const CONST_AS int* worker_begin = (const CONST_AS int*)p.worker_begin;
@@ -212,6 +219,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       kT[kk] = to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST)));
     }
     __syncthreads();
+    PROF_MARK(kProfPro);
 
 #ifdef DASH_REPLAY
     constexpr bool kZeroStart = true;
@@ -363,6 +371,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     floatx16 ld = {};
     bool loaded = false;
     for (int s = 0; s < n_steps; ++s) {
+      PROF_COUNT(kProfSteps);
       const int buf = (par0 + s) & 1;
       const int q0 = rec_cur.y;
       const int j = q0 / BC;
@@ -386,11 +395,70 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #define SLOT() __builtin_amdgcn_sched_barrier(0)
       // Operand rings: LDS reads issued kR - 1 slots ahead of their MFMAs.
       constexpr int kR = DASH_PAIR_RING;
+      // The next step's tiles, into buffer buf ^ 1 (free since the last barrier): A waves
+      // copy the Q tile and -LSE*log2e, B waves the dO tile and -D. Copy op o < kPW is
+      // block pr + 4 o of the tile: LDS slot 64 blk + lane holds chunk c of row r (pad
+      // slots re-read chunk 0); rows past N repeat row N - 1. The lane's offset is
+      // recomputed at every step rather than kept in a register. At an item's last step
+      // the next record is the next item's first step; at the worker's last step it is
+      // another worker's (or a zero) record, copied all the same: nothing reads it.
+      constexpr int kPW = TileCopy<D, BQ, 4>::PER_WAVE;
+      constexpr int kQNI = TileCopy<D, BQ, 4>::NI;
+      constexpr int kCopyOps = kPW + 1;
+      const int q0_n = rec_nxt.y;
+      const int64_t bh_n = rec_nxt.x;
+      auto copy_op = [&](int o, int lane_op) __attribute__((always_inline)) {
+        if (o < kPW) {
+          const int blk = pr + 4 * o;
+          if (o + 1 < kPW || blk < kQNI) {
+            constexpr int SPR = TileGeom<D>::CPR + 1;
+            const int slot = blk * 64 + lane_op;
+            const int r = slot / SPR;
+            int c = slot - r * SPR;
+            c = c < TileGeom<D>::CPR ? c : 0;
+            int row = q0_n + r;
+            row = row < N - 1 ? row : N - 1;
+            dma16((roleA ? p.q : p.dO) + bh_n * N * D, static_cast<unsigned>(row * (2 * D) + 16 * c),
+                  smem + (roleA ? C::OFF_Q : C::OFF_DO) + (buf ^ 1) * C::QT + blk * 1024);
+          }
+        } else if (pr == 0) {
+          dma4((roleA ? p.nlse2 : p.neg_delta) + bh_n * p.row_stride + q0_n, row_lane,
+               smem + (roleA ? C::OFF_NL : C::OFF_DL) + (buf ^ 1) * 256);
+        }
+      };
       Pending pd_n;
       int sem_now = 0;
       if constexpr (roleA) {
         // ---- S = Q K^T (both 32-row blocks), operands two slots ahead.
         floatx16 S0, S1;
+        // Causal diagonal: S = -inf (P = 0) where the key comes after the query. Row of
+        // element r = 4 t + e of block qb: pi(m) = 32 qb + 16 (t / 2) + 2 (t % 2) + 4 e + hi.
+        const bool diag = p.causal && j == kv_tile;
+        const int mask_thr = kvcol - q0 - hi;
+        auto mask_block = [&](int qb, floatx16& S) __attribute__((always_inline)) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = r >> 2, e = r & 3;
+            if (32 * qb + 16 * (t >> 1) + 2 * (t & 1) + 4 * e < mask_thr) S[r] = -__builtin_inff();
+          }
+        };
+        // P = exp2(s log2(e) S - LSE log2(e)) of elements r, r + 1 of block qb, as a bf16 pair.
+        u32x4 P[2][2];
+        floatx4 nl[2][4];
+        auto softmax2 = [&](int qb, int r, const floatx16& S) __attribute__((always_inline)) {
+          const floatx4& n4 = nl[qb][r >> 2];
+          const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, n4[r & 3]));
+          const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], p.scale_log2, n4[(r & 3) + 1]));
+          P[qb][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
+        };
+        auto load_nl = [&](int qb) __attribute__((always_inline)) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            nl[qb][t] = *reinterpret_cast<const LDS_AS floatx4*>(sNL + (qb * 32 + 8 * t + 4 * hi) * 4);
+        };
+        // S of block 0, then S of block 1 with block 0's softmax and the copies between its
+        // MFMAs (two elements per slot), then block 1's softmax.
+        int lane_op = 0;
         bf16x8 aq[kR];
 #pragma unroll
         for (int i = 0; i < kR - 1; ++i) aq[i] = lds_ld16(sQ, sdp_off(i / DK, i % DK));
@@ -398,135 +466,111 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #pragma unroll
         for (int i = 0; i < 2 * DK; ++i) {
           if (i + kR - 1 < 2 * DK) aq[(i + kR - 1) % kR] = lds_ld16(sQ, sdp_off((i + kR - 1) / DK, (i + kR - 1) % DK));
+          if (i == 0) load_nl(0);
+          if (i == DK / 2) load_nl(1);
           floatx16& S = i < DK ? S0 : S1;
           if (i % DK == 0)
             mfma32_vab_zero(S, aq[i % kR], kv[0]);
           else
             mfma32_vab(S, aq[i % kR], kv[i % DK]);
+          if (i == DK - 1) {
+            mfma_result_wait(S0);
+            if (diag) mask_block(0, S0);
+          }
+          if (i >= DK) {
+#pragma unroll
+            for (int r = 16 * (i - DK) / DK; r < 16 * (i - DK + 1) / DK; r += 2) softmax2(0, r, S0);
+            // The running sums loaded at the end of the last step have landed before the
+            // first copy is issued (the copies are invisible to the compiler's counters).
+            if (i == DK) {
+              asm volatile("" : "+v"(ld));
+              lane_op = opaque_lane();
+            }
+#pragma unroll
+            for (int o = (i - DK) * kCopyOps / DK; o < (i - DK + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
+          }
           SLOT();
         }
-        // -LSE*log2(e) of the row groups, read while the MFMAs finish.
-        floatx4 nl[2][4];
+        PROF_MARK(kProfSd0);
+        // P to the pair's exchange area: block 0 now, block 1 after its softmax.
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int h = 0; h < 2; ++h) *reinterpret_cast<LDS_AS u32x4*>(sPX + 1024 * h) = P[0][h];
+        mfma_result_wait(S1);
+        if (diag) mask_block(1, S1);
 #pragma unroll
-          for (int t = 0; t < 4; ++t)
-            nl[qb][t] = *reinterpret_cast<const LDS_AS floatx4*>(sNL + (qb * 32 + 8 * t + 4 * hi) * 4);
-        mfma_result_wait(S0, S1);
-        if (p.causal && j == kv_tile) {
-          // Causal diagonal: S = -inf (P = 0) where the key comes after the query. Row of
-          // element r = 4 t + e of block qb: pi(m) = 32 qb + 16 (t / 2) + 2 (t % 2) + 4 e + hi.
-          const int mask_thr = kvcol - q0 - hi;
+        for (int r = 0; r < 16; r += 2) softmax2(1, r, S1);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int t = r >> 2, e = r & 3;
-            if (16 * (t >> 1) + 2 * (t & 1) + 4 * e < mask_thr) S0[r] = -__builtin_inff();
-            if (32 + 16 * (t >> 1) + 2 * (t & 1) + 4 * e < mask_thr) S1[r] = -__builtin_inff();
-          }
-        }
-        // P = exp2(s log2(e) S - LSE log2(e)), bf16 pairs; to the pair's exchange area.
-        u32x4 P[2][2];
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const floatx16& S = qb ? S1 : S0;
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const floatx4& n4 = nl[qb][r >> 2];
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], p.scale_log2, n4[r & 3]));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], p.scale_log2, n4[(r & 3) + 1]));
-            P[qb][r >> 3][(r & 7) >> 1] = pack_bf16(p0, p1);
-          }
-        }
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int h = 0; h < 2; ++h) *reinterpret_cast<LDS_AS u32x4*>(sPX + 1024 * (2 * qb + h)) = P[qb][h];
+        for (int h = 0; h < 2; ++h) *reinterpret_cast<LDS_AS u32x4*>(sPX + 1024 * (2 + h)) = P[1][h];
+        PROF_MARK(kProfMid0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();  // X: P of every pair in LDS
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        PROF_MARK(kProfBarrierX);
         // ---- dV += P^T dO, with the previous step's dQ block in the second half.
         if (have_prev && !loaded) {
           reduce_wait(pd);
           reduce_load(pd, ld);
+          PROF_COUNT(kProfLate);
         }
+        PROF_MARK(kProfWait);
 #ifdef DASH_REPLAY
         run = ld;
 #endif
         pd_n = reduce_prepare(rec_cur);
         sem_now = reduce_poll(pd_n);
-        bf16x8 bo[kR], aqd[2];
+        PROF_MARK(kProfDq);
+        bf16x8 bo[kR], aqd[kR];
 #pragma unroll
         for (int i = 0; i < kR - 1; ++i) bo[i] = bt_load(sdO, i);
         SLOT();
 #pragma unroll
         for (int jj = 0; jj < 2 * NIT; ++jj) {
           if (jj + kR - 1 < 2 * NIT) bo[(jj + kR - 1) % kR] = bt_load(sdO, jj + kR - 1);
-          if (jj == 2 * NIT - KK - 1) aqd[0] = dq_opnd(sdSprev, 0);
+          const int kk = jj - (2 * NIT - KK);
+          if (kk + kR - 1 >= 0 && kk + kR - 1 < KK) aqd[(kk + kR - 1) % kR] = dq_opnd(sdSprev, kk + kR - 1);
           const int qb = jj / NIT, itr = jj % NIT;
           mfma32_acc(acc[itr % DB], as_bf16x8(P[qb][itr / DB]), bo[jj % kR]);
-          const int kk = jj - (2 * NIT - KK);
-          if (kk >= 0) {
-            if (kk + 1 < KK) aqd[(kk + 1) & 1] = dq_opnd(sdSprev, kk + 1);
-            dq_mma(ld, kk, aqd[kk & 1], kT[kk]);
-          }
+          if (kk >= 0) dq_mma(ld, kk, aqd[kk % kR], kT[kk]);
           SLOT();
         }
+        PROF_MARK(kProfDv0);
         mfma_result_wait(ld);
         reduce_store(pd, ld);
+        PROF_MARK(kProfLoads);
         if (DET) {
+          // Stores (and this step's copies) acknowledged: the previous step's turn is
+          // passed on.
           wait_mem_done();
           if (have_prev) reduce_signal(pd);
+        } else {
+          // The copies have landed before the step-end barrier; the 16 float atomics
+          // issued after them stay in flight.
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
+          __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+          __atomic_signal_fence(__ATOMIC_SEQ_CST);
         }
+        PROF_MARK(kProfReduce);
         const int sem_seen = __builtin_amdgcn_readfirstlane(sem_now);
         loaded = !reduce_needs_turn(pd_n) || sem_seen == pd_n.rank;
         if (loaded) reduce_load(pd_n, ld);
+        PROF_MARK(kProfBody);
       } else {
         // ---- The next step's copies; dP - D = dO V^T - D (the accumulation starts from
         // -D); the previous step's dQ block in the second half; its stores.
         if (have_prev && !loaded) {
           reduce_wait(pd);
           reduce_load(pd, ld);
+          PROF_COUNT(kProfLate);
         }
+        PROF_MARK(kProfWait);
         // The running sums have landed before the first copy is issued.
         asm volatile("" : "+v"(ld));
+        PROF_MARK(kProfLoads);
 #ifdef DASH_REPLAY
         run = ld;
 #endif
-        const int q0_n = rec_nxt.y;
-        const int64_t bh_n = rec_nxt.x;
-        const bf16* q_n = p.q + bh_n * N * D;
-        const bf16* do_n = p.dO + bh_n * N * D;
-        LDS_AS char* const sQn = smem + C::OFF_Q + (buf ^ 1) * C::QT;
-        LDS_AS char* const sdOn = smem + C::OFF_DO + (buf ^ 1) * C::QT;
-        constexpr int kPW = TileCopy<D, BQ, 4>::PER_WAVE;
-        constexpr int kQNI = TileCopy<D, BQ, 4>::NI;
         const int lane_op = opaque_lane();
-        constexpr int kCopyOps = 2 * kPW + 1;
-        auto copy_op = [&](int o) __attribute__((always_inline)) {
-          if (o < 2 * kPW) {
-            // Block m of this wave's share of the Q (or dO) tile: LDS slot 64 blk + lane
-            // holds chunk c of row r (pad slots re-read chunk 0); rows past N repeat row
-            // N - 1. The lane's offset is recomputed here rather than kept in a register.
-            const int m = o < kPW ? o : o - kPW;
-            const int blk = pr + 4 * m;
-            if (m + 1 < kPW || blk < kQNI) {
-              constexpr int SPR = TileGeom<D>::CPR + 1;
-              const int slot = blk * 64 + lane_op;
-              const int r = slot / SPR;
-              int c = slot - r * SPR;
-              c = c < TileGeom<D>::CPR ? c : 0;
-              int row = q0_n + r;
-              row = row < N - 1 ? row : N - 1;
-              dma16(o < kPW ? q_n : do_n, static_cast<unsigned>(row * (2 * D) + 16 * c),
-                    (o < kPW ? sQn : sdOn) + blk * 1024);
-            }
-          } else {
-            const float* row_src = (pr & 1) ? p.neg_delta : p.nlse2;
-            dma4(row_src + bh_n * p.row_stride + q0_n, row_lane,
-                 smem + ((pr & 1) ? C::OFF_DL : C::OFF_NL) + (buf ^ 1) * 256);
-          }
-        };
         floatx16 dP0, dP1;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
@@ -538,31 +582,33 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
             for (int e = 0; e < 4; ++e) x[4 * t + e] = d4[e];
           }
         }
-        bf16x8 ad[kR], aqd[2];
+        bf16x8 ad[kR], aqd[kR];
 #pragma unroll
         for (int i = 0; i < kR - 1; ++i) ad[i] = lds_ld16(sdO, sdp_off(i / DK, i % DK));
         SLOT();
 #pragma unroll
         for (int i = 0; i < 2 * DK; ++i) {
           if (i + kR - 1 < 2 * DK) ad[(i + kR - 1) % kR] = lds_ld16(sdO, sdp_off((i + kR - 1) / DK, (i + kR - 1) % DK));
-          if (i == 2 * DK - KK - 1) aqd[0] = dq_opnd(sdSprev, 0);
-          mfma32_vab(i < DK ? dP0 : dP1, ad[i % kR], kv[i % DK]);
           const int kk = i - (2 * DK - KK);
-          if (kk >= 0) {
-            if (kk + 1 < KK) aqd[(kk + 1) & 1] = dq_opnd(sdSprev, kk + 1);
-            dq_mma(ld, kk, aqd[kk & 1], kT[kk]);
-          }
+          if (kk + kR - 1 >= 0 && kk + kR - 1 < KK) aqd[(kk + kR - 1) % kR] = dq_opnd(sdSprev, kk + kR - 1);
+          mfma32_vab(i < DK ? dP0 : dP1, ad[i % kR], kv[i % DK]);
+          if (kk >= 0) dq_mma(ld, kk, aqd[kk % kR], kT[kk]);
+          if (i < DK) {
 #pragma unroll
-          for (int o = i * kCopyOps / (2 * DK); o < (i + 1) * kCopyOps / (2 * DK); ++o) copy_op(o);
+            for (int o = i * kCopyOps / DK; o < (i + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
+          }
           SLOT();
         }
+        PROF_MARK(kProfSd0);
         mfma_result_wait(dP0, dP1);
         mfma_result_wait(ld);
         reduce_store(pd, ld);
+        PROF_MARK(kProfMid0);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();  // X: P of every pair in LDS
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        PROF_MARK(kProfBarrierX);
         // ---- dS = P (dP - D): bf16 pairs in registers, dS^T to LDS; dK += dS^T Q.
         pd_n = reduce_prepare(rec_cur);
         sem_now = reduce_poll(pd_n);
@@ -571,24 +617,27 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
           for (int h = 0; h < 2; ++h) Pw[qb][h] = *reinterpret_cast<const LDS_AS u32x4*>(sPX + 1024 * (2 * qb + h));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
+        // dS of elements r, r + 1 of block qb; after the last pair of a row group t, the
+        // group's dS^T goes to LDS.
+        auto ds2 = [&](int qb, int r) __attribute__((always_inline)) {
           const floatx16& dPx = qb ? dP1 : dP0;
-#pragma unroll
-          for (int r = 0; r < 16; r += 2) {
-            const unsigned u = Pw[qb][r >> 3][(r & 7) >> 1];
-            const float p0 = __builtin_bit_cast(float, u << 16);
-            const float p1 = __builtin_bit_cast(float, u & 0xffff0000u);
-            dS[qb][r >> 3][(r & 7) >> 1] = pack_bf16(p0 * dPx[r], p1 * dPx[r + 1]);
-          }
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
+          const unsigned u = Pw[qb][r >> 3][(r & 7) >> 1];
+          const float p0 = __builtin_bit_cast(float, u << 16);
+          const float p1 = __builtin_bit_cast(float, u & 0xffff0000u);
+          dS[qb][r >> 3][(r & 7) >> 1] = pack_bf16(p0 * dPx[r], p1 * dPx[r + 1]);
+          if ((r & 3) == 2) {
+            const int t = r >> 2;
             u32x2 v2;
             v2[0] = dS[qb][t >> 1][2 * (t & 1)];
             v2[1] = dS[qb][t >> 1][2 * (t & 1) + 1];
             *reinterpret_cast<LDS_AS u32x2*>(sdS + ds_wr_lane + 64 * qb + 16 * t) = v2;
           }
-        }
+        };
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) ds2(0, r);
+        PROF_MARK(kProfSd1);
+        // dK of block 0 with block 1's dS between its MFMAs (two elements per slot), then
+        // dK of block 1.
         bf16x8 bq[kR];
 #pragma unroll
         for (int i = 0; i < kR - 1; ++i) bq[i] = bt_load(sQ, i);
@@ -598,7 +647,12 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
           if (jj + kR - 1 < 2 * NIT) bq[(jj + kR - 1) % kR] = bt_load(sQ, jj + kR - 1);
           const int qb = jj / NIT, itr = jj % NIT;
           mfma32_acc(acc[itr % DB], as_bf16x8(dS[qb][itr / DB]), bq[jj % kR]);
+          if (jj < NIT) {
+#pragma unroll
+            for (int r = 16 * jj / NIT; r < 16 * (jj + 1) / NIT; r += 2) ds2(1, r);
+          }
           if (jj == NIT) {
+            PROF_MARK(kProfDv0);
             // Stores and copies acknowledged: the previous step's turn is passed on. (The
             // atomic variant waits for the copies only; its atomics stay in flight.)
             if (DET) {
@@ -609,6 +663,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
               __atomic_signal_fence(__ATOMIC_SEQ_CST);
             }
             if (have_prev) reduce_signal(pd);
+            PROF_MARK(kProfReduce);
           }
           if (jj == NIT + NIT / 2) {
             const int sem_seen = __builtin_amdgcn_readfirstlane(sem_now);
@@ -620,11 +675,13 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       }
 #undef SLOT
       pd = pd_n;
+      if constexpr (!roleA) PROF_MARK(kProfBody);
       // Y: dS^T of every pair is visible, the copies have landed, P has been read.
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
       __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
       __builtin_amdgcn_s_barrier();
       __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      PROF_MARK(kProfBarrier);
       rec_cur = rec_nxt;
       rec_nxt = rec_nn;
       mfma_settle(acc);
@@ -652,6 +709,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       reduce_store(pd, ld);
       wait_mem_done();
       reduce_signal(pd);
+      PROF_MARK(kProfFlush);
     }
     par0 = (par0 + n_steps) & 1;
     if (has_next && !roleA) issue_kv(it + 1, par0);
@@ -683,7 +741,9 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         if (kvr < N) *reinterpret_cast<u32x4*>(g + static_cast<int64_t>(kvr) * D + 64 * half + 8 * c16) = v;
       }
     }
+    PROF_MARK(kProfEpi);
   }
+  PROF_STORE(p, w, 8);
 }
 
 // DET: ordered reduction inside one XCD's L2 (every dQ tile's contributors share an

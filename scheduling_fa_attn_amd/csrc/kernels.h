@@ -116,6 +116,7 @@ enum ProfSlot {
   kProfWait = 3,     // waiting for the dQ turn (semaphore)
   kProfReduce = 4,   // waiting for this wave's copies at the step's end
   kProfItem = 5,     // the step's first LDS reads issued and its running sums landed
+  kProfBarrierX = 5, // (two-waves kernel) the mid-step barrier
   kProfSteps = 6,    // number of steps
   kProfTotal = 7,    // whole kernel
   kProfSd0 = 8,      // S/dP of the first block (with dQ MFMAs), from the accumulator loads on
