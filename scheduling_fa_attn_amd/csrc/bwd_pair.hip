@@ -520,23 +520,29 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         pd_n = reduce_prepare(rec_cur);
         sem_now = reduce_poll(pd_n);
         PROF_MARK(kProfDq);
+        // The dQ MFMAs run in the first half, so that their stores are acknowledged
+        // under the second half's dV MFMAs.
         bf16x8 bo[kR], aqd[kR];
 #pragma unroll
-        for (int i = 0; i < kR - 1; ++i) bo[i] = bt_load(sdO, i);
+        for (int i = 0; i < kR - 1; ++i) {
+          bo[i] = bt_load(sdO, i);
+          aqd[i] = dq_opnd(sdSprev, i);
+        }
         SLOT();
 #pragma unroll
         for (int jj = 0; jj < 2 * NIT; ++jj) {
           if (jj + kR - 1 < 2 * NIT) bo[(jj + kR - 1) % kR] = bt_load(sdO, jj + kR - 1);
-          const int kk = jj - (2 * NIT - KK);
-          if (kk + kR - 1 >= 0 && kk + kR - 1 < KK) aqd[(kk + kR - 1) % kR] = dq_opnd(sdSprev, kk + kR - 1);
+          if (jj + kR - 1 < KK) aqd[(jj + kR - 1) % kR] = dq_opnd(sdSprev, jj + kR - 1);
           const int qb = jj / NIT, itr = jj % NIT;
           mfma32_acc(acc[itr % DB], as_bf16x8(P[qb][itr / DB]), bo[jj % kR]);
-          if (kk >= 0) dq_mma(ld, kk, aqd[kk % kR], kT[kk]);
+          if (jj < KK) dq_mma(ld, jj, aqd[jj % kR], kT[jj]);
+          if (jj == KK) {
+            mfma_result_wait(ld);
+            reduce_store(pd, ld);
+          }
           SLOT();
         }
         PROF_MARK(kProfDv0);
-        mfma_result_wait(ld);
-        reduce_store(pd, ld);
         PROF_MARK(kProfLoads);
         if (DET) {
           // Stores (and this step's copies) acknowledged: the previous step's turn is
