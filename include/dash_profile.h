@@ -33,7 +33,7 @@ extern "C" {
  *  17 the item's last reduction                 18 item epilogue (dK, dV stores)
  * The two-waves-per-SIMD kernel uses the same slots for its roles' phases (A: S, P,
  * dV; B: dP, dS, dK): 8 S (A) or dP + dQ MFMAs + copies (B); 9 softmax and P stores (A)
- * or dQ stores (B); 5 the mid-step barrier; 3 a late turn wait; 2 turn bookkeeping (A);
+ * or dQ stores (B); 5 the mid-step handoff of P (A: flag set, B: flag awaited); 3 a late turn wait; 2 turn bookkeeping (A);
  * 10 P read and dS (B); 12 dV + dQ MFMAs (A) or the first dK MFMAs (B); 13 dQ stores
  * (A) or the running sums landing (B); 4 acknowledgement and turn passed on; 0 the
  * rest of the step; 1 the step-end barrier; 6, 7, 14, 16-18 as above.

@@ -27,17 +27,21 @@
 // the same S/dP accumulator elements as lane l of A); dS goes to LDS transposed, as the
 // dQ contraction needs it anyway.
 //
-// Step of 64 Q rows (two barriers):
+// Step of 64 Q rows (a pair-local handoff X and a workgroup barrier Y):
 //   A: S MFMAs of Q block 0, then of block 1 with block 0's softmax and the next step's
-//      Q-tile copies between them; block 1's softmax; P -> LDS      | barrier X |
+//      Q-tile copies between them; block 1's softmax; P -> LDS      | flag X set |
 //      dV MFMAs with the previous step's dQ block (8 MFMAs) in their second half, its
 //      stores, its turn passed on; this step's turn polled and running sum loaded
 //                                                                   | barrier Y |
 //   B: dP MFMAs with the next step's dO-tile copies and the previous step's dQ block;
-//      its stores                                                   | barrier X |
+//      its stores                                                   | flag X awaited |
 //      P from LDS; dS of block 0 (registers, and transposed to LDS); dK MFMAs of
 //      block 0 with block 1's dS between them; dK MFMAs of block 1; the previous step's
 //      turn passed on; this step's turn polled and running sum loaded | barrier Y |
+// X synchronises only the two waves of a pair (an LDS flag holding the number of the
+// step whose P is in the pair's exchange area; A writes it after its P stores have
+// completed, B polls it), so that pairs do not wait for each other mid-step; Y is the
+// workgroup barrier that publishes every pair's dS^T and the next step's tiles.
 // A waves copy the next step's Q tile (after their S MFMAs), B waves its dO tile (during
 // their dP MFMAs). The compiler does not see these copies (inline assembly), so a wave
 // waits for its running-sum loads before issuing them (the vector-memory counter is in
@@ -122,6 +126,9 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
   const int ds_wr_lane = (32 * pr + l32) * kDsStride + 8 * hi;
   LDS_AS char* const sK = smem + C::OFF_K;
   LDS_AS char* const sPX = smem + C::OFF_PX + pr * C::PXW + 16 * lane;  // + 1024 c
+  // The pair's P-ready flag: the number of the step whose P is in the exchange area.
+  volatile LDS_AS int* const sFlag = reinterpret_cast<volatile LDS_AS int*>(smem + C::OFF_MISC + 16) + pr;
+  int gstep = 0;  // steps begun by this wave (the same sequence in both waves of a pair)
 
   // Copies are issued by the four B waves (wave index pr in the copy plans). The plans
   // are built where they are used, from the lane index passed through an empty asm, so
@@ -372,6 +379,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     bool loaded = false;
     for (int s = 0; s < n_steps; ++s) {
       PROF_COUNT(kProfSteps);
+      ++gstep;
       const int buf = (par0 + s) & 1;
       const int q0 = rec_cur.y;
       const int j = q0 / BC;
@@ -502,9 +510,12 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #pragma unroll
         for (int h = 0; h < 2; ++h) *reinterpret_cast<LDS_AS u32x4*>(sPX + 1024 * (2 + h)) = P[1][h];
         PROF_MARK(kProfMid0);
+        // This pair's P is in LDS: the flag tells the pair's B wave (the LDS writes have
+        // completed before the flag is written).
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();  // X: P of every pair in LDS
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (lane == 0) *sFlag = gstep;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         PROF_MARK(kProfBarrierX);
         // ---- dV += P^T dO, with the previous step's dQ block in the second half.
@@ -610,9 +621,19 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         mfma_result_wait(ld);
         reduce_store(pd, ld);
         PROF_MARK(kProfMid0);
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();  // X: P of every pair in LDS
+        // Wait for this pair's P (bounded, like the turn waits).
+        {
+          const long long t0 = wall_clock64();
+          int spins = 0;
+          while (__builtin_amdgcn_readfirstlane(*sFlag) != gstep) {
+            __builtin_amdgcn_s_sleep(1);
+            if ((++spins & 63) == 0 && wall_clock64() - t0 > p.timeout_ticks) {
+              if (lane == 0) raise_error(p.err, kErrTimeout);
+              failed = true;
+              break;
+            }
+          }
+        }
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         PROF_MARK(kProfBarrierX);
         // ---- dS = P (dP - D): bf16 pairs in registers, dS^T to LDS; dK += dS^T Q.
@@ -774,6 +795,7 @@ bwd_pair_kernel(BwdParams p) {
     if (v < 0) raise_error(p.err, kErrPlacement);
     sMisc[0] = v;
   }
+  if (tid < 4) sMisc[4 + tid] = 0;  // P-ready flags of the pairs (no step yet)
   __syncthreads();
   const int worker = sMisc[0];
   if (worker < 0) return;
