@@ -326,15 +326,24 @@ def sweep(steps, warmup):
 
 # Sources of the main kernel: the HBM-traffic figures in profiles/ hold for the kernel
 # these hashed to when the counters were taken.
-KERNEL_SOURCES = ("scheduling_fa_attn_amd/csrc/bwd_main.hip", "scheduling_fa_attn_amd/csrc/device_common.h",
-                  "scheduling_fa_attn_amd/csrc/kernels.h", "scheduling_fa_attn_amd/build.py")
+COMMON_SOURCES = ("scheduling_fa_attn_amd/csrc/device_common.h", "scheduling_fa_attn_amd/csrc/kernels.h",
+                  "scheduling_fa_attn_amd/build.py")
+KERNEL_SOURCES = {"bwd_main": ("scheduling_fa_attn_amd/csrc/bwd_main.hip",) + COMMON_SOURCES,
+                  "bwd_pair": ("scheduling_fa_attn_amd/csrc/bwd_pair.hip",) + COMMON_SOURCES}
 
 
-def kernel_source_hash():
+def main_kernel_name(N, d, kernel_choice):
+    """The main kernel dash_attn_bwd launches (deterministic = 1, one XCD per chain)."""
+    if d == 128 and N >= 512 and kernel_choice != "one_wave":
+        return "bwd_pair_kernel<128, true>"
+    return f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false>"
+
+
+def kernel_source_hash(kernel="bwd_pair_kernel<128, true>"):
     import hashlib
 
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[kernel.split("<")[0].replace("_kernel", "")]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -349,7 +358,7 @@ def traffic_bytes(workload, kernel):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel") != kernel or t.get("source_hash") != kernel_source_hash():
+    if t.get("kernel") != kernel or t.get("source_hash") != kernel_source_hash(kernel):
         return None
     return int(t["fetch_bytes"] + t["write_bytes"])
 
@@ -417,7 +426,7 @@ def main():
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
-    kernel = f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false>"
+    kernel = main_kernel_name(N, d, args.kernel)
     result = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 3),

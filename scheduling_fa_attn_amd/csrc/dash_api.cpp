@@ -109,8 +109,9 @@ std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
 int g_kernel = DASH_KERNEL_AUTO;  // main-kernel choice of later calls
-// What DASH_KERNEL_AUTO resolves to where the two-waves-per-SIMD kernel applies.
-constexpr bool kPairAuto = false;
+// What DASH_KERNEL_AUTO resolves to where the two-waves-per-SIMD kernel applies: that
+// kernel, measured at least as fast as the one-wave kernel on every d = 128 workload.
+constexpr bool kPairAuto = true;
 #ifdef DASH_REPLAY
 float* g_replay = nullptr;              // replay builds: dump of the ordered dQ partials
 size_t g_replay_bytes = 0;

@@ -69,20 +69,13 @@ def test_repeat_runs_bitwise_identical(causal):
             assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, det, rep)
 
 
-# The two-waves-per-SIMD kernel (d = 128, 128-row tiles: N >= 512), selected explicitly.
+# d = 128 with 128-row tiles (N >= 512): both main kernels, selected explicitly (the
+# default selects the two-waves-per-SIMD kernel there).
 PAIR_CASES = [
     (2, 4, 2, 700, 128),    # GQA, 6 tiles, ragged tail of 60 rows
     (1, 2, 2, 1024, 128),   # 8 tiles
     (1, 1, 1, 520, 128),    # 5 tiles (odd), ragged tail of 8 rows
 ]
-
-
-@pytest.fixture
-def two_waves():
-    from scheduling_fa_attn_amd import dash
-    assert dash.dash_set_kernel("two_waves") == dash.DASH_OK
-    yield
-    assert dash.dash_set_kernel("auto") == dash.DASH_OK
 
 
 def _with_kernel(kernel, fn):
@@ -94,9 +87,13 @@ def _with_kernel(kernel, fn):
         dash.dash_set_kernel("auto")
 
 
+KERNELS = ("two_waves", "one_wave")
+
+
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("pshape", PAIR_CASES, ids=_ids)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_parity_two_waves_kernel(pshape, causal):
+def test_parity_d128_kernels(pshape, causal, kernel):
     B, H, Hkv, N, d = pshape
     case = make_case(B, H, Hkv, N, d, causal, seed=2000 + N)
     dq_r, dk_r, dv_r = oracle_grads(case)
@@ -106,8 +103,8 @@ def test_parity_two_waves_kernel(pshape, causal):
         if sched == "sym_shift" and n_tiles % 2:
             continue
         for det in (1, 0):
-            print(f"two_waves case {_ids(pshape)} causal={causal} schedule={sched} det={det}", flush=True)
-            (dq, dk, dv), _ = _with_kernel("two_waves", lambda: run(case, dev, sched, det))
+            print(f"{kernel} case {_ids(pshape)} causal={causal} schedule={sched} det={det}", flush=True)
+            (dq, dk, dv), _ = _with_kernel(kernel, lambda: run(case, dev, sched, det))
             errs = rel_errs((dq, dk, dv), (dq_r, dk_r, dv_r))
             assert max(errs) <= TOL, (sched, det, errs)
 
@@ -122,13 +119,18 @@ def test_two_waves_kernel_is_selected():
     assert bf16_bytes(one[1]) != bf16_bytes(two[1])
 
 
+@pytest.mark.parametrize("kernel", KERNELS)
 @pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
-def test_repeat_runs_bitwise_identical_two_waves(causal, two_waves):
+def test_repeat_runs_bitwise_identical_d128_kernels(causal, kernel):
     case = make_case(2, 4, 2, 700, 128, causal, seed=78)
     dev = to_device(case)
-    for sched in SCHEDS[causal]:
-        ref, ws = run(case, dev, sched, 1)
-        ref_bytes = [bf16_bytes(t) for t in ref]
-        for rep in range(19):
-            out, ws = run(case, dev, sched, 1, workspace=ws)
-            assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, rep)
+
+    def body():
+        for sched in SCHEDS[causal]:
+            ref, ws = run(case, dev, sched, 1)
+            ref_bytes = [bf16_bytes(t) for t in ref]
+            for rep in range(19):
+                out, ws = run(case, dev, sched, 1, workspace=ws)
+                assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, rep)
+
+    _with_kernel(kernel, body)

@@ -113,7 +113,8 @@ def test_ordered_replay_bitwise(lib, case_args):
                     assert np.array_equal(got, want[ok]), (sched, bh, stp, blk)
 
 
-# The two-waves-per-SIMD kernel (d = 128, 128-row tiles), selected explicitly.
+# d = 128 with 128-row tiles: both main kernels, selected explicitly (1: one wave per
+# SIMD, 2: two waves per SIMD, the default there).
 PAIR_CASES = [
     (1, 4, 2, 512, 128, True),
     (1, 2, 2, 700, 128, False),  # ragged: rows 700..767 past N
@@ -121,11 +122,12 @@ PAIR_CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", [2, 1], ids=["two_waves", "one_wave"])
 @pytest.mark.parametrize("case_args", PAIR_CASES,
-                         ids=[f"two_waves-B{c[0]}H{c[1]}Hkv{c[2]}N{c[3]}d{c[4]}-{'causal' if c[5] else 'full'}"
+                         ids=[f"B{c[0]}H{c[1]}Hkv{c[2]}N{c[3]}d{c[4]}-{'causal' if c[5] else 'full'}"
                               for c in PAIR_CASES])
-def test_ordered_replay_bitwise_two_waves(lib, case_args):
-    assert lib.dash_set_kernel(2) == 0
+def test_ordered_replay_bitwise_d128_kernels(lib, case_args, kernel):
+    assert lib.dash_set_kernel(kernel) == 0
     try:
         test_ordered_replay_bitwise(lib, case_args)
     finally:
