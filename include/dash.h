@@ -179,10 +179,35 @@ int dash_tile_size(int N);
  * reduction order of dQ tile (b, h, j). *count receives the number of records (also
  * when capacity is too small, in which case DASH_ERR_WORKSPACE is returned and
  * nothing is written). *xcd_local (may be null) receives 1 when every dQ tile's
- * contributors sit on one L2 domain. Errors: as dash_attn_bwd's argument checks. */
+ * contributors sit on one L2 domain. DASH_SCHED_AUTO is resolved as by
+ * dash_schedule_resolve with d = 128. Errors: as dash_attn_bwd's argument checks. */
 int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
                         int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local);
+
+/* Hardware-aware schedule model (DASH paper, section 3.1 "Graph Construction": every
+ * task is a compute edge c then a reduction edge r on its CU, the reductions into one dQ
+ * tile follow each other in rank order; section 4.2: synchronising through a remote L2
+ * segment costs more than through the local one). Host-only, no GPU work.
+ * Builds the table of `schedule` for `num_xcd` L2 domains of `cus_per_xcd` CUs (the
+ * current placement) and writes into *makespan the longest path of its DAG when a task
+ * costs c, a reduction costs r_remote if the previous reduction into its dQ tile ran on
+ * another L2 domain and r_local otherwise (any time unit). DASH_SCHED_AUTO is resolved
+ * first as by dash_schedule_resolve with d = 128. Errors: as dash_schedule_table, and
+ * DASH_ERR_INVALID_ARG for negative or non-finite costs or a null makespan. */
+int dash_schedule_makespan(int B, int H, int Hkv, int N, int mask, int schedule,
+                           int num_xcd, int cus_per_xcd,
+                           double c, double r_local, double r_remote, double* makespan);
+
+/* The schedule dash_attn_bwd runs for `schedule` (host-only): a concrete schedule is
+ * returned unchanged after the argument checks; DASH_SCHED_AUTO becomes the valid
+ * schedule (naive, descending, and shift for the full mask or symmetric shift for the
+ * causal mask) with the smallest dash_schedule_makespan under costs measured on MI355X
+ * for head dimension d (task compute, reduction inside one XCD, reduction across XCDs),
+ * ties to shift / symmetric shift. Returns the schedule (>= 0) or a dash_status code
+ * (< 0) for invalid arguments, as dash_attn_bwd's checks. */
+int dash_schedule_resolve(int B, int H, int Hkv, int N, int d, int mask, int schedule,
+                          int num_xcd, int cus_per_xcd);
 
 #ifdef __cplusplus
 }

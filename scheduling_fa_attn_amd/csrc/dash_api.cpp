@@ -56,14 +56,79 @@ WsLayout ws_layout(int B, int H, int N, int d) {
 }
 
 // Checks shared by every entry point; pointers are checked separately.
-// DASH_SCHED_AUTO: the schedule measured fastest on MI355X at every point of the DASH
-// paper's benchmark grid (section 4.1: N = 512 .. 16384, d = 64 and 128): shift for the
-// full mask, symmetric shift for the causal mask (descending when the tile count is odd,
-// where symmetric shift is not defined). Other values are returned unchanged.
+// A valid stand-in for DASH_SCHED_AUTO while the arguments are checked (the call itself
+// resolves AUTO with the cost model below once the device topology is known): shift for
+// the full mask, symmetric shift for the causal mask, descending when the tile count is
+// odd (symmetric shift is not defined there). Other values are returned unchanged.
 int resolve_schedule(int schedule, int N, int mask) {
   if (schedule != DASH_SCHED_AUTO) return schedule;
   if (mask != DASH_MASK_CAUSAL) return DASH_SCHED_SHIFT;
   return cdiv(N, tile_for(N)) % 2 == 0 ? DASH_SCHED_SYM_SHIFT : DASH_SCHED_DESCENDING;
+}
+
+// Costs of one task (one KV tile against one Q tile) on MI355X for the hardware-aware
+// schedule model (DASH paper, section 3.1 model; section 4.2 local vs remote L2
+// segments), in microseconds, measured with the library's kernels:
+//  - d = 128, 128-row tiles: C2 (B=8, H=16, N=2048) main kernel at 828 TFLOP/s with the
+//    ordered reduction and 960 TFLOP/s with the reduction's memory traffic removed, over
+//    256 CUs and 20.97 MFLOP per task: c = 5.6, r_local = 0.9;
+//  - d = 64: C3 (B=4, H=32, N=4096, causal) main kernel 0.962 ms for 264 tasks per CU,
+//    split in the same proportion: c = 3.2, r_local = 0.45;
+//  - r_remote: dQ chains across XCDs (C4, B=1, H=16, N=16384, causal, symmetric shift)
+//    ran at 49.7 TFLOPS against 853.7 inside one XCD, 104 us instead of 6.1 us per task:
+//    r_remote = 98, independent of d (an L2 write-back and invalidate per step).
+// 64-row tiles (N < 512) do a quarter of the contraction work and half of the dQ
+// traffic per task. The same kernel binary runs every schedule (the table is data), so
+// the model has no schedule-dependent register term.
+dash::CostModel measured_costs(int d, int tile) {
+  dash::CostModel m;
+  m.c = d == 128 ? 5.6 : 3.2;
+  m.r_local = d == 128 ? 0.9 : 0.45;
+  m.r_remote = 98.0;
+  if (tile == 64) {
+    m.c *= 0.25;
+    m.r_local *= 0.5;
+  }
+  return m;
+}
+
+// DASH_SCHED_AUTO: the valid schedule (shift or symmetric shift for its mask, naive,
+// descending) with the smallest makespan under measured_costs on the tables built for
+// this topology and placement; ties go to the later candidate (shift, symmetric shift).
+// Returns a dash_status code on error.
+int model_schedule(int B, int H, int Hkv, int N, int d, int mask, int num_xcd, int cus_per_xcd, bool spread) {
+  const bool causal = mask == DASH_MASK_CAUSAL;
+  const int tile = tile_for(N);
+  const int n = static_cast<int>(cdiv(N, tile));
+  const int cands[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, causal ? DASH_SCHED_SYM_SHIFT : DASH_SCHED_SHIFT};
+  const dash::CostModel m = measured_costs(d, tile);
+  int best = -1;
+  double best_t = 0.0;
+  for (int sched : cands) {
+    if (sched == DASH_SCHED_SYM_SHIFT && n % 2) continue;
+    dash::SchedParams sp;
+    sp.B = B;
+    sp.H = H;
+    sp.Hkv = Hkv;
+    sp.N = N;
+    sp.tile = tile;
+    sp.causal = causal;
+    sp.kind = static_cast<Sched>(sched);
+    sp.num_xcd = num_xcd;
+    sp.cus_per_xcd = cus_per_xcd;
+    sp.spread = spread;
+    dash::Table t;
+    std::string err;
+    const int s = dash::build_table(sp, &t, &err);
+    if (s != 0) return s;
+    double span = 0.0;
+    if (!dash::table_makespan(t, cus_per_xcd, m, &span)) continue;  // (validated tables never cycle)
+    if (best < 0 || span <= best_t) {
+      best = sched;
+      best_t = span;
+    }
+  }
+  return best < 0 ? DASH_ERR_UNSUPPORTED : best;
 }
 
 int check_sizes(int B, int H, int Hkv, int N, int d, int mask, int schedule) {
@@ -109,6 +174,8 @@ std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
 int g_kernel = DASH_KERNEL_AUTO;  // main-kernel choice of later calls
+// DASH_SCHED_AUTO resolutions, per (B, H, Hkv, N, d, mask, XCDs, CUs per XCD, placement).
+std::map<std::tuple<int, int, int, int, int, int, int, int, int>, int> g_auto;
 // What DASH_KERNEL_AUTO resolves to where the two-waves-per-SIMD kernel applies: that
 // kernel, measured at least as fast as the one-wave kernel on every d = 128 workload.
 constexpr bool kPairAuto = true;
@@ -256,6 +323,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
             void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int mask, int schedule,
             int deterministic, void* workspace, size_t workspace_bytes, void* stream_ptr, void* ev_start,
             void* ev_stop) {
+  const int requested = schedule;
   schedule = resolve_schedule(schedule, N, mask);
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
@@ -278,6 +346,17 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     std::lock_guard<std::mutex> lock(g_mu);
     s = get_device(&st);
     if (s != DASH_OK) return s;
+    if (requested == DASH_SCHED_AUTO) {
+      const auto key = std::make_tuple(B, H, Hkv, N, d, mask, st->num_xcd, st->cus_per_xcd, g_placement);
+      auto it = g_auto.find(key);
+      if (it == g_auto.end()) {
+        const int r = model_schedule(B, H, Hkv, N, d, mask, st->num_xcd, st->cus_per_xcd,
+                                     g_placement == DASH_PLACEMENT_SPREAD);
+        if (r < 0) return r;
+        it = g_auto.emplace(key, r).first;
+      }
+      schedule = it->second;
+    }
     s = get_table(st, B, H, Hkv, N, causal, schedule, &tab);
     if (s != DASH_OK) return s;
   }
@@ -519,9 +598,68 @@ int dash_set_placement(int placement) {
   return DASH_OK;
 }
 
+int dash_schedule_resolve(int B, int H, int Hkv, int N, int d, int mask, int schedule, int num_xcd,
+                          int cus_per_xcd) {
+  const int requested = schedule;
+  schedule = resolve_schedule(schedule, N, mask);
+  int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
+  if (s != DASH_OK) return s;
+  if (num_xcd <= 0 || cus_per_xcd <= 0 || num_xcd > 64 || cus_per_xcd > 4096) return DASH_ERR_INVALID_ARG;
+  if (requested != DASH_SCHED_AUTO) return schedule;
+  bool spread;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    spread = g_placement == DASH_PLACEMENT_SPREAD;
+  }
+  return model_schedule(B, H, Hkv, N, d, mask, num_xcd, cus_per_xcd, spread);
+}
+
+int dash_schedule_makespan(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
+                           double c, double r_local, double r_remote, double* makespan) {
+  if (makespan == nullptr || !(c >= 0.0) || !(r_local >= 0.0) || !(r_remote >= 0.0) || !std::isfinite(c) ||
+      !std::isfinite(r_local) || !std::isfinite(r_remote))
+    return DASH_ERR_INVALID_ARG;
+  if (schedule == DASH_SCHED_AUTO) {
+    schedule = dash_schedule_resolve(B, H, Hkv, N, 128, mask, schedule, num_xcd, cus_per_xcd);
+    if (schedule < 0) return schedule;
+  }
+  int s = check_sizes(B, H, Hkv, N, 64, mask, schedule);
+  if (s != DASH_OK) return s;
+  if (num_xcd <= 0 || cus_per_xcd <= 0 || num_xcd > 64 || cus_per_xcd > 4096) return DASH_ERR_INVALID_ARG;
+  dash::SchedParams sp;
+  sp.B = B;
+  sp.H = H;
+  sp.Hkv = Hkv;
+  sp.N = N;
+  sp.tile = tile_for(N);
+  sp.causal = mask == DASH_MASK_CAUSAL;
+  sp.kind = static_cast<Sched>(schedule);
+  sp.num_xcd = num_xcd;
+  sp.cus_per_xcd = cus_per_xcd;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    sp.spread = g_placement == DASH_PLACEMENT_SPREAD;
+  }
+  dash::Table t;
+  std::string err;
+  s = dash::build_table(sp, &t, &err);
+  if (s != 0) return s;
+  dash::CostModel m;
+  m.c = c;
+  m.r_local = r_local;
+  m.r_remote = r_remote;
+  double span = 0.0;
+  if (!dash::table_makespan(t, cus_per_xcd, m, &span)) return DASH_ERR_INVALID_ARG;
+  *makespan = span;
+  return DASH_OK;
+}
+
 int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local) {
-  schedule = resolve_schedule(schedule, N, mask);
+  if (schedule == DASH_SCHED_AUTO) {
+    schedule = dash_schedule_resolve(B, H, Hkv, N, 128, mask, schedule, num_xcd, cus_per_xcd);
+    if (schedule < 0) return schedule;
+  }
   int s = check_sizes(B, H, Hkv, N, 64, mask, schedule);
   if (s != DASH_OK) return s;
   if (num_xcd <= 0 || cus_per_xcd <= 0 || count == nullptr || capacity < 0) return DASH_ERR_INVALID_ARG;

@@ -19,6 +19,9 @@
 #include "schedule.h"
 
 #include <algorithm>
+#include <unordered_map>
+
+#include <algorithm>
 #include <numeric>
 
 namespace dash {
@@ -195,6 +198,77 @@ int build_table(const SchedParams& p, Table* out, std::string* err) {
     }
   }
   return 0;
+}
+
+bool table_makespan(const Table& t, int cus_per_xcd, const CostModel& m, double* makespan) {
+  const size_t nt = t.tasks.size();
+  // Predecessor of every task on its CU and in its dQ tile's reduction order (-1: none).
+  std::vector<int64_t> prev_cu(nt, -1), prev_chain(nt, -1);
+  std::vector<int64_t> next_cu(nt, -1), next_chain(nt, -1);
+  std::vector<int64_t> last_of_worker(t.workers > 0 ? t.workers : 0, -1);
+  for (size_t k = 0; k < nt; ++k) {
+    const int w = t.task_worker[k];
+    if (last_of_worker[w] >= 0) {
+      prev_cu[k] = last_of_worker[w];
+      next_cu[last_of_worker[w]] = static_cast<int64_t>(k);
+    }
+    last_of_worker[w] = static_cast<int64_t>(k);
+  }
+  // Chains: members of dQ tile (b, h, j), placed by rank.
+  std::unordered_map<int64_t, std::vector<int64_t>> chains;
+  for (size_t k = 0; k < nt; ++k) {
+    const Item& it = t.items[t.task_item[k]];
+    const int64_t key = (static_cast<int64_t>(it.b) * 65536 + t.tasks[k].h) * (int64_t(1) << 24) + t.tasks[k].j;
+    std::vector<int64_t>& v = chains[key];
+    const int r = t.tasks[k].rank;
+    if (r < 0) return false;
+    if (static_cast<size_t>(r) >= v.size()) v.resize(r + 1, -1);
+    if (v[r] >= 0) return false;  // two tasks with one rank
+    v[r] = static_cast<int64_t>(k);
+  }
+  for (const auto& kv : chains) {
+    const std::vector<int64_t>& v = kv.second;
+    for (size_t r = 1; r < v.size(); ++r) {
+      if (v[r] < 0 || v[r - 1] < 0) return false;  // a gap in the ranks
+      prev_chain[v[r]] = v[r - 1];
+      next_chain[v[r - 1]] = v[r];
+    }
+  }
+  // Kahn's order over tasks; per task: compute start = end of the CU's previous
+  // reduction, reduction start = max(compute end, end of the chain predecessor's
+  // reduction).
+  std::vector<int> indeg(nt, 0);
+  std::vector<double> c_start(nt, 0.0), r_floor(nt, 0.0), r_end(nt, 0.0);
+  std::vector<int64_t> queue;
+  queue.reserve(nt);
+  for (size_t k = 0; k < nt; ++k) {
+    indeg[k] = (prev_cu[k] >= 0) + (prev_chain[k] >= 0);
+    if (indeg[k] == 0) queue.push_back(static_cast<int64_t>(k));
+  }
+  const int S = cus_per_xcd > 0 ? cus_per_xcd : 1;
+  double span = 0.0;
+  size_t head = 0;
+  while (head < queue.size()) {
+    const int64_t k = queue[head++];
+    const int64_t pc = prev_chain[k];
+    const bool remote = pc >= 0 && t.task_worker[pc] / S != t.task_worker[k] / S;
+    const double rs = std::max(c_start[k] + m.c, r_floor[k]);
+    r_end[k] = rs + (remote ? m.r_remote : m.r_local);
+    span = std::max(span, r_end[k]);
+    const int64_t nc = next_cu[k];
+    if (nc >= 0) {
+      c_start[nc] = std::max(c_start[nc], r_end[k]);
+      if (--indeg[nc] == 0) queue.push_back(nc);
+    }
+    const int64_t nr = next_chain[k];
+    if (nr >= 0) {
+      r_floor[nr] = std::max(r_floor[nr], r_end[k]);
+      if (--indeg[nr] == 0) queue.push_back(nr);
+    }
+  }
+  if (queue.size() != nt) return false;
+  *makespan = span;
+  return true;
 }
 
 }  // namespace dash

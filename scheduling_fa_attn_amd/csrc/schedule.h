@@ -57,4 +57,23 @@ inline int tiles_per_head(int N, int tile) { return (N + tile - 1) / tile; }
 // Builds the table. Returns 0 on success, or a dash_status code with a message in *err.
 int build_table(const SchedParams& p, Table* out, std::string* err);
 
+// Cost model of a table (DASH paper, section 3.1, "Graph Construction"): every task is
+// a compute edge c followed by a reduction edge r on its CU; a CU runs its tasks back
+// to back; the reductions into one dQ tile follow each other in rank order (zero-weight
+// edge from the end of one to the start of the next). Hardware-aware refinement
+// (section 4.2: synchronisation through the local L2 segment is cheaper than through a
+// remote one; on MI355X the L2 domains are the XCDs): a reduction whose predecessor in
+// its dQ tile's order ran on another L2 domain costs r_remote instead of r_local. The
+// first reduction of a tile costs r_local.
+struct CostModel {
+  double c = 1.0;
+  double r_local = 0.0;
+  double r_remote = 0.0;
+};
+
+// Longest path (makespan) of the table's DAG under `m`, with the CU of worker w on L2
+// domain w / cus_per_xcd. Returns false if the DAG has a cycle (the table would
+// deadlock), true otherwise.
+bool table_makespan(const Table& t, int cus_per_xcd, const CostModel& m, double* makespan);
+
 }  // namespace dash

@@ -34,6 +34,8 @@ EXPORTED = (
     "dash_status_string",
     "dash_tile_size",
     "dash_schedule_table",
+    "dash_schedule_makespan",
+    "dash_schedule_resolve",
     "dash_set_placement",
     "dash_set_kernel",
     "dash_attn_fwd",
@@ -81,6 +83,11 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_schedule_table.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), ctypes.c_longlong,
                                         ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
     lib.dash_schedule_table.restype = i
+    lib.dash_schedule_makespan.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, ctypes.c_double,
+                                           ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
+    lib.dash_schedule_makespan.restype = i
+    lib.dash_schedule_resolve.argtypes = [i, i, i, i, i, i, i, i, i]
+    lib.dash_schedule_resolve.restype = i
     lib.dash_set_placement.argtypes = [i]
     lib.dash_set_placement.restype = i
     lib.dash_set_kernel.argtypes = [i]
@@ -129,6 +136,25 @@ def dash_set_kernel(kernel, lib=None) -> int:
     SIMD, every configuration) or "two_waves" (two waves per SIMD, d = 128 with the
     ordered or atomic reduction; other calls keep the one-wave kernel)."""
     return int((lib or load()).dash_set_kernel(KERNELS.get(kernel, kernel)))
+
+
+def dash_schedule_makespan(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd, c, r_local, r_remote, lib=None):
+    """Makespan of the schedule table's DAG under task cost c and reduction costs
+    r_local / r_remote (host only). Raises DashError on an error status."""
+    out = ctypes.c_double(0.0)
+    st = (lib or load()).dash_schedule_makespan(B, H, Hkv, N, MASKS.get(mask, mask), SCHEDULES.get(schedule, schedule),
+                                                num_xcd, cus_per_xcd, float(c), float(r_local), float(r_remote),
+                                                ctypes.byref(out))
+    if st != DASH_OK:
+        raise DashError(st, "dash_schedule_makespan")
+    return out.value
+
+
+def dash_schedule_resolve(B, H, Hkv, N, d, mask, schedule, num_xcd, cus_per_xcd, lib=None) -> int:
+    """The schedule dash_attn_bwd runs for `schedule` ("auto" resolved by the cost model);
+    a negative value is an error status."""
+    return int((lib or load()).dash_schedule_resolve(B, H, Hkv, N, d, MASKS.get(mask, mask),
+                                                     SCHEDULES.get(schedule, schedule), num_xcd, cus_per_xcd))
 
 
 def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):

@@ -152,16 +152,117 @@ def test_placement_argument_errors():
     assert dash.dash_set_placement(-1) == dash.DASH_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("N,mask,resolved", [
-    (2048, "full", "shift"),
-    (4096, "causal", "sym_shift"),
-    (1000, "causal", "sym_shift"),     # 8 tiles of 128
-    (1100, "causal", "descending"),    # 9 tiles: symmetric shift is not defined
-    (448, "causal", "descending"),     # 7 tiles of 64
-    (256, "full", "shift"),
-])
-def test_auto_schedule_resolves_to_the_measured_best(N, mask, resolved):
-    """schedule=auto gives the same table as the schedule it resolves to."""
+NAMES = {0: "naive", 1: "descending", 2: "shift", 3: "sym_shift"}
+
+
+@pytest.mark.parametrize("N,mask", [(2048, "full"), (4096, "causal"), (1000, "causal"), (1100, "causal"),
+                                    (448, "causal"), (256, "full")])
+def test_auto_schedule_table_is_the_resolved_schedule(N, mask):
+    """schedule=auto gives the same table as the schedule dash_schedule_resolve names
+    (odd tile counts, 1100 and 448, never resolve to symmetric shift)."""
+    resolved = dash.dash_schedule_resolve(2, 4, 2, N, 128, mask, "auto", 8, 32)
+    assert resolved in NAMES
+    n = -(-N // dash.dash_tile_size(N))
+    assert not (resolved == 3 and n % 2)
     auto, local_a = dash.dash_schedule_table(2, 4, 2, N, mask, "auto", 8, 32)
-    ref, local_r = dash.dash_schedule_table(2, 4, 2, N, mask, resolved, 8, 32)
+    ref, local_r = dash.dash_schedule_table(2, 4, 2, N, mask, NAMES[resolved], 8, 32)
     assert np.array_equal(auto, ref) and local_a == local_r
+
+
+# ---------------------------------------------------------------------------------
+# Hardware-aware cost model (dash_schedule_makespan / dash_schedule_resolve).
+# ---------------------------------------------------------------------------------
+
+def _oracle_makespan(rec, table, cus_per_xcd, c, r_local, r_remote):
+    """The oracle DAG simulator on the exported table, each task's reduction costing
+    r_remote when the previous reduction into its dQ tile ran on another L2 domain."""
+    pred_worker = {}
+    chains = {}
+    for w, b, h, g, i, j, rank in rec.tolist():
+        chains.setdefault((b, h, j), []).append((rank, w, (b, h, g, i, j, rank)))
+    for members in chains.values():
+        members.sort()
+        for (_, w0, _), (_, w1, key1) in zip(members, members[1:]):
+            pred_worker[key1] = (w0, w1)
+
+    def r_cost(task):
+        pw = pred_worker.get(tuple(task))
+        return r_remote if pw is not None and pw[0] // cus_per_xcd != pw[1] // cus_per_xcd else r_local
+
+    return osch.simulate(table, c, r_cost)
+
+
+MODEL_CASES = [
+    # (B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd, placement)
+    (1, 2, 2, 256, "full", "shift", 1, 4, "aggregate"),
+    (1, 2, 2, 256, "causal", "descending", 2, 4, "aggregate"),
+    (2, 8, 8, 2048, "full", "naive", 8, 32, "aggregate"),
+    (2, 8, 8, 2048, "full", "shift", 8, 32, "aggregate"),
+    (2, 16, 16, 4096, "causal", "sym_shift", 8, 32, "aggregate"),
+    (1, 16, 4, 4096, "causal", "descending", 8, 32, "aggregate"),
+    (1, 4, 4, 16384, "causal", "sym_shift", 8, 32, "spread"),   # chains across XCDs
+    (1, 2, 2, 16384, "full", "shift", 4, 32, "spread"),
+]
+
+
+@pytest.mark.parametrize("case", MODEL_CASES, ids=["-".join(map(str, c)) for c in MODEL_CASES])
+def test_makespan_equals_oracle_simulator(case):
+    """The C++ model's longest path equals the oracle simulator's on the same table
+    (integer costs, so the sums are exact), with local and remote reduction costs."""
+    B, H, Hkv, N, mask, sched, X, S, placement = case
+    assert dash.dash_set_placement(placement) == dash.DASH_OK
+    try:
+        rec, local = dash.dash_schedule_table(B, H, Hkv, N, mask, sched, X, S)
+        table = to_table(rec, B, H, Hkv, N, mask, sched, X * S)
+        for c, rl, rr in ((5.0, 1.0, 7.0), (2.0, 3.0, 3.0), (1.0, 0.0, 0.0)):
+            got = dash.dash_schedule_makespan(B, H, Hkv, N, mask, sched, X, S, c, rl, rr)
+            want = _oracle_makespan(rec, table, S, c, rl, rr)
+            assert got == want, (c, rl, rr, got, want)
+        if placement == "spread" and -(-N // 128) > S:
+            assert not local  # the case does exercise remote reductions
+            got_l = dash.dash_schedule_makespan(B, H, Hkv, N, mask, sched, X, S, 5.0, 1.0, 1.0)
+            got_r = dash.dash_schedule_makespan(B, H, Hkv, N, mask, sched, X, S, 5.0, 1.0, 7.0)
+            assert got_r > got_l
+    finally:
+        dash.dash_set_placement("aggregate")
+
+
+@pytest.mark.parametrize("kind,causal,n,m", [("naive", False, 8, 4), ("shift", False, 8, 4), ("naive", True, 8, 4),
+                                             ("sym_shift", True, 8, 4), ("shift", False, 16, 2),
+                                             ("descending", True, 8, 2)])
+def test_makespan_closed_forms(kind, causal, n, m):
+    """In the paper's normalisation (one group of n lanes, m heads) the C++ model gives
+    the section 3.2-3.4 closed forms (exact for these cases, r < c)."""
+    c, r = 3.0, 1.0
+    N = n * (64 if n * 64 < 512 else 128)
+    got = dash.dash_schedule_makespan(1, m, m, N, "causal" if causal else "full", kind, 1, n, c, r, r)
+    want = {"naive": m * n * (c + r) + (n - 1) * r, "shift": m * n * (c + r),
+            "sym_shift": m * (n + 1) * (c + r) / 2, "descending": m * (n + 1) * (c + r) / 2 + (n - 1) * r}[kind]
+    assert got == want, (got, want)
+
+
+def test_auto_picks_measured_fastest_on_paper_grid():
+    """On the DASH paper's benchmark grid (section 4.1: 16 384 tokens, hidden 2048, N =
+    512 .. 16384, d = 64 and 128) the cost model picks the schedule measured fastest on
+    MI355X at every point: shift for the full mask, symmetric shift for the causal mask."""
+    for d in (64, 128):
+        for mask, want in (("full", 2), ("causal", 3)):
+            for N in (512, 1024, 2048, 4096, 8192, 16384):
+                B, H = 16384 // N, 2048 // d
+                assert dash.dash_schedule_resolve(B, H, H, N, d, mask, "auto", 8, 32) == want, (d, mask, N)
+
+
+def test_auto_never_picks_an_invalid_schedule():
+    """An odd tile count rules symmetric shift out; explicit schedules pass through."""
+    assert dash.dash_schedule_resolve(1, 4, 4, 640, 128, "causal", "auto", 8, 32) in (0, 1)
+    assert dash.dash_schedule_resolve(1, 4, 4, 640, 128, "causal", "naive", 8, 32) == 0
+    assert dash.dash_schedule_resolve(1, 4, 4, 640, 128, "causal", "sym_shift", 8, 32) == dash.DASH_ERR_UNSUPPORTED
+    assert dash.dash_schedule_resolve(1, 4, 4, 2048, 96, "full", "auto", 8, 32) == dash.DASH_ERR_UNSUPPORTED
+    assert dash.dash_schedule_resolve(1, 4, 4, 2048, 128, "full", "auto", 0, 32) == dash.DASH_ERR_INVALID_ARG
+
+
+def test_makespan_rejects_bad_costs():
+    with pytest.raises(dash.DashError):
+        dash.dash_schedule_makespan(1, 2, 2, 256, "full", "shift", 1, 4, -1.0, 0.0, 0.0)
+    with pytest.raises(dash.DashError):
+        dash.dash_schedule_makespan(1, 2, 2, 256, "full", "shift", 1, 4, float("nan"), 0.0, 0.0)
