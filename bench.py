@@ -334,8 +334,8 @@ KERNEL_SOURCES = {"bwd_main": ("scheduling_fa_attn_amd/csrc/bwd_main.hip",) + CO
 
 def main_kernel_name(N, d, kernel_choice):
     """The main kernel dash_attn_bwd launches (deterministic = 1, one XCD per chain)."""
-    if d == 128 and N >= 512 and kernel_choice != "one_wave":
-        return "bwd_pair_kernel<128, true>"
+    if N >= 512 and kernel_choice != "one_wave":
+        return f"bwd_pair_kernel<{d}, true>"
     return f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false>"
 
 
@@ -378,7 +378,7 @@ def main():
                     help="skip the cold-cache timing (L2 and memory-side cache flushed before every call)")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--kernel", default="auto", choices=["auto", "one_wave", "two_waves"],
-                    help="main backward kernel (dash_set_kernel); two_waves applies to d = 128")
+                    help="main backward kernel (dash_set_kernel); two_waves applies to 128-row tiles (N >= 512)")
     ap.add_argument("--sweep", action="store_true",
                     help="only time every schedule and the atomic variant over the paper's grid (16 384 tokens, "
                          "hidden 2048, N = 512 .. 16384, d = 64 and 128, both masks) and print one JSON line")

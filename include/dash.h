@@ -88,9 +88,9 @@ int dash_set_placement(int placement);
 /* Main backward kernel. The one-wave-per-SIMD kernel gives each of 4 waves per CU 32 KV
  * rows and all five contractions. The two-waves-per-SIMD kernel gives the same 32 rows
  * to a pair of waves that split the contractions by role (S, P, dV and dP, dS, dK; one
- * dQ block each), so that two waves share every SIMD. The latter covers d = 128 with
- * deterministic = 0 or 1 (dQ chains inside one XCD); other calls use the former under
- * every setting. DASH_KERNEL_AUTO picks the one measured faster: the two-waves
+ * dQ block each), so that two waves share every SIMD. The latter covers 128-row tiles
+ * (N >= 512) with deterministic = 0 or 1 (dQ chains inside one XCD); other calls use the
+ * former under every setting. DASH_KERNEL_AUTO picks the one measured faster: the two-waves
  * kernel wherever it applies. Both give results
  * within the same tolerance; their bits differ (dS is formed from the bf16 P in the
  * two-waves kernel), and each is bitwise reproducible on its own. */

@@ -1,5 +1,5 @@
 // Main HIP kernel of the deterministic attention backward for gfx950 (MI355X), two
-// waves per SIMD (head dimension 128).
+// waves per SIMD (head dimension 128 or 64, 128-row tiles).
 //
 // Math (DASH paper, arXiv 2601.21824, section 2.1; "Writing an Attention Kernel",
 // section "In the real world"): per (batch b, query head h, key/value head g):
@@ -23,7 +23,8 @@
 // wave and 64-row step that is 40 MFMAs (16 + 16 + 8) and about 250 registers: a K or V
 // operand (32 AGPRs), K^T of one d block (32), one accumulator (dV or dK, 64) and the
 // VGPRs in flight, so the two waves of a pair share one SIMD and each covers the other's
-// stalls. P goes from A to B as bf16 through a 4 KiB LDS area per pair (lane l of B holds
+// stalls. At d = 64 the step's partial has four 32x32 blocks: the A waves compute them
+// (24 MFMAs per A wave and step, 16 per B wave). P goes from A to B as bf16 through a 4 KiB LDS area per pair (lane l of B holds
 // the same S/dP accumulator elements as lane l of A); dS goes to LDS transposed, as the
 // dQ contraction needs it anyway.
 //
@@ -87,11 +88,16 @@ struct PairCfg {
   static constexpr int OFF_DL = OFF_NL + 2 * 256;   // 2 x 64 floats: -D
   static constexpr int OFF_MISC = OFF_DL + 2 * 256;
   static constexpr int BYTES = OFF_MISC + 64;
-  static_assert(2 * DB == NW, "one 32x32 dQ block per wave and step");
+  // dQ blocks of a step's 64 x D partial: one per wave at D = 128; at D = 64 the four
+  // blocks go to the A waves and the B waves compute no dQ.
+  static_assert(2 * DB == NW || 2 * DB == NW / 2, "one 32x32 dQ block per wave, or per A wave");
+  static constexpr bool kAllWavesDq = 2 * DB == NW;
   static_assert(BYTES <= 160 * 1024, "LDS of one CU");
   static_assert(QT % 1024 == 0 && DST % 1024 == 0 && (BC * ST) % 1024 == 0, "1 KiB-aligned tiles");
 };
 
+// (B's dQ MFMAs, at D = 128, run in the last KK slots of its 2 DK dP slots, with their
+// operands prefetched from the slot before.)
 // Body of the kernel for one role (ROLE_A: waves 0-3, else waves 4-7). Each role is
 // its own inlined copy, so that the register allocator never sees the values of one
 // role live in the other's code.
@@ -100,6 +106,9 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
   using C = PairCfg<D>;
   constexpr int BC = C::BC, BQ = C::BQ, SUBS = C::SUBS, DB = C::DB, DK = C::DK, KK = C::KK, ST = C::ST;
   constexpr bool roleA = ROLE_A;
+  // This wave's dQ block (32 Q rows x 32 d columns of the step's partial) and whether it
+  // has one: block dqb is Q block dqb / DB, d block dqb % DB.
+  constexpr bool HAS_DQ = C::kAllWavesDq || ROLE_A;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int pr = w & 3;  // pair: KV rows 32 pr .. 32 pr + 31 of the tile
@@ -218,12 +227,13 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     const int kvcol = kv0 + 32 * pr + l32;  // this lane's KV row in S, P, dP, dS
     // dQ block of this wave: Q rows 32 (w / 4) .. of the step, d columns 32 pr ..; its B
     // operand K^T (k-step kk: KV rows 16 kk .. 16 kk + 15 in the dS operand's order).
-    const int qbq = w >> 2;
+    const int dqb = C::kAllWavesDq ? w : pr;
+    const int qbq = dqb / DB, dbq = dqb % DB;
     bf16x8 kT[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      const int koff = kd_lane + 16 * kk * ST + 64 * pr;
-      kT[kk] = to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST)));
+      const int koff = kd_lane + 16 * kk * ST + 64 * dbq;
+      kT[kk] = HAS_DQ ? to_agpr(join(lds_tr(sK, koff), lds_tr(sK, koff + ST))) : bf16x8{};
     }
     __syncthreads();
     PROF_MARK(kProfPro);
@@ -247,7 +257,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 
     constexpr int kBlkBytes = kDqBlock * 4;
     // Ordered variant: this lane's first 4 floats in block w of the step's 2 DB blocks.
-    const int acc_off = lane * 16 + w * kBlkBytes;
+    const int acc_off = lane * 16 + dqb * kBlkBytes;
     struct Pending {
       int rank, last;
       int* sem;
@@ -268,7 +278,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       pd.go = !failed;
       pd.acc_rs = DET ? make_rsrc(pd.acc_blk, pd.go ? 2 * DB * kBlkBytes : 0)
                       : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, pd.go ? 64 * D * 4 : 0);
-      pd.sem = p.sem + bh * p.sem_stride + (q0s / BQ) * kSemPerStep + w;
+      pd.sem = p.sem + bh * p.sem_stride + (q0s / BQ) * kSemPerStep + dqb;
 #ifdef DASH_REPLAY
       pd.dump = p.replay ? p.replay + (((bh * (p.row_stride / BQ) + q0s / BQ) * (2 * DB)) * p.replay_ranks + pd.rank) *
                                           static_cast<int64_t>(kDqBlock)
@@ -277,7 +287,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       return pd;
     };
     auto reduce_needs_turn = [&](const Pending& pd) __attribute__((always_inline)) {
-      return DET && pd.go && pd.rank > 0;
+      return HAS_DQ && DET && pd.go && pd.rank > 0;
     };
     auto reduce_wait = [&](Pending& pd) __attribute__((always_inline)) {
       if (reduce_needs_turn(pd)) {
@@ -288,7 +298,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     };
     // Running sum so far; the first contributor reads through an empty descriptor (zeros).
     auto reduce_load = [&](const Pending& pd, floatx16& ld) __attribute__((always_inline)) {
-      if (!DET) return;
+      if (!DET || !HAS_DQ) return;
       const rsrc_t lrs = make_rsrc(pd.acc_blk, reduce_needs_turn(pd) ? 2 * DB * kBlkBytes : 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -304,6 +314,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     floatx16 run;  // replay builds: running sum loaded for the partial being reduced
 #endif
     auto reduce_store = [&](const Pending& pd, const floatx16& v_in) __attribute__((always_inline)) {
+      if (!HAS_DQ) return;
 #ifdef DASH_REPLAY
       if (!pd.go) return;
       floatx16 v = v_in;
@@ -317,7 +328,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
               const float f = v_in[4 * i + e];
               x[e] = __builtin_bit_cast(unsigned, f);
             }
-            float* dst = pd.dump + static_cast<int64_t>(w) * p.replay_ranks * kDqBlock + 256 * i + 4 * lane;
+            float* dst = pd.dump + static_cast<int64_t>(dqb) * p.replay_ranks * kDqBlock + 256 * i + 4 * lane;
             *reinterpret_cast<u32x4*>(dst) = x;
           }
         }
@@ -331,9 +342,9 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       for (int i = 0; i < 4; ++i) {
         if (!DET) {
           // Row-major accumulator; element (t = i, e) sits at row 32 qbq + 16 (t / 2) +
-          // 2 (t % 2) + hi + 4 e, column 32 pr + l32.
+          // 2 (t % 2) + hi + 4 e, column 32 dbq + l32.
           const int t = i;
-          const int vb = 4 * (hi * D + 32 * pr + l32);
+          const int vb = 4 * (hi * D + 32 * dbq + l32);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float x = v[4 * t + e];
@@ -353,14 +364,14 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     };
     // After wait_mem_done(): this wave's accumulator stores are in the L2.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
-      if (!DET || !pd.go || pd.last) return;
+      if (!HAS_DQ || !DET || !pd.go || pd.last) return;
       if (lane == 0)
         __builtin_amdgcn_raw_buffer_store_b32(static_cast<unsigned>(pd.rank + 1), make_rsrc(pd.sem, 4), 0, 0, 0);
     };
     // Poll of the turn: a plain load whose value is read later (issued on every step,
     // through an empty descriptor when no turn is needed).
     auto reduce_poll = [&](const Pending& pd) __attribute__((always_inline)) -> int {
-      if (!DET) return 0;
+      if (!DET || !HAS_DQ) return 0;
       const rsrc_t srs = make_rsrc(pd.sem, reduce_needs_turn(pd) ? 4 : 0);
       return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(srs, 0, 0, kSC0));
     };
@@ -537,21 +548,26 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #pragma unroll
         for (int i = 0; i < kR - 1; ++i) {
           bo[i] = bt_load(sdO, i);
-          aqd[i] = dq_opnd(sdSprev, i);
+          if (HAS_DQ) aqd[i] = dq_opnd(sdSprev, i);
         }
         SLOT();
 #pragma unroll
         for (int jj = 0; jj < 2 * NIT; ++jj) {
           if (jj + kR - 1 < 2 * NIT) bo[(jj + kR - 1) % kR] = bt_load(sdO, jj + kR - 1);
-          if (jj + kR - 1 < KK) aqd[(jj + kR - 1) % kR] = dq_opnd(sdSprev, jj + kR - 1);
+          if (HAS_DQ && jj + kR - 1 < KK) aqd[(jj + kR - 1) % kR] = dq_opnd(sdSprev, jj + kR - 1);
           const int qb = jj / NIT, itr = jj % NIT;
           mfma32_acc(acc[itr % DB], as_bf16x8(P[qb][itr / DB]), bo[jj % kR]);
-          if (jj < KK) dq_mma(ld, jj, aqd[jj % kR], kT[jj]);
+          if (HAS_DQ && jj < KK) dq_mma(ld, jj, aqd[jj % kR], kT[jj]);
           if (jj == KK) {
             mfma_result_wait(ld);
             reduce_store(pd, ld);
           }
           SLOT();
+        }
+        if constexpr (2 * NIT <= KK) {
+          // (d = 64: the dQ MFMAs span the whole phase.)
+          mfma_result_wait(ld);
+          reduce_store(pd, ld);
         }
         PROF_MARK(kProfDv0);
         PROF_MARK(kProfLoads);
@@ -607,9 +623,10 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         for (int i = 0; i < 2 * DK; ++i) {
           if (i + kR - 1 < 2 * DK) ad[(i + kR - 1) % kR] = lds_ld16(sdO, sdp_off((i + kR - 1) / DK, (i + kR - 1) % DK));
           const int kk = i - (2 * DK - KK);
-          if (kk + kR - 1 >= 0 && kk + kR - 1 < KK) aqd[(kk + kR - 1) % kR] = dq_opnd(sdSprev, kk + kR - 1);
+          if (HAS_DQ && kk + kR - 1 >= 0 && kk + kR - 1 < KK)
+            aqd[(kk + kR - 1) % kR] = dq_opnd(sdSprev, kk + kR - 1);
           mfma32_vab(i < DK ? dP0 : dP1, ad[i % kR], kv[i % DK]);
-          if (kk >= 0) dq_mma(ld, kk, aqd[kk % kR], kT[kk]);
+          if (HAS_DQ && kk >= 0) dq_mma(ld, kk, aqd[kk % kR], kT[kk]);
           if (i < DK) {
 #pragma unroll
             for (int o = i * kCopyOps / DK; o < (i + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
@@ -686,7 +703,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
               wait_mem_done();
             } else {
               __atomic_signal_fence(__ATOMIC_SEQ_CST);
-              __builtin_amdgcn_s_waitcnt(wait_vmcnt(16));
+              __builtin_amdgcn_s_waitcnt(wait_vmcnt(HAS_DQ ? 16 : 0));
               __atomic_signal_fence(__ATOMIC_SEQ_CST);
             }
             if (have_prev) reduce_signal(pd);
@@ -714,7 +731,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       mfma_settle(acc);
     }
     // The item's last step: its dQ block and reduction.
-    {
+    if constexpr (HAS_DQ) {
       if (!loaded) {
         reduce_wait(pd);
         reduce_load(pd, ld);
@@ -821,6 +838,10 @@ static hipError_t launch_pair_t(const BwdParams& prm, int grid, hipStream_t stre
 
 hipError_t launch_pair_d128(const BwdParams& prm, int grid, hipStream_t stream) {
   return launch_pair_t<128>(prm, grid, stream);
+}
+
+hipError_t launch_pair_d64(const BwdParams& prm, int grid, hipStream_t stream) {
+  return launch_pair_t<64>(prm, grid, stream);
 }
 
 }  // namespace dash

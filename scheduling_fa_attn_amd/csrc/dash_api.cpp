@@ -431,19 +431,20 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   }
 #endif
   if (ev_start && hipEventRecord(static_cast<hipEvent_t>(ev_start), stream) != hipSuccess) return DASH_ERR_HIP;
-  // The two-waves-per-SIMD kernel covers d = 128 with 128-row tiles, the ordered
-  // reduction inside one XCD and the atomic variant; everything else runs on the
+  // The two-waves-per-SIMD kernel covers 128-row tiles with the ordered reduction
+  // inside one XCD and the atomic variant; everything else runs on the
   // one-wave-per-SIMD kernel.
   int kernel;
   {
     std::lock_guard<std::mutex> lock(g_mu);
     kernel = g_kernel;
   }
-  const bool pair_ok = d == 128 && tab->tile == 128 && deterministic != 2 && (deterministic == 0 || bp.xcd_local ||
+  const bool pair_ok = tab->tile == 128 && deterministic != 2 && (deterministic == 0 || bp.xcd_local ||
                        st->num_xcd == 1);
   const bool use_pair = pair_ok && (kernel == DASH_KERNEL_TWO_WAVES_PER_SIMD || (kernel == DASH_KERNEL_AUTO && kPairAuto));
-  hipError_t e = use_pair ? dash::launch_pair_d128(bp, tab->workers, stream)
-                          : dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream);
+  hipError_t e = !use_pair ? dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream)
+                 : d == 128 ? dash::launch_pair_d128(bp, tab->workers, stream)
+                            : dash::launch_pair_d64(bp, tab->workers, stream);
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
   if (e != hipSuccess) return DASH_ERR_HIP;
   if (ev_stop && hipEventRecord(static_cast<hipEvent_t>(ev_stop), stream) != hipSuccess) return DASH_ERR_HIP;

@@ -91,6 +91,9 @@ __device__ __forceinline__ void mfma_result_wait(floatx16& x, floatx16& y) {
 __device__ __forceinline__ void mfma_settle(floatx16 (&a)[2], floatx16 (&b)[2]) {
   asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[0]), "+a"(a[1]), "+a"(b[0]), "+a"(b[1]));
 }
+__device__ __forceinline__ void mfma_settle(floatx16 (&a)[2]) {
+  asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[0]), "+a"(a[1]));
+}
 __device__ __forceinline__ void mfma_settle(floatx16 (&a)[4]) {
   asm volatile("s_nop 7\n\ts_nop 4" : "+a"(a[0]), "+a"(a[1]), "+a"(a[2]), "+a"(a[3]));
 }

@@ -141,6 +141,7 @@ hipError_t launch_main_d128_nw4(const BwdParams& prm, int grid, hipStream_t stre
 // Two-waves-per-SIMD main kernel (d = 128, 128-row tiles, ordered XCD-local or atomic
 // reduction; 8 waves per workgroup).
 hipError_t launch_pair_d128(const BwdParams& prm, int grid, hipStream_t stream);
+hipError_t launch_pair_d64(const BwdParams& prm, int grid, hipStream_t stream);
 inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hipStream_t stream) {
   if (d == 64 && nw == 2) return launch_main_d64_nw2(prm, grid, stream);
   if (d == 64 && nw == 4) return launch_main_d64_nw4(prm, grid, stream);

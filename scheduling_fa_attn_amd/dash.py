@@ -133,7 +133,7 @@ KERNELS = {"auto": 0, "one_wave": 1, "two_waves": 2}
 
 def dash_set_kernel(kernel, lib=None) -> int:
     """Main backward kernel of later calls: "auto" (default), "one_wave" (one wave per
-    SIMD, every configuration) or "two_waves" (two waves per SIMD, d = 128 with the
+    SIMD, every configuration) or "two_waves" (two waves per SIMD, 128-row tiles with the
     ordered or atomic reduction; other calls keep the one-wave kernel)."""
     return int((lib or load()).dash_set_kernel(KERNELS.get(kernel, kernel)))
 

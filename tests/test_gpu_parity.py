@@ -69,12 +69,14 @@ def test_repeat_runs_bitwise_identical(causal):
             assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, det, rep)
 
 
-# d = 128 with 128-row tiles (N >= 512): both main kernels, selected explicitly (the
-# default selects the two-waves-per-SIMD kernel there).
+# 128-row tiles (N >= 512): both main kernels, selected explicitly (the default selects
+# the two-waves-per-SIMD kernel there).
 PAIR_CASES = [
     (2, 4, 2, 700, 128),    # GQA, 6 tiles, ragged tail of 60 rows
     (1, 2, 2, 1024, 128),   # 8 tiles
     (1, 1, 1, 520, 128),    # 5 tiles (odd), ragged tail of 8 rows
+    (1, 3, 1, 1000, 64),    # d = 64 (A waves own the dQ blocks), GQA 3:1, ragged tail
+    (2, 2, 2, 640, 64),     # d = 64, 5 tiles
 ]
 
 

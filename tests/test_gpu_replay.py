@@ -113,12 +113,14 @@ def test_ordered_replay_bitwise(lib, case_args):
                     assert np.array_equal(got, want[ok]), (sched, bh, stp, blk)
 
 
-# d = 128 with 128-row tiles: both main kernels, selected explicitly (1: one wave per
-# SIMD, 2: two waves per SIMD, the default there).
+# 128-row tiles: both main kernels, selected explicitly (1: one wave per SIMD, 2: two
+# waves per SIMD, the default there).
 PAIR_CASES = [
     (1, 4, 2, 512, 128, True),
     (1, 2, 2, 700, 128, False),  # ragged: rows 700..767 past N
     (1, 2, 2, 640, 128, True),   # 5 tiles
+    (1, 4, 2, 1000, 64, True),   # d = 64: the A waves reduce all four dQ blocks of a step
+    (2, 2, 1, 512, 64, False),
 ]
 
 
