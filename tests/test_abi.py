@@ -135,3 +135,31 @@ def test_forward_argument_errors_before_any_launch(kw, status):
 def test_empty_inputs_are_a_no_op():
     assert _call(B=0, q=None, ws=None) == dash.DASH_OK
     assert _call(N=0, q=None, ws=None) == dash.DASH_OK
+
+
+def test_kernel_selection_arguments():
+    """dash_set_kernel accepts the three documented values and rejects others; the
+    setting is library-wide and is restored here to the default."""
+    try:
+        for k in ("one_wave", "two_waves", "auto"):
+            assert dash.dash_set_kernel(k) == dash.DASH_OK
+        for bad in (-1, 3, 99):
+            assert dash.dash_set_kernel(bad) == dash.DASH_ERR_INVALID_ARG
+    finally:
+        dash.dash_set_kernel("auto")
+
+
+def test_schedule_model_arguments():
+    """The host-only model calls check their arguments like the table export."""
+    assert dash.dash_schedule_resolve(1, 2, 2, 256, 64, "full", "shift", 1, 4) == 2
+    assert dash.dash_schedule_resolve(1, 3, 2, 256, 64, "full", "auto", 1, 4) == dash.DASH_ERR_INVALID_ARG
+    assert dash.dash_schedule_resolve(1, 2, 2, 256, 64, "causal", "shift", 1, 4) == dash.DASH_ERR_UNSUPPORTED
+    assert dash.dash_schedule_resolve(1, 2, 2, 256, 64, "full", "auto", 1, 0) == dash.DASH_ERR_INVALID_ARG
+    lib = dash.load()
+    import ctypes
+    out = ctypes.c_double(0.0)
+    assert lib.dash_schedule_makespan(1, 2, 2, 256, 0, 2, 1, 4, 1.0, 0.0, 0.0, None) == dash.DASH_ERR_INVALID_ARG
+    assert lib.dash_schedule_makespan(1, 2, 2, 256, 0, 2, 1, 4, 1.0, 0.0, -1.0, ctypes.byref(out)) == \
+        dash.DASH_ERR_INVALID_ARG
+    assert lib.dash_schedule_makespan(1, 2, 2, 256, 0, 2, 1, 4, 1.0, 0.0, 0.0, ctypes.byref(out)) == dash.DASH_OK
+    assert out.value == 2 * 4 * 1.0  # shift: m n (c + r) with m = 2 heads on n = 4 lanes, r = 0
