@@ -69,12 +69,12 @@ int resolve_schedule(int schedule, int N, int mask) {
 // Costs of one task (one KV tile against one Q tile) on MI355X for the hardware-aware
 // schedule model (DASH paper, section 3.1 model; section 4.2 local vs remote L2
 // segments), in microseconds, measured with the library's kernels:
-//  - d = 128, 128-row tiles: C2 (B=8, H=16, N=2048) main kernel at 828 TFLOP/s with the
+//  - d = 128, 128-row tiles: full mask, B=8, H=16, N=2048: main kernel at 828 TFLOP/s with the
 //    ordered reduction and 960 TFLOP/s with the reduction's memory traffic removed, over
 //    256 CUs and 20.97 MFLOP per task: c = 5.6, r_local = 0.9;
-//  - d = 64: C3 (B=4, H=32, N=4096, causal) main kernel 0.962 ms for 264 tasks per CU,
+//  - d = 64: causal mask, B=4, H=32, N=4096: main kernel 0.962 ms for 264 tasks per CU,
 //    split in the same proportion: c = 3.2, r_local = 0.45;
-//  - r_remote: dQ chains across XCDs (C4, B=1, H=16, N=16384, causal, symmetric shift)
+//  - r_remote: dQ chains across XCDs (causal mask, B=1, H=16, N=16384, d=128, symmetric shift)
 //    ran at 49.7 TFLOPS against 853.7 inside one XCD, 104 us instead of 6.1 us per task:
 //    r_remote = 98, independent of d (an L2 write-back and invalidate per step).
 // 64-row tiles (N < 512) do a quarter of the contraction work and half of the dQ

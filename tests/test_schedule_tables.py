@@ -118,7 +118,7 @@ def test_ragged_and_empty():
 
 @pytest.mark.parametrize("schedule,lanes", [("sym_shift", 64), ("naive", 128), ("descending", 128)])
 def test_spread_placement_of_the_long_causal_head(schedule, lanes):
-    """C4 (n = 128 KV tiles per head): with the spread placement a head's group takes one
+    """Causal, B=1, H=16, N=16384 (n = 128 KV tiles per head): with the spread placement a head's group takes one
     CU per lane over several XCDs (the paper's n-SM layout), its chains cross XCDs, and
     the table stays valid; the symmetric shift still reaches the work bound (each CU then
     runs its single lane for every unit of its group: 16 units over 4 groups of 64 CUs).
