@@ -185,6 +185,26 @@ int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
                         int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local);
 
+/* Variable-length batches (the paper's workloads pack sequences of different lengths
+ * into one batch; section 4.1 benchmarks one length at a time). Same call as
+ * dash_attn_bwd on the padded layout: q, o, dO, dq [B,H,N,d], k, v, dk, dv [B,Hkv,N,d],
+ * lse [B,H,N], where batch b holds seqlens[b] rows (a HOST array of B ints, 1 <=
+ * seqlens[b] <= N; N is the padded length and the row stride). Batch b's backward is
+ * exactly the attention backward of its first seqlens[b] rows (causal: top-left
+ * aligned within the batch); rows at or past seqlens[b] of dq, dk and dv are left
+ * unchanged, and those rows of the inputs are never read as data. The schedule applies
+ * per batch (DASH_SCHED_AUTO: the model's choice at each batch's length).
+ * Supported: N >= 512 (128-row tiles), deterministic = 0 or 1, and the
+ * two-waves-per-SIMD kernel (DASH_KERNEL_AUTO or DASH_KERNEL_TWO_WAVES_PER_SIMD);
+ * otherwise DASH_ERR_UNSUPPORTED. The workspace is dash_attn_bwd_workspace_size(B, H,
+ * Hkv, N, d). Errors: as dash_attn_bwd, and DASH_ERR_INVALID_ARG for a null seqlens or
+ * a length outside [1, N]; symmetric shift needs an even tile count in every batch. */
+int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                         const float* lse, void* dq, void* dk, void* dv,
+                         int B, int H, int Hkv, int N, int d, const int* seqlens,
+                         float softmax_scale, int mask, int schedule, int deterministic,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Hardware-aware schedule model (DASH paper, section 3.1 "Graph Construction": every
  * task is a compute edge c then a reduction edge r on its CU, the reductions into one dQ
  * tile follow each other in rank order; section 4.2: synchronising through a remote L2

@@ -34,9 +34,14 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 #pragma unroll
     for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, LPR);
     if (part == 0) {
-      const int64_t out = (row / p.N) * p.row_stride + row % p.N;
-      p.neg_delta[out] = -acc;
-      p.nlse2[out] = -p.lse[row] * 1.4426950408889634f;
+      const int64_t bh = row / p.N;
+      const int r = static_cast<int>(row % p.N);
+      const int64_t out = bh * p.row_stride + r;
+      // Variable-length batches: rows past the batch's length are padding, like rows
+      // past N (their inputs are never read as data).
+      const bool valid = !p.seqlens || r < p.seqlens[bh / p.H];
+      p.neg_delta[out] = valid ? -acc : 0.f;
+      p.nlse2[out] = valid ? -p.lse[row] * 1.4426950408889634f : -__builtin_inff();
     }
   }
   // Rows past N (up to the tile boundary): P = exp2(S * c - inf) = 0 there, dS = 0.
@@ -66,7 +71,8 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 // and in the shift schedules every step of one CU holds up the steps that wait for it.)
 template <int D>
 __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                             int N, int row_stride, float scale) {
+                                                             int N, int row_stride, float scale,
+                                                             const int* __restrict__ seqlens, int H) {
   constexpr int DB = D / 32;
   constexpr int LROW = D + 8;  // bf16 per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) bf16 tile[32 * LROW];
@@ -90,7 +96,10 @@ __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __rest
   }
   __syncthreads();
   constexpr int CPR = D / 8;  // 16-byte chunks per row
-  const int r_end = N - 32 * qblk < 32 ? N - 32 * qblk : 32;
+  // Rows < N (variable-length batches: < the batch's length) are written; rows past it
+  // are left as they are.
+  const int nb = seqlens ? seqlens[bh / H] : N;
+  const int r_end = nb - 32 * qblk < 32 ? nb - 32 * qblk : 32;
 #pragma unroll
   for (int k = 0; k < 32 * CPR / 256; ++k) {
     const int c = threadIdx.x + 256 * k;
@@ -105,7 +114,8 @@ __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __rest
 // dQ = bf16(s * dQacc), for the atomic variant; the accumulator is row-major with
 // row_stride rows per head, of which the first N are output.
 __global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
-                                                      int64_t quads, int N, int row_stride, int d, float scale) {
+                                                      int64_t quads, int N, int row_stride, int d, float scale,
+                                                      const int* __restrict__ seqlens, int H) {
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int qpr = d / 4;  // float4 per row
@@ -114,6 +124,7 @@ __global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ 
     const int col = static_cast<int>(x % qpr) * 4;
     const int64_t bh = row_all / N;
     const int row = static_cast<int>(row_all % N);
+    if (seqlens && row >= seqlens[bh / H]) continue;  // padding of a shorter batch: left as it is
     const floatx4 a = *reinterpret_cast<const floatx4*>(acc + (bh * row_stride + row) * d + col);
     bf16x4 r;
 #pragma unroll
@@ -139,26 +150,26 @@ hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t 
 }
 
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                          hipStream_t stream) {
+                          hipStream_t stream, const int* seqlens, int H) {
   const int64_t quads = heads * N * (d / 4);
   int64_t grid = (quads + 255) / 256;
   grid = grid < 1 ? 1 : (grid > 8192 ? 8192 : grid);
   hipLaunchKernelGGL(dq_cast_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
-                     reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale);
+                     reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale, seqlens, H);
   return hipGetLastError();
 }
 
 hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                                 hipStream_t stream) {
+                                 hipStream_t stream, const int* seqlens, int H) {
   const int64_t grid = heads * (row_stride / 32);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (d == 64) {
     hipLaunchKernelGGL(dq_cast_blocks_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
-                       reinterpret_cast<bf16*>(dq), N, row_stride, scale);
+                       reinterpret_cast<bf16*>(dq), N, row_stride, scale, seqlens, H);
   } else if (d == 128) {
     hipLaunchKernelGGL(dq_cast_blocks_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
-                       reinterpret_cast<bf16*>(dq), N, row_stride, scale);
+                       reinterpret_cast<bf16*>(dq), N, row_stride, scale, seqlens, H);
   } else {
     return hipErrorInvalidValue;
   }

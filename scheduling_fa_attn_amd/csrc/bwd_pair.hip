@@ -118,6 +118,10 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
   const int nb = (lane >> 4) & 1;
   PROF_DECL
   const int H = p.H, Hkv = p.Hkv, N = p.N;
+  // Rows of batch b: N, or seqlens[b] <= N for variable-length batches (N stays the row
+  // stride of every tensor; rows past a batch's length are padding, never read as data).
+  const CONST_AS int* seqlens = (const CONST_AS int*)p.seqlens;
+  auto len_of = [&](int b) __attribute__((always_inline)) { return p.seqlens ? seqlens[b] : N; };
   bool failed = false;  // this wave gave up waiting (error reported); it keeps going without reducing
   const CONST_AS int* worker_begin = (const CONST_AS int*)p.worker_begin;
   const CONST_AS Quad* items = (const CONST_AS Quad*)p.items;
@@ -156,25 +160,27 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     const Quad item2 = load_quad(items, it2);
     const int64_t bg2 = static_cast<int64_t>(item2.x) * Hkv + item2.y;
     const int kv02 = item2.z * BC;
+    const int nb2 = len_of(item2.x);
     TileCopy<D, BC, 4> kcopy;
     kcopy.init(pr, opaque_lane());
-    kcopy.issue(sK, p.k + bg2 * N * D, kv02, N, pr);
+    kcopy.issue(sK, p.k + bg2 * N * D, kv02, nb2, pr);
     TileCopy<D, BQ, 4> qcopy;
     qcopy.init(pr, opaque_lane());
 #pragma unroll
     for (int hh = 0; hh < BC / BQ; ++hh)
-      qcopy.issue(smem + (hh == 0 ? C::OFF_Q : C::OFF_DO) + (par0 ^ 1) * C::QT, p.v + bg2 * N * D, kv02 + BQ * hh, N,
-                  pr);
+      qcopy.issue(smem + (hh == 0 ? C::OFF_Q : C::OFF_DO) + (par0 ^ 1) * C::QT, p.v + bg2 * N * D, kv02 + BQ * hh,
+                  nb2, pr);
   };
   auto issue_first_step = [&](int it2, int par0) __attribute__((always_inline)) {
     const Quad item2 = load_quad(items, it2);
     const Quad task = load_quad(tasks, item2.w);
     const int q0 = task.y * BC;
     const int64_t bh = static_cast<int64_t>(item2.x) * H + task.x;
+    const int nb2 = len_of(item2.x);
     TileCopy<D, BQ, 4> qcopy;
     qcopy.init(pr, opaque_lane());
-    qcopy.issue(smem + C::OFF_Q + par0 * C::QT, p.q + bh * N * D, q0, N, pr);
-    qcopy.issue(smem + C::OFF_DO + par0 * C::QT, p.dO + bh * N * D, q0, N, pr);
+    qcopy.issue(smem + C::OFF_Q + par0 * C::QT, p.q + bh * N * D, q0, nb2, pr);
+    qcopy.issue(smem + C::OFF_DO + par0 * C::QT, p.dO + bh * N * D, q0, nb2, pr);
     if (pr == 0) dma4(p.nlse2 + bh * p.row_stride + q0, row_lane, smem + C::OFF_NL + par0 * 256);
     if (pr == 1) dma4(p.neg_delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + par0 * 256);
   };
@@ -199,16 +205,17 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     const int n_steps = (t_end - t_begin) * SUBS;
     const int kv0 = kv_tile * BC;
     const int64_t bg = static_cast<int64_t>(item.x) * Hkv + item.y;
+    const int nb = len_of(item.x);  // rows of this item's batch
     const bool has_next = it + 1 < it_end;
 
     // Item prologue: the item's tiles have landed; the K (A) or V (B) rows of the pair
     // and K^T of this wave's dQ d block to AGPRs; accumulator zeroed.
     wait_mem_done();
     __syncthreads();
-    if (kv0 + BC > N) {
-      // Ragged KV tile: K rows past N become zero, so that dS of those columns adds
-      // nothing to dQ; their dK/dV rows are never stored.
-      const int r0 = N - kv0;
+    if (kv0 + BC > nb) {
+      // Ragged KV tile: K rows past the batch's length become zero, so that dS of those
+      // columns adds nothing to dQ; their dK/dV rows are never stored.
+      const int r0 = nb - kv0;
       LDS_AS floatx4* z = reinterpret_cast<LDS_AS floatx4*>(sK + r0 * ST);
       for (int x = tid; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
@@ -426,6 +433,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       constexpr int kCopyOps = kPW + 1;
       const int q0_n = rec_nxt.y;
       const int64_t bh_n = rec_nxt.x;
+      const int nb_n = p.seqlens ? seqlens[rec_nxt.x / H] : N;  // rows of the next step's batch
       auto copy_op = [&](int o, int lane_op) __attribute__((always_inline)) {
         if (o < kPW) {
           const int blk = pr + 4 * o;
@@ -436,7 +444,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
             int c = slot - r * SPR;
             c = c < TileGeom<D>::CPR ? c : 0;
             int row = q0_n + r;
-            row = row < N - 1 ? row : N - 1;
+            row = row < nb_n - 1 ? row : nb_n - 1;
             dma16((roleA ? p.q : p.dO) + bh_n * N * D, static_cast<unsigned>(row * (2 * D) + 16 * c),
                   smem + (roleA ? C::OFF_Q : C::OFF_DO) + (buf ^ 1) * C::QT + blk * 1024);
           }
@@ -782,7 +790,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         const int chunk = lane + 64 * k, row = chunk >> 3, c16 = chunk & 7;
         const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(stage + row * sst + 16 * c16);
         const int kvr = kv0 + 32 * pr + row;
-        if (kvr < N) *reinterpret_cast<u32x4*>(g + static_cast<int64_t>(kvr) * D + 64 * half + 8 * c16) = v;
+        if (kvr < nb) *reinterpret_cast<u32x4*>(g + static_cast<int64_t>(kvr) * D + 64 * half + 8 * c16) = v;
       }
     }
     PROF_MARK(kProfEpi);

@@ -153,6 +153,7 @@ struct DevTable {
   const int4* items = nullptr;
   const int4* tasks = nullptr;
   const int4* steps = nullptr;
+  const int* seqlens = nullptr;  // variable-length tables: the batch lengths
   int workers = 0;
   int tile = 0;
   bool xcd_local = true;
@@ -167,6 +168,7 @@ struct DeviceState {
   int* err = nullptr;
   long long ticks_per_second = 100000000LL;
   std::map<std::tuple<int, int, int, int, int, int, int, int>, DevTable> tables;
+  std::map<std::vector<int>, DevTable> varlen_tables;  // variable-length batches
 };
 
 std::mutex g_mu;
@@ -250,6 +252,8 @@ int get_device(DeviceState** out) {
   return DASH_OK;
 }
 
+int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* lens, DevTable* out);
+
 int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int schedule, const DevTable** out) {
   const int tile = tile_for(N);
   auto key = std::make_tuple(B, H, Hkv, N, tile, causal ? 1 : 0, schedule, g_placement);
@@ -273,6 +277,16 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   std::string err;
   const int s = dash::build_table(sp, &t, &err);
   if (s != 0) return s;
+  DevTable dt;
+  const int u = upload_table(t, H, tile, nullptr, &dt);
+  if (u != DASH_OK) return u;
+  auto ins = st->tables.emplace(key, dt);
+  *out = &ins.first->second;
+  return DASH_OK;
+}
+
+// Device copy of a table: worker_begin | items | tasks | step records | batch lengths.
+int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* lens, DevTable* out) {
   const size_t wb_bytes = align256(sizeof(int32_t) * t.worker_begin.size());
   const size_t it_bytes = align256(sizeof(dash::Item) * t.items.size());
   const size_t tk_bytes = align256(sizeof(dash::Task) * (t.tasks.size() + 1));
@@ -292,7 +306,9 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   steps.push_back(int4{0, 0, 0, 0});
   steps.push_back(int4{0, 0, 0, 0});
   const size_t st_bytes = align256(sizeof(int4) * steps.size());
-  std::vector<char> host(wb_bytes + it_bytes + tk_bytes + st_bytes, 0);
+  const size_t ln_bytes = lens ? align256(sizeof(int) * lens->size()) : 0;
+  std::vector<char> host(wb_bytes + it_bytes + tk_bytes + st_bytes + ln_bytes, 0);
+  if (lens) std::memcpy(host.data() + wb_bytes + it_bytes + tk_bytes + st_bytes, lens->data(), sizeof(int) * lens->size());
   std::memcpy(host.data(), t.worker_begin.data(), sizeof(int32_t) * t.worker_begin.size());
   std::memcpy(host.data() + wb_bytes, t.items.data(), sizeof(dash::Item) * t.items.size());
   if (!t.tasks.empty())
@@ -309,10 +325,45 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   dt.items = reinterpret_cast<const int4*>(base + wb_bytes);
   dt.tasks = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes);
   dt.steps = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes + tk_bytes);
+  dt.seqlens = lens ? reinterpret_cast<const int*>(base + wb_bytes + it_bytes + tk_bytes + st_bytes) : nullptr;
   dt.workers = t.workers;
   dt.tile = tile;
   dt.xcd_local = t.xcd_local;
-  auto ins = st->tables.emplace(key, dt);
+  *out = dt;
+  return DASH_OK;
+}
+
+// Variable-length batches: the table of dash::build_table_varlen, cached per lengths.
+int get_table_varlen(DeviceState* st, int B, int H, int Hkv, int N, bool causal, const std::vector<int>& lens,
+                     const std::vector<int>& scheds, const DevTable** out) {
+  std::vector<int> key = {B, H, Hkv, N, causal ? 1 : 0, g_placement};
+  key.insert(key.end(), lens.begin(), lens.end());
+  key.insert(key.end(), scheds.begin(), scheds.end());
+  auto found = st->varlen_tables.find(key);
+  if (found != st->varlen_tables.end()) {
+    *out = &found->second;
+    return DASH_OK;
+  }
+  dash::SchedParams sp;
+  sp.B = B;
+  sp.H = H;
+  sp.Hkv = Hkv;
+  sp.N = N;
+  sp.tile = tile_for(N);
+  sp.causal = causal;
+  sp.num_xcd = st->num_xcd;
+  sp.cus_per_xcd = st->cus_per_xcd;
+  sp.spread = g_placement == DASH_PLACEMENT_SPREAD;
+  std::vector<Sched> kinds;
+  for (int x : scheds) kinds.push_back(static_cast<Sched>(x));
+  dash::Table t;
+  std::string err;
+  const int s = dash::build_table_varlen(sp, lens, kinds, &t, &err);
+  if (s != 0) return s < 0 ? DASH_ERR_INVALID_ARG : s;
+  DevTable dt;
+  const int u = upload_table(t, H, sp.tile, &lens, &dt);
+  if (u != DASH_OK) return u;
+  auto ins = st->varlen_tables.emplace(key, dt);
   *out = &ins.first->second;
   return DASH_OK;
 }
@@ -322,12 +373,34 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
             void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int mask, int schedule,
             int deterministic, void* workspace, size_t workspace_bytes, void* stream_ptr, void* ev_start,
-            void* ev_stop) {
+            void* ev_stop, const int* seqlens = nullptr) {
   const int requested = schedule;
   schedule = resolve_schedule(schedule, N, mask);
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
   if (deterministic < 0 || deterministic > 2) return DASH_ERR_INVALID_ARG;
+  // Variable-length batches: lengths in [1, N]; 128-row tiles, the two-waves kernel and
+  // the ordered or atomic reduction only.
+  std::vector<int> lens, scheds;
+  if (seqlens && B > 0 && N > 0) {
+    for (int b = 0; b < B; ++b) {
+      if (seqlens[b] < 1 || seqlens[b] > N) return DASH_ERR_INVALID_ARG;
+      lens.push_back(seqlens[b]);
+    }
+    if (tile_for(N) != 128 || deterministic == 2) return DASH_ERR_UNSUPPORTED;
+    for (int b = 0; b < B; ++b) {
+      int sb = requested;
+      if (sb != DASH_SCHED_AUTO) {
+        const int c = check_sizes(1, H, Hkv, lens[b] < 512 ? 512 : lens[b], d, mask, sb);
+        // (the batch's tiles are 128 rows even where its own length is below 512)
+        if (c != DASH_OK) return c;
+        if (sb == DASH_SCHED_SYM_SHIFT && cdiv(lens[b], 128) % 2) return DASH_ERR_UNSUPPORTED;
+      }
+      scheds.push_back(sb);
+    }
+    std::lock_guard<std::mutex> lock(g_mu);
+    if (g_kernel == DASH_KERNEL_ONE_WAVE_PER_SIMD) return DASH_ERR_UNSUPPORTED;
+  }
   if (!(scale > 0.f) || !std::isfinite(scale)) return DASH_ERR_INVALID_ARG;
   if (B == 0 || N == 0) return DASH_OK;
   const void* ptrs[] = {q, k, v, o, dO, dq, dk, dv};
@@ -357,7 +430,26 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
       }
       schedule = it->second;
     }
-    s = get_table(st, B, H, Hkv, N, causal, schedule, &tab);
+    if (seqlens) {
+      // AUTO per batch: the model's choice at the batch's own length (cached like AUTO).
+      for (int b = 0; b < B; ++b) {
+        if (scheds[b] != DASH_SCHED_AUTO) continue;
+        const int nb = lens[b] < 512 ? 512 : lens[b];
+        const auto key = std::make_tuple(1, H, Hkv, nb, d, mask, st->num_xcd, st->cus_per_xcd, g_placement);
+        auto it = g_auto.find(key);
+        if (it == g_auto.end()) {
+          const int r = model_schedule(1, H, Hkv, nb, d, mask, st->num_xcd, st->cus_per_xcd,
+                                       g_placement == DASH_PLACEMENT_SPREAD);
+          if (r < 0) return r;
+          it = g_auto.emplace(key, r).first;
+        }
+        scheds[b] = it->second;
+        if (scheds[b] == DASH_SCHED_SYM_SHIFT && cdiv(lens[b], 128) % 2) scheds[b] = DASH_SCHED_DESCENDING;
+      }
+      s = get_table_varlen(st, B, H, Hkv, N, causal, lens, scheds, &tab);
+    } else {
+      s = get_table(st, B, H, Hkv, N, causal, schedule, &tab);
+    }
     if (s != DASH_OK) return s;
   }
   char* ws = static_cast<char*>(workspace);
@@ -380,6 +472,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   pp.sem_count = int64_t(B) * H * L.sem_stride;
   pp.ctr = ctr;
   pp.ctr_count = kCtrInts;
+  pp.seqlens = tab->seqlens;
+  pp.H = H;
   pp.dqacc_zero = deterministic == 0 ? dqacc : nullptr;
   pp.zero_count = int64_t(B) * H * L.row_stride * d;
   const int64_t pre_threads = pp.rows * (d / 8);
@@ -420,6 +514,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.prof = g_prof;
   bp.replay = nullptr;
   bp.replay_ranks = 0;
+  bp.seqlens = tab->seqlens;
 #ifdef DASH_REPLAY
   if (g_replay && deterministic) {
     const int tile = tile_for(N);
@@ -442,6 +537,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   const bool pair_ok = tab->tile == 128 && deterministic != 2 && (deterministic == 0 || bp.xcd_local ||
                        st->num_xcd == 1);
   const bool use_pair = pair_ok && (kernel == DASH_KERNEL_TWO_WAVES_PER_SIMD || (kernel == DASH_KERNEL_AUTO && kPairAuto));
+  if (tab->seqlens && !use_pair) return DASH_ERR_UNSUPPORTED;  // (the one-wave kernel has no per-batch lengths)
   hipError_t e = !use_pair ? dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream)
                  : d == 128 ? dash::launch_pair_d128(bp, tab->workers, stream)
                             : dash::launch_pair_d64(bp, tab->workers, stream);
@@ -469,9 +565,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     dp.scale_log2 = scale * 1.4426950408889634f;
     ec = dash::launch_dq_pass(dp, d, stream);
   } else if (deterministic == 1) {
-    ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream);
+    ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream, tab->seqlens, H);
   } else {
-    ec = dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream);
+    ec = dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream, tab->seqlens, H);
   }
   if (ec != hipSuccess) return DASH_ERR_HIP;
   return DASH_OK;
@@ -523,6 +619,15 @@ int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o, co
                   int schedule, int deterministic, void* workspace, size_t workspace_bytes, void* stream) {
   return run_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, softmax_scale, mask, schedule, deterministic,
                  workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                         const int* seqlens, float softmax_scale, int mask, int schedule, int deterministic,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  if (seqlens == nullptr && B > 0) return DASH_ERR_INVALID_ARG;
+  return run_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, softmax_scale, mask, schedule, deterministic,
+                 workspace, workspace_bytes, stream, nullptr, nullptr, seqlens);
 }
 
 int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,

@@ -25,6 +25,8 @@ struct PreParams {
   int64_t ctr_count;
   float* dqacc_zero;   // non-null: clear this fp32 buffer (atomic variant)
   int64_t zero_count;  // elements, multiple of 4
+  const int* seqlens;  // non-null: rows of batch b at or past seqlens[b] are padding
+  int H;               // query heads (batch of a row = row / N / H)
 };
 
 struct BwdParams {
@@ -58,6 +60,7 @@ struct BwdParams {
   unsigned long long* prof; // profiling builds (DASH_PROFILE): per-wave phase cycle counters, or null
   float* replay;            // replay builds (DASH_REPLAY): dump of every ordered dQ partial, or null
   int replay_ranks;         // replay builds: rank slots per dQ block in the dump (KV tiles per head)
+  const int* seqlens;       // non-null: batch b has seqlens[b] rows (<= N, the row stride of q, k, ...)
 };
 
 // Forward kernel (O and the natural-log LSE from Q, K, V).
@@ -152,10 +155,10 @@ inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hip
 hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t stream);
 // dQ = bf16(scale * dqacc) for rows < N, from the ordered variant's block layout.
 hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                                 hipStream_t stream);
+                                 hipStream_t stream, const int* seqlens = nullptr, int H = 1);
 // dQ = bf16(scale * dqacc) for rows < N, from the atomic variant's row-major layout.
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                          hipStream_t stream);
+                          hipStream_t stream, const int* seqlens = nullptr, int H = 1);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& prm, int d, hipStream_t stream);
 hipError_t launch_dq_pass(const DqParams& prm, int d, hipStream_t stream);

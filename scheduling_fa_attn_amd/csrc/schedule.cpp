@@ -200,6 +200,59 @@ int build_table(const SchedParams& p, Table* out, std::string* err) {
   return 0;
 }
 
+int build_table_varlen(const SchedParams& p, const std::vector<int>& lens, const std::vector<Sched>& kinds,
+                       Table* out, std::string* err) {
+  if (static_cast<int>(lens.size()) != p.B || static_cast<int>(kinds.size()) != p.B) {
+    *err = "one length and one schedule per batch";
+    return -1;
+  }
+  std::vector<Table> parts(p.B);
+  for (int b = 0; b < p.B; ++b) {
+    if (lens[b] < 1 || lens[b] > p.N) {
+      *err = "batch length outside [1, N]";
+      return -1;
+    }
+    SchedParams q = p;
+    q.B = 1;
+    q.N = lens[b];
+    q.kind = kinds[b];
+    const int s = build_table(q, &parts[b], err);
+    if (s != 0) return s;
+  }
+  Table t;
+  t.workers = p.num_xcd * p.cus_per_xcd;
+  t.tile = p.tile;
+  t.n = tiles_per_head(p.N, p.tile);
+  t.xcd_local = true;
+  for (const Table& q : parts) t.xcd_local = t.xcd_local && q.xcd_local;
+  t.worker_begin.push_back(0);
+  for (int w = 0; w < t.workers; ++w) {
+    for (int b = 0; b < p.B; ++b) {
+      const Table& q = parts[b];
+      if (q.workers != t.workers) {
+        *err = "tables of different topologies";
+        return -1;
+      }
+      for (int x = q.worker_begin[w]; x < q.worker_begin[w + 1]; ++x) {
+        Item it = q.items[x];
+        const int t0 = it.t0, t1 = q.items[x + 1].t0;
+        it.b = b;
+        it.t0 = static_cast<int32_t>(t.tasks.size());
+        t.items.push_back(it);
+        for (int k = t0; k < t1; ++k) {
+          t.tasks.push_back(q.tasks[k]);
+          t.task_worker.push_back(w);
+          t.task_item.push_back(static_cast<int32_t>(t.items.size() - 1));
+        }
+      }
+    }
+    t.worker_begin.push_back(static_cast<int32_t>(t.items.size()));
+  }
+  t.items.push_back(Item{0, 0, 0, static_cast<int32_t>(t.tasks.size())});
+  *out = std::move(t);
+  return 0;
+}
+
 bool table_makespan(const Table& t, int cus_per_xcd, const CostModel& m, double* makespan) {
   const size_t nt = t.tasks.size();
   // Predecessor of every task on its CU and in its dQ tile's reduction order (-1: none).

@@ -57,6 +57,15 @@ inline int tiles_per_head(int N, int tile) { return (N + tile - 1) / tile; }
 // Builds the table. Returns 0 on success, or a dash_status code with a message in *err.
 int build_table(const SchedParams& p, Table* out, std::string* err);
 
+// Variable-length batches: batch b has lens[b] rows (1 <= lens[b] <= p.N) and runs
+// schedule kinds[b]. Each batch's table is built as for B = 1 at its own length on the
+// whole topology, and every worker runs its items of batch 0, then of batch 1, and so on.
+// The reduction chains of different batches never meet, and a worker's batches follow
+// each other in one order on every worker, so the merged table is as deadlock-free as
+// its parts. Returns 0 or a dash_status code with a message in *err.
+int build_table_varlen(const SchedParams& p, const std::vector<int>& lens, const std::vector<Sched>& kinds,
+                       Table* out, std::string* err);
+
 // Cost model of a table (DASH paper, section 3.1, "Graph Construction"): every task is
 // a compute edge c followed by a reduction edge r on its CU; a CU runs its tasks back
 // to back; the reductions into one dQ tile follow each other in rank order (zero-weight

@@ -30,6 +30,7 @@ EXPORTED = (
     "dash_attn_bwd_workspace_size",
     "dash_attn_bwd",
     "dash_attn_bwd_timed",
+    "dash_attn_bwd_varlen",
     "dash_last_kernel_error",
     "dash_status_string",
     "dash_tile_size",
@@ -74,6 +75,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_attn_bwd.restype = i
     lib.dash_attn_bwd_timed.argtypes = common + [vp, vp]
     lib.dash_attn_bwd_timed.restype = i
+    lib.dash_attn_bwd_varlen.argtypes = common[:14] + [ctypes.POINTER(ctypes.c_int)] + common[14:]
+    lib.dash_attn_bwd_varlen.restype = i
     lib.dash_last_kernel_error.argtypes = []
     lib.dash_last_kernel_error.restype = i
     lib.dash_status_string.argtypes = [i]
@@ -219,3 +222,21 @@ def dash_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, softmax_scale, mask, schedule
         return int(lib.dash_attn_bwd_timed(*args, ctypes.c_void_p(main_start or 0),
                                            ctypes.c_void_p(main_stop or 0)))
     return int(lib.dash_attn_bwd(*args))
+
+
+def dash_attn_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, seqlens, softmax_scale, mask, schedule, deterministic,
+                         workspace, stream=None, lib=None) -> int:
+    """Call dash_attn_bwd_varlen on torch device tensors in the padded layout ([B, H, N, d]
+    etc., N the padded length); seqlens: B host ints, batch b's rows. Returns the status."""
+    import torch
+
+    lib = lib or load()
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    lens = (ctypes.c_int * max(len(seqlens), 1))(*[int(x) for x in seqlens])
+    return int(lib.dash_attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                        _ptr(dv), B, H, Hkv, N, d, lens, float(softmax_scale), MASKS.get(mask, mask),
+                                        SCHEDULES.get(schedule, schedule), int(deterministic), _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), ctypes.c_void_p(stream)))
