@@ -205,6 +205,13 @@ int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void
                          float softmax_scale, int mask, int schedule, int deterministic,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* Host-only export of the table dash_attn_bwd_varlen runs for these batch lengths
+ * (seqlens: B host ints in [1, N]; N >= 512), in the records of dash_schedule_table;
+ * DASH_SCHED_AUTO resolves per batch as in dash_attn_bwd_varlen with d = 128. */
+int dash_schedule_table_varlen(int B, int H, int Hkv, int N, const int* seqlens, int mask, int schedule,
+                               int num_xcd, int cus_per_xcd,
+                               int* records, long long capacity, long long* count, int* xcd_local);
+
 /* Hardware-aware schedule model (DASH paper, section 3.1 "Graph Construction": every
  * task is a compute edge c then a reduction edge r on its CU, the reductions into one dQ
  * tile follow each other in rank order; section 4.2: synchronising through a remote L2

@@ -760,6 +760,64 @@ int dash_schedule_makespan(int B, int H, int Hkv, int N, int mask, int schedule,
   return DASH_OK;
 }
 
+int dash_schedule_table_varlen(int B, int H, int Hkv, int N, const int* seqlens, int mask, int schedule, int num_xcd,
+                               int cus_per_xcd, int* records, long long capacity, long long* count, int* xcd_local) {
+  if (seqlens == nullptr || count == nullptr || capacity < 0 || B <= 0) return DASH_ERR_INVALID_ARG;
+  if (num_xcd <= 0 || cus_per_xcd <= 0 || num_xcd > 64 || cus_per_xcd > 4096) return DASH_ERR_INVALID_ARG;
+  if (tile_for(N) != 128) return DASH_ERR_UNSUPPORTED;
+  std::vector<int> lens;
+  std::vector<Sched> kinds;
+  for (int b = 0; b < B; ++b) {
+    if (seqlens[b] < 1 || seqlens[b] > N) return DASH_ERR_INVALID_ARG;
+    lens.push_back(seqlens[b]);
+    const int nb = seqlens[b] < 512 ? 512 : seqlens[b];
+    int sb = schedule;
+    if (sb == DASH_SCHED_AUTO) {
+      sb = dash_schedule_resolve(1, H, Hkv, nb, 128, mask, sb, num_xcd, cus_per_xcd);
+      if (sb < 0) return sb;
+      if (sb == DASH_SCHED_SYM_SHIFT && cdiv(seqlens[b], 128) % 2) sb = DASH_SCHED_DESCENDING;
+    } else {
+      const int c = check_sizes(1, H, Hkv, nb, 128, mask, sb);
+      if (c != DASH_OK) return c;
+      if (sb == DASH_SCHED_SYM_SHIFT && cdiv(seqlens[b], 128) % 2) return DASH_ERR_UNSUPPORTED;
+    }
+    kinds.push_back(static_cast<Sched>(sb));
+  }
+  dash::SchedParams sp;
+  sp.B = B;
+  sp.H = H;
+  sp.Hkv = Hkv;
+  sp.N = N;
+  sp.tile = 128;
+  sp.causal = mask == DASH_MASK_CAUSAL;
+  sp.num_xcd = num_xcd;
+  sp.cus_per_xcd = cus_per_xcd;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    sp.spread = g_placement == DASH_PLACEMENT_SPREAD;
+  }
+  dash::Table t;
+  std::string err;
+  int s = dash::build_table_varlen(sp, lens, kinds, &t, &err);
+  if (s != 0) return s < 0 ? DASH_ERR_INVALID_ARG : s;
+  *count = static_cast<long long>(t.tasks.size());
+  if (xcd_local) *xcd_local = t.xcd_local ? 1 : 0;
+  if (static_cast<long long>(t.tasks.size()) > capacity) return DASH_ERR_WORKSPACE;
+  if (!t.tasks.empty() && records == nullptr) return DASH_ERR_INVALID_ARG;
+  for (size_t x = 0; x < t.tasks.size(); ++x) {
+    const dash::Item& it = t.items[t.task_item[x]];
+    int* r = records + 7 * x;
+    r[0] = t.task_worker[x];
+    r[1] = it.b;
+    r[2] = t.tasks[x].h;
+    r[3] = it.g;
+    r[4] = it.i;
+    r[5] = t.tasks[x].j;
+    r[6] = t.tasks[x].rank;
+  }
+  return DASH_OK;
+}
+
 int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local) {
   if (schedule == DASH_SCHED_AUTO) {

@@ -35,6 +35,7 @@ EXPORTED = (
     "dash_status_string",
     "dash_tile_size",
     "dash_schedule_table",
+    "dash_schedule_table_varlen",
     "dash_schedule_makespan",
     "dash_schedule_resolve",
     "dash_set_placement",
@@ -86,6 +87,10 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_schedule_table.argtypes = [i, i, i, i, i, i, i, i, ctypes.POINTER(ctypes.c_int), ctypes.c_longlong,
                                         ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
     lib.dash_schedule_table.restype = i
+    lib.dash_schedule_table_varlen.argtypes = [i, i, i, i, ctypes.POINTER(ctypes.c_int), i, i, i, i,
+                                               ctypes.POINTER(ctypes.c_int), ctypes.c_longlong,
+                                               ctypes.POINTER(ctypes.c_longlong), ctypes.POINTER(ctypes.c_int)]
+    lib.dash_schedule_table_varlen.restype = i
     lib.dash_schedule_makespan.argtypes = [i, i, i, i, i, i, i, i, ctypes.c_double, ctypes.c_double,
                                            ctypes.c_double, ctypes.POINTER(ctypes.c_double)]
     lib.dash_schedule_makespan.restype = i
@@ -177,6 +182,27 @@ def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):
                                  ctypes.byref(count), ctypes.byref(local))
     if st != DASH_OK:
         raise DashError(st, "dash_schedule_table")
+    return rec[: count.value], bool(local.value)
+
+
+def dash_schedule_table_varlen(B, H, Hkv, N, seqlens, mask, schedule, num_xcd, cus_per_xcd):
+    """Host-only export of a variable-length table: returns (records [T, 7] int32, xcd_local)."""
+    lib = load()
+    m = MASKS.get(mask, mask)
+    s = SCHEDULES.get(schedule, schedule)
+    lens = (ctypes.c_int * max(len(seqlens), 1))(*[int(x) for x in seqlens])
+    count = ctypes.c_longlong(0)
+    local = ctypes.c_int(0)
+    st = lib.dash_schedule_table_varlen(B, H, Hkv, N, lens, m, s, num_xcd, cus_per_xcd, None, 0, ctypes.byref(count),
+                                        ctypes.byref(local))
+    if st not in (DASH_OK, DASH_ERR_WORKSPACE):
+        raise DashError(st, "dash_schedule_table_varlen")
+    rec = np.zeros((max(count.value, 1), 7), dtype=np.int32)
+    st = lib.dash_schedule_table_varlen(B, H, Hkv, N, lens, m, s, num_xcd, cus_per_xcd,
+                                        rec.ctypes.data_as(ctypes.POINTER(ctypes.c_int)), count.value,
+                                        ctypes.byref(count), ctypes.byref(local))
+    if st != DASH_OK:
+        raise DashError(st, "dash_schedule_table_varlen")
     return rec[: count.value], bool(local.value)
 
 

@@ -266,3 +266,47 @@ def test_makespan_rejects_bad_costs():
         dash.dash_schedule_makespan(1, 2, 2, 256, "full", "shift", 1, 4, -1.0, 0.0, 0.0)
     with pytest.raises(dash.DashError):
         dash.dash_schedule_makespan(1, 2, 2, 256, "full", "shift", 1, 4, float("nan"), 0.0, 0.0)
+
+
+# ---------------------------------------------------------------------------------
+# Variable-length batches: one table per batch at its own length, merged per CU.
+# ---------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mask,schedule", [("full", "shift"), ("full", "naive"), ("causal", "descending"),
+                                           ("causal", "auto"), ("full", "auto")])
+def test_varlen_table_is_the_per_batch_tables_merged(mask, schedule):
+    """Each batch's part of the merged table passes the oracle validator at its own tile
+    count (coverage, KV contiguity, rank order, acyclicity); the whole merged DAG is
+    acyclic (the oracle simulator raises on a cycle); every CU runs its batches in order."""
+    B, H, Hkv, N, lens = 3, 4, 2, 2048, (2048, 1100, 512)
+    rec, local = dash.dash_schedule_table_varlen(B, H, Hkv, N, lens, mask, schedule, 8, 32)
+    assert local
+    for b, nb in enumerate(lens):
+        n_b = -(-nb // 128)
+        kind = schedule
+        if kind == "auto":
+            kind = NAMES[dash.dash_schedule_resolve(1, H, Hkv, max(nb, 512), 128, mask, "auto", 8, 32)]
+            if kind == "sym_shift" and n_b % 2:
+                kind = "descending"
+        part = rec[rec[:, 1] == b].copy()
+        part[:, 1] = 0
+        table = to_table(part, 1, H, Hkv, max(nb, 512), mask, kind, 256)
+        table["n"] = n_b
+        osch.validate(table)
+        assert {int(t) for t in part[:, 5]} <= set(range(-(-nb // 128)))
+    full = to_table(rec, B, H, Hkv, N, mask, "naive", 256)
+    assert osch.simulate(full, 1.0, 0.5) > 0
+    for w in range(256):
+        bs = rec[rec[:, 0] == w][:, 1]
+        assert (np.diff(bs) >= 0).all()
+
+
+def test_varlen_table_argument_errors():
+    with pytest.raises(dash.DashError):
+        dash.dash_schedule_table_varlen(2, 2, 2, 1024, (0, 1024), "full", "shift", 8, 32)
+    with pytest.raises(dash.DashError):
+        dash.dash_schedule_table_varlen(2, 2, 2, 1024, (1024, 1025), "full", "shift", 8, 32)
+    with pytest.raises(dash.DashError):
+        dash.dash_schedule_table_varlen(2, 2, 2, 1024, (1024, 384), "causal", "sym_shift", 8, 32)  # 3 tiles
+    with pytest.raises(dash.DashError):
+        dash.dash_schedule_table_varlen(1, 2, 2, 256, (256,), "full", "shift", 8, 32)  # 64-row tiles
