@@ -202,46 +202,118 @@ int build_table(const SchedParams& p, Table* out, std::string* err) {
 
 int build_table_varlen(const SchedParams& p, const std::vector<int>& lens, const std::vector<Sched>& kinds,
                        Table* out, std::string* err) {
-  if (static_cast<int>(lens.size()) != p.B || static_cast<int>(kinds.size()) != p.B) {
+  if (static_cast<int>(lens.size()) != p.B || static_cast<int>(kinds.size()) != p.B || p.B < 1) {
     *err = "one length and one schedule per batch";
     return -1;
   }
-  std::vector<Table> parts(p.B);
   for (int b = 0; b < p.B; ++b) {
     if (lens[b] < 1 || lens[b] > p.N) {
       *err = "batch length outside [1, N]";
       return -1;
     }
+  }
+  const int X = p.num_xcd, S = p.cus_per_xcd;
+  const int workers = X * S;
+  // Up to S batches run side by side: batch b gets a band of width[b] slots in every L2
+  // domain (slots off[b] .. off[b] + width[b] - 1), widths in proportion to the batch's
+  // tasks (at least one slot); its table is built for that band as its whole device, so
+  // its chains stay inside a domain and batches never wait for each other. More batches
+  // than slots share the device: each batch's table is built for the whole device and
+  // every worker runs its items of batch 0, then of batch 1, and so on, batch b's
+  // workers rotated (whole domains and slots within every domain) to even out the task
+  // counts. Reduction chains never cross batches, and in both layouts a worker's batches
+  // follow one fixed order, so the merged table is as deadlock-free as its parts.
+  const bool banded = p.B <= S;
+  std::vector<int> width(p.B, S), off(p.B, 0);
+  if (banded) {
+    std::vector<double> work(p.B);
+    double total = 0.0;
+    for (int b = 0; b < p.B; ++b) {
+      const double n = static_cast<double>(tiles_per_head(lens[b], p.tile));
+      work[b] = p.causal ? n * (n + 1) / 2 : n * n;
+      total += work[b];
+    }
+    int used = 0;
+    std::vector<std::pair<double, int>> rem;
+    for (int b = 0; b < p.B; ++b) {
+      const double share = work[b] / total * (S - p.B);  // one slot each, the rest by share
+      width[b] = 1 + static_cast<int>(share);
+      used += width[b];
+      rem.push_back({share - static_cast<int>(share), b});
+    }
+    std::sort(rem.begin(), rem.end(), [](const std::pair<double, int>& a, const std::pair<double, int>& c) {
+      return a.first > c.first || (a.first == c.first && a.second < c.second);
+    });
+    for (size_t x = 0; used < S && x < rem.size(); ++x, ++used) ++width[rem[x].second];
+    for (int b = 1; b < p.B; ++b) off[b] = off[b - 1] + width[b - 1];
+  }
+  std::vector<Table> parts(p.B);
+  for (int b = 0; b < p.B; ++b) {
     SchedParams q = p;
     q.B = 1;
     q.N = lens[b];
     q.kind = kinds[b];
+    q.cus_per_xcd = width[b];
     const int s = build_table(q, &parts[b], err);
     if (s != 0) return s;
   }
+  // Worker of batch b's table -> device worker: banded, slot s of domain x goes to slot
+  // off[b] + s of domain x; shared, a rotation chosen as described above.
+  std::vector<std::vector<int>> dev_of(p.B);
+  if (banded) {
+    for (int b = 0; b < p.B; ++b) {
+      dev_of[b].resize(X * width[b]);
+      for (int w = 0; w < X * width[b]; ++w) dev_of[b][w] = (w / width[b]) * S + off[b] + w % width[b];
+    }
+  } else {
+    auto rot = [&](int w, int r) { return ((w / S + r / S) % X) * S + (w % S + r % S) % S; };
+    std::vector<int64_t> load(workers, 0);
+    for (int b = 0; b < p.B; ++b) {
+      const Table& q = parts[b];
+      std::vector<int64_t> own(workers, 0);
+      for (int w = 0; w < workers; ++w) own[w] = q.items[q.worker_begin[w + 1]].t0 - q.items[q.worker_begin[w]].t0;
+      int64_t best = -1;
+      int best_r = 0;
+      for (int r = 0; r < workers; ++r) {
+        int64_t mx = 0;
+        for (int w = 0; w < workers; ++w) mx = std::max(mx, load[rot(w, r)] + own[w]);
+        if (best < 0 || mx < best) {
+          best = mx;
+          best_r = r;
+        }
+      }
+      dev_of[b].resize(workers);
+      for (int w = 0; w < workers; ++w) {
+        dev_of[b][w] = rot(w, best_r);
+        load[dev_of[b][w]] += own[w];
+      }
+    }
+  }
+  // Items of every device worker: its batches in order.
+  std::vector<std::vector<std::pair<int, int>>> runs(workers);  // (batch, table worker)
+  for (int b = 0; b < p.B; ++b)
+    for (int w = 0; w < static_cast<int>(dev_of[b].size()); ++w) runs[dev_of[b][w]].push_back({b, w});
   Table t;
-  t.workers = p.num_xcd * p.cus_per_xcd;
+  t.workers = workers;
   t.tile = p.tile;
   t.n = tiles_per_head(p.N, p.tile);
   t.xcd_local = true;
   for (const Table& q : parts) t.xcd_local = t.xcd_local && q.xcd_local;
   t.worker_begin.push_back(0);
-  for (int w = 0; w < t.workers; ++w) {
-    for (int b = 0; b < p.B; ++b) {
-      const Table& q = parts[b];
-      if (q.workers != t.workers) {
-        *err = "tables of different topologies";
-        return -1;
-      }
+  for (int wd = 0; wd < workers; ++wd) {
+    std::sort(runs[wd].begin(), runs[wd].end());
+    for (const auto& bw : runs[wd]) {
+      const Table& q = parts[bw.first];
+      const int w = bw.second;
       for (int x = q.worker_begin[w]; x < q.worker_begin[w + 1]; ++x) {
         Item it = q.items[x];
         const int t0 = it.t0, t1 = q.items[x + 1].t0;
-        it.b = b;
+        it.b = bw.first;
         it.t0 = static_cast<int32_t>(t.tasks.size());
         t.items.push_back(it);
         for (int k = t0; k < t1; ++k) {
           t.tasks.push_back(q.tasks[k]);
-          t.task_worker.push_back(w);
+          t.task_worker.push_back(wd);
           t.task_item.push_back(static_cast<int32_t>(t.items.size() - 1));
         }
       }

@@ -310,3 +310,28 @@ def test_varlen_table_argument_errors():
         dash.dash_schedule_table_varlen(2, 2, 2, 1024, (1024, 384), "causal", "sym_shift", 8, 32)  # 3 tiles
     with pytest.raises(dash.DashError):
         dash.dash_schedule_table_varlen(1, 2, 2, 256, (256,), "full", "shift", 8, 32)  # 64-row tiles
+
+
+@pytest.mark.parametrize("B,topology", [(3, (8, 32)), (6, (2, 4))], ids=["banded", "shared"])
+def test_varlen_layouts_valid(B, topology):
+    """Up to one batch per slot of a domain: batches on disjoint bands of slots (no CU
+    runs two batches); more batches than slots: shared CUs, batches in order. Both merged
+    tables pass the per-batch validator and are acyclic."""
+    X, S = topology
+    H, Hkv, N = 2, 1, 1024
+    lens = [1024, 600, 513, 1000, 777, 512][:B]
+    rec, _ = dash.dash_schedule_table_varlen(B, H, Hkv, N, lens, "causal", "descending", X, S)
+    per_cu = {}
+    for w, b in rec[:, :2].tolist():
+        per_cu.setdefault(w, set()).add(b)
+    if B <= S:
+        assert max(len(v) for v in per_cu.values()) == 1
+    else:
+        assert max(len(v) for v in per_cu.values()) > 1
+    for b, nb in enumerate(lens):
+        part = rec[rec[:, 1] == b].copy()
+        part[:, 1] = 0
+        table = to_table(part, 1, H, Hkv, max(nb, 512), "causal", "descending", X * S)
+        table["n"] = -(-nb // 128)
+        osch.validate(table)
+    assert osch.simulate(to_table(rec, B, H, Hkv, N, "causal", "descending", X * S), 1.0, 0.5) > 0
