@@ -185,8 +185,8 @@ int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
                         int num_xcd, int cus_per_xcd,
                         int* records, long long capacity, long long* count, int* xcd_local);
 
-/* Variable-length batches (the paper's workloads pack sequences of different lengths
- * into one batch; section 4.1 benchmarks one length at a time). Same call as
+/* Variable-length batches (a training batch often holds sequences of different
+ * lengths; the DASH paper's section 4.1 benchmarks one length at a time). Same call as
  * dash_attn_bwd on the padded layout: q, o, dO, dq [B,H,N,d], k, v, dk, dv [B,Hkv,N,d],
  * lse [B,H,N], where batch b holds seqlens[b] rows (a HOST array of B ints, 1 <=
  * seqlens[b] <= N; N is the padded length and the row stride). Batch b's backward is
