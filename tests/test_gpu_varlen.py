@@ -29,6 +29,8 @@ CASES = [
     (3, 4, 2, 1024, 128, (1024, 700, 513)),  # GQA, ragged lengths, odd tile counts (8, 6, 5)
     (2, 2, 2, 768, 64, (300, 768)),          # a batch shorter than one 512-row block
     (2, 2, 1, 1024, 128, (1024, 512)),       # even tile counts (8, 4): symmetric shift allowed
+    # More batches than CUs per XCD (the shared layout), lengths 1 .. 512 (single tiles too).
+    (34, 1, 1, 512, 64, tuple(int(x) for x in np.random.default_rng(5).integers(1, 513, 34))),
 ]
 
 
