@@ -24,15 +24,16 @@
 // operand (32 AGPRs), K^T of one d block (32), one accumulator (dV or dK, 64) and the
 // VGPRs in flight, so the two waves of a pair share one SIMD and each covers the other's
 // stalls. At d = 64 the step's partial has four 32x32 blocks: the A waves compute them
-// (24 MFMAs per A wave and step, 16 per B wave). P goes from A to B as bf16 through a 4 KiB LDS area per pair (lane l of B holds
-// the same S/dP accumulator elements as lane l of A); dS goes to LDS transposed, as the
-// dQ contraction needs it anyway.
+// (24 MFMAs per A wave and step, 16 per B wave). P goes from A to B as bf16 through a
+// 4 KiB LDS area per pair (lane l of B holds the same S/dP accumulator elements as lane
+// l of A); dS goes to LDS transposed, as the dQ contraction needs it anyway.
 //
 // Step of 64 Q rows (a pair-local handoff X and a workgroup barrier Y):
 //   A: S MFMAs of Q block 0, then of block 1 with block 0's softmax and the next step's
 //      Q-tile copies between them; block 1's softmax; P -> LDS      | flag X set |
-//      dV MFMAs with the previous step's dQ block (8 MFMAs) in their second half, its
-//      stores, its turn passed on; this step's turn polled and running sum loaded
+//      dV MFMAs with the previous step's dQ block (8 MFMAs) between those of the first
+//      half, its stores (acknowledged under the second half), its turn passed on; this
+//      step's turn polled and running sum loaded
 //                                                                   | barrier Y |
 //   B: dP MFMAs with the next step's dO-tile copies and the previous step's dQ block;
 //      its stores                                                   | flag X awaited |
@@ -47,6 +48,9 @@
 // their dP MFMAs). The compiler does not see these copies (inline assembly), so a wave
 // waits for its running-sum loads before issuing them (the vector-memory counter is in
 // order) and for the copies themselves before the step-end barrier.
+// Variable-length batches: every row limit (copy clamps, the zeroed K rows of a ragged
+// KV tile, the dK/dV stores) is the length of the item's or step's batch; N stays the
+// row stride.
 // Operand layouts, the padded and row-permuted LDS tiles, the fp32 accumulator's block
 // layout, the step records and the turn protocol are those of bwd_main.hip.
 #include <hip/hip_runtime.h>
@@ -456,7 +460,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       Pending pd_n;
       int sem_now = 0;
       if constexpr (roleA) {
-        // ---- S = Q K^T (both 32-row blocks), operands two slots ahead.
+        // ---- S = Q K^T (both 32-row blocks), operands kR - 1 slots ahead.
         floatx16 S0, S1;
         // Causal diagonal: S = -inf (P = 0) where the key comes after the query. Row of
         // element r = 4 t + e of block qb: pi(m) = 32 qb + 16 (t / 2) + 2 (t % 2) + 4 e + hi.
@@ -537,7 +541,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         if (lane == 0) *sFlag = gstep;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         PROF_MARK(kProfBarrierX);
-        // ---- dV += P^T dO, with the previous step's dQ block in the second half.
+        // ---- dV += P^T dO, with the previous step's dQ block in the first half.
         if (have_prev && !loaded) {
           reduce_wait(pd);
           reduce_load(pd, ld);
@@ -597,8 +601,8 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         if (loaded) reduce_load(pd_n, ld);
         PROF_MARK(kProfBody);
       } else {
-        // ---- The next step's copies; dP - D = dO V^T - D (the accumulation starts from
-        // -D); the previous step's dQ block in the second half; its stores.
+        // ---- The next step's dO-tile copies; dP - D = dO V^T - D (the accumulation
+        // starts from -D); the previous step's dQ block in the second half; its stores.
         if (have_prev && !loaded) {
           reduce_wait(pd);
           reduce_load(pd, ld);
