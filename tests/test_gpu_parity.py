@@ -136,3 +136,25 @@ def test_repeat_runs_bitwise_identical_d128_kernels(causal, kernel):
                 assert [bf16_bytes(t) for t in out] == ref_bytes, (sched, rep)
 
     _with_kernel(kernel, body)
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 2, 2, 256, 64), True), ((2, 4, 2, 2048, 128), False),
+                                          ((2, 4, 2, 4096, 128), True), ((1, 4, 4, 640, 128), True),
+                                          ((2, 16, 16, 2048, 64), True)],
+                         ids=["tiny-causal", "full-d128", "causal-d128", "causal-odd-tiles", "causal-d64-wide"])
+def test_auto_runs_the_resolved_schedule(shape, causal):
+    """dash_attn_bwd with schedule = auto runs exactly the schedule the host model names
+    (dash_schedule_resolve with the device's topology): same bits as that schedule."""
+    from scheduling_fa_attn_amd import dash
+    B, H, Hkv, N, d = shape
+    case = make_case(B, H, Hkv, N, d, causal, seed=41)
+    dev = to_device(case)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    if cus % 8:
+        pytest.skip("the topology probe finds 8 equal L2 domains only on a whole MI355X")
+    names = {0: "naive", 1: "descending", 2: "shift", 3: "sym_shift"}
+    resolved = dash.dash_schedule_resolve(B, H, Hkv, N, d, "causal" if causal else "full", "auto", 8, cus // 8)
+    assert resolved in names
+    auto, _ = run(case, dev, "auto", 1)
+    ref, _ = run(case, dev, names[resolved], 1)
+    assert [bf16_bytes(t) for t in auto] == [bf16_bytes(t) for t in ref], names[resolved]
