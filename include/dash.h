@@ -194,9 +194,8 @@ int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
  * aligned within the batch); rows at or past seqlens[b] of dq, dk and dv are left
  * unchanged, and those rows of the inputs are never read as data. The schedule applies
  * per batch (DASH_SCHED_AUTO: the model's choice at each batch's length).
- * Supported: N >= 512 (128-row tiles), deterministic = 0 or 1, and the
- * two-waves-per-SIMD kernel (DASH_KERNEL_AUTO or DASH_KERNEL_TWO_WAVES_PER_SIMD);
- * otherwise DASH_ERR_UNSUPPORTED. The workspace is dash_attn_bwd_workspace_size(B, H,
+ * Supported: deterministic = 0 or 1 (the two-pass variant, 2, gives
+ * DASH_ERR_UNSUPPORTED), every tile size and both main kernels. The workspace is dash_attn_bwd_workspace_size(B, H,
  * Hkv, N, d). Errors: as dash_attn_bwd, and DASH_ERR_INVALID_ARG for a null seqlens or
  * a length outside [1, N]; symmetric shift needs an even tile count in every batch. */
 int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -206,7 +205,7 @@ int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Host-only export of the table dash_attn_bwd_varlen runs for these batch lengths
- * (seqlens: B host ints in [1, N]; N >= 512), in the records of dash_schedule_table;
+ * (seqlens: B host ints in [1, N]), in the records of dash_schedule_table;
  * DASH_SCHED_AUTO resolves per batch as in dash_attn_bwd_varlen with d = 128. */
 int dash_schedule_table_varlen(int B, int H, int Hkv, int N, const int* seqlens, int mask, int schedule,
                                int num_xcd, int cus_per_xcd,

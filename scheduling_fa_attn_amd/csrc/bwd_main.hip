@@ -134,6 +134,10 @@ bwd_main_kernel(BwdParams p) {
 
   PROF_DECL
   const int H = p.H, Hkv = p.Hkv, N = p.N;
+  // Rows of batch b: N, or seqlens[b] <= N for variable-length batches (N stays the row
+  // stride of every tensor; rows past a batch's length are padding, never read as data).
+  const CONST_AS int* seqlens = (const CONST_AS int*)p.seqlens;
+  auto len_of = [&](int b) __attribute__((always_inline)) { return p.seqlens ? seqlens[b] : N; };
   constexpr bool cross = CROSS;
   static_assert(DET || !CROSS, "device-scope chains exist only in the ordered reduction");
   static_assert(!(DET && NODQ), "the ordered reduction reduces dQ");
@@ -179,12 +183,13 @@ bwd_main_kernel(BwdParams p) {
     const Quad item2 = load_quad(items, it2);
     const int64_t bg2 = static_cast<int64_t>(item2.x) * Hkv + item2.y;
     const int kv02 = item2.z * BC;
+    const int nrow2 = len_of(item2.x);
     TileCopy<D, BC, NW> kcopy;  // plan computed in place
     kcopy.init(w, lane);
-    kcopy.issue(sK, p.k + bg2 * N * D, kv02, N, w);
+    kcopy.issue(sK, p.k + bg2 * N * D, kv02, nrow2, w);
 #pragma unroll
     for (int hh = 0; hh < BC / BQ; ++hh)
-      qcopy.issue(smem + (hh == 0 ? C::OFF_Q : C::OFF_DO) + (par0 ^ 1) * C::QT, p.v + bg2 * N * D, kv02 + BQ * hh, N,
+      qcopy.issue(smem + (hh == 0 ? C::OFF_Q : C::OFF_DO) + (par0 ^ 1) * C::QT, p.v + bg2 * N * D, kv02 + BQ * hh, nrow2,
                   w);
   };
   auto issue_first_step = [&](int it2, int par0) __attribute__((always_inline)) {
@@ -192,8 +197,9 @@ bwd_main_kernel(BwdParams p) {
     const Quad task = load_quad(tasks, item2.w);
     const int q0 = task.y * BC;
     const int64_t bh = static_cast<int64_t>(item2.x) * H + task.x;
-    qcopy.issue(smem + C::OFF_Q + par0 * C::QT, p.q + bh * N * D, q0, N, w);
-    qcopy.issue(smem + C::OFF_DO + par0 * C::QT, p.dO + bh * N * D, q0, N, w);
+    const int nrow2 = len_of(item2.x);
+    qcopy.issue(smem + C::OFF_Q + par0 * C::QT, p.q + bh * N * D, q0, nrow2, w);
+    qcopy.issue(smem + C::OFF_DO + par0 * C::QT, p.dO + bh * N * D, q0, nrow2, w);
     // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist.
     if (w == 0) dma4(p.nlse2 + bh * p.row_stride + q0, row_lane, smem + C::OFF_NL + par0 * 256);
     if (w == 1) dma4(p.neg_delta + bh * p.row_stride + q0, row_lane, smem + C::OFF_DL + par0 * 256);
@@ -220,17 +226,18 @@ bwd_main_kernel(BwdParams p) {
     const int n_steps = (t_end - t_begin) * SUBS;
     const int kv0 = kv_tile * BC;
     const int64_t bg = static_cast<int64_t>(item.x) * Hkv + item.y;
+    const int nrow = len_of(item.x);  // rows of this item's batch
     const bool has_next = it + 1 < it_end;
 
     // Item prologue: the item's tiles (issued before) have landed; K and V rows of this
     // wave to AGPRs, dK and dV accumulators zeroed.
     wait_mem_done();
     __syncthreads();
-    if (kv0 + BC > N) {
-      // Ragged KV tile: K rows past N become zero in LDS, so that the (unmasked,
-      // finite) dS of those columns adds nothing to dQ. Their dK/dV rows are never
-      // stored; their K/V operands (copies of row N - 1) only feed those rows.
-      const int r0 = N - kv0;
+    if (kv0 + BC > nrow) {
+      // Ragged KV tile: K rows past the batch's length become zero in LDS, so that the
+      // (unmasked, finite) dS of those columns adds nothing to dQ. Their dK/dV rows are
+      // never stored; their K/V operands (copies of the last row) only feed those rows.
+      const int r0 = nrow - kv0;
       LDS_AS floatx4* z = reinterpret_cast<LDS_AS floatx4*>(sK + r0 * ST);
       for (int x = tid; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
@@ -530,8 +537,8 @@ bwd_main_kernel(BwdParams p) {
       const LDS_AS char* sNL = smem + C::OFF_NL + buf * 256;
       const LDS_AS char* sDL = smem + C::OFF_DL + buf * 256;
       LDS_AS char* sdS = smem + C::OFF_DS + buf * C::DST;
-      // Only the diagonal task of a causal mask needs a mask: rows past N have
-      // -LSE*log2(e) = -inf (P = 0) and columns past N meet zero K rows in dQ.
+      // Only the diagonal task of a causal mask needs a mask: rows past the batch's length
+      // have -LSE*log2(e) = -inf (P = 0) and columns past it meet zero K rows in dQ.
       const bool diag = p.causal && j == kv_tile;
       // Causal diagonal (diagonal steps only): S = -inf, hence P = 0 and dS = 0, where the
       // key comes after the query, i.e. where pi(m) < kvcol - q0. Row of element r of
@@ -553,6 +560,7 @@ bwd_main_kernel(BwdParams p) {
       // same, so that the copies need no branch; nothing reads that buffer any more.
       const int q0_n = rec_nxt.y;
       const int64_t bh_n = rec_nxt.x;
+      const int nrow_n = len_of(rec_nxt.x / H);  // rows of the next step's batch
       const bf16* q_n = p.q + bh_n * N * D;
       const bf16* do_n = p.dO + bh_n * N * D;
       LDS_AS char* const sQn = smem + C::OFF_Q + (buf ^ 1) * C::QT;
@@ -561,9 +569,9 @@ bwd_main_kernel(BwdParams p) {
       constexpr int kCopyOps = 2 * kPW + 1;
       auto copy_op = [&](int o) __attribute__((always_inline)) {
         if (o < kPW) {
-          qcopy.issue_one_clamped(sQn, q_n, q0_n, N, w, o);
+          qcopy.issue_one_clamped(sQn, q_n, q0_n, nrow_n, w, o);
         } else if (o < 2 * kPW) {
-          qcopy.issue_one_clamped(sdOn, do_n, q0_n, N, w, o - kPW);
+          qcopy.issue_one_clamped(sdOn, do_n, q0_n, nrow_n, w, o - kPW);
         } else {
           // Row arrays are padded to the tile, so rows q0 .. q0+63 always exist. Waves of
           // one parity write the same values to the same LDS slots.
@@ -902,7 +910,7 @@ bwd_main_kernel(BwdParams p) {
           const int chunk = lane + 64 * k, row = chunk >> 3, c16 = chunk & 7;
           const u32x4 v = *reinterpret_cast<const LDS_AS u32x4*>(stage + row * kDsStride + 16 * c16);
           const int kvr = kv0 + 32 * w + row;
-          if (kvr < N) *reinterpret_cast<u32x4*>(g + static_cast<int64_t>(kvr) * D + 64 * half + 8 * c16) = v;
+          if (kvr < nrow) *reinterpret_cast<u32x4*>(g + static_cast<int64_t>(kvr) * D + 64 * half + 8 * c16) = v;
         }
       }
     }

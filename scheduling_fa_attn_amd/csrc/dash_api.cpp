@@ -333,6 +333,12 @@ int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* 
   return DASH_OK;
 }
 
+// Variable-length batches: the length at which the cost model prices batch b (its own
+// length, raised to 512 when the padded length N uses 128-row tiles, so that the model
+// prices the tile the table uses), and whether its tile count is odd (no symmetric shift).
+int varlen_model_len(int N, int len) { return tile_for(N) == 128 && len < 512 ? 512 : len; }
+bool varlen_odd_tiles(int N, int len) { return cdiv(len, tile_for(N)) % 2 != 0; }
+
 // Variable-length batches: the table of dash::build_table_varlen, cached per lengths.
 int get_table_varlen(DeviceState* st, int B, int H, int Hkv, int N, bool causal, const std::vector<int>& lens,
                      const std::vector<int>& scheds, const DevTable** out) {
@@ -379,27 +385,23 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
   if (deterministic < 0 || deterministic > 2) return DASH_ERR_INVALID_ARG;
-  // Variable-length batches: lengths in [1, N]; 128-row tiles, the two-waves kernel and
-  // the ordered or atomic reduction only.
+  // Variable-length batches: lengths in [1, N]; the ordered or atomic reduction only.
   std::vector<int> lens, scheds;
   if (seqlens && B > 0 && N > 0) {
     for (int b = 0; b < B; ++b) {
       if (seqlens[b] < 1 || seqlens[b] > N) return DASH_ERR_INVALID_ARG;
       lens.push_back(seqlens[b]);
     }
-    if (tile_for(N) != 128 || deterministic == 2) return DASH_ERR_UNSUPPORTED;
+    if (deterministic == 2) return DASH_ERR_UNSUPPORTED;
     for (int b = 0; b < B; ++b) {
       int sb = requested;
       if (sb != DASH_SCHED_AUTO) {
-        const int c = check_sizes(1, H, Hkv, lens[b] < 512 ? 512 : lens[b], d, mask, sb);
-        // (the batch's tiles are 128 rows even where its own length is below 512)
+        const int c = check_sizes(1, H, Hkv, varlen_model_len(N, lens[b]), d, mask, sb);
         if (c != DASH_OK) return c;
-        if (sb == DASH_SCHED_SYM_SHIFT && cdiv(lens[b], 128) % 2) return DASH_ERR_UNSUPPORTED;
+        if (sb == DASH_SCHED_SYM_SHIFT && varlen_odd_tiles(N, lens[b])) return DASH_ERR_UNSUPPORTED;
       }
       scheds.push_back(sb);
     }
-    std::lock_guard<std::mutex> lock(g_mu);
-    if (g_kernel == DASH_KERNEL_ONE_WAVE_PER_SIMD) return DASH_ERR_UNSUPPORTED;
   }
   if (!(scale > 0.f) || !std::isfinite(scale)) return DASH_ERR_INVALID_ARG;
   if (B == 0 || N == 0) return DASH_OK;
@@ -434,7 +436,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
       // AUTO per batch: the model's choice at the batch's own length (cached like AUTO).
       for (int b = 0; b < B; ++b) {
         if (scheds[b] != DASH_SCHED_AUTO) continue;
-        const int nb = lens[b] < 512 ? 512 : lens[b];
+        const int nb = varlen_model_len(N, lens[b]);
         const auto key = std::make_tuple(1, H, Hkv, nb, d, mask, st->num_xcd, st->cus_per_xcd, g_placement);
         auto it = g_auto.find(key);
         if (it == g_auto.end()) {
@@ -444,7 +446,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
           it = g_auto.emplace(key, r).first;
         }
         scheds[b] = it->second;
-        if (scheds[b] == DASH_SCHED_SYM_SHIFT && cdiv(lens[b], 128) % 2) scheds[b] = DASH_SCHED_DESCENDING;
+        if (scheds[b] == DASH_SCHED_SYM_SHIFT && varlen_odd_tiles(N, lens[b])) scheds[b] = DASH_SCHED_DESCENDING;
       }
       s = get_table_varlen(st, B, H, Hkv, N, causal, lens, scheds, &tab);
     } else {
@@ -537,7 +539,6 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   const bool pair_ok = tab->tile == 128 && deterministic != 2 && (deterministic == 0 || bp.xcd_local ||
                        st->num_xcd == 1);
   const bool use_pair = pair_ok && (kernel == DASH_KERNEL_TWO_WAVES_PER_SIMD || (kernel == DASH_KERNEL_AUTO && kPairAuto));
-  if (tab->seqlens && !use_pair) return DASH_ERR_UNSUPPORTED;  // (the one-wave kernel has no per-batch lengths)
   hipError_t e = !use_pair ? dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream)
                  : d == 128 ? dash::launch_pair_d128(bp, tab->workers, stream)
                             : dash::launch_pair_d64(bp, tab->workers, stream);
@@ -764,22 +765,21 @@ int dash_schedule_table_varlen(int B, int H, int Hkv, int N, const int* seqlens,
                                int cus_per_xcd, int* records, long long capacity, long long* count, int* xcd_local) {
   if (seqlens == nullptr || count == nullptr || capacity < 0 || B <= 0) return DASH_ERR_INVALID_ARG;
   if (num_xcd <= 0 || cus_per_xcd <= 0 || num_xcd > 64 || cus_per_xcd > 4096) return DASH_ERR_INVALID_ARG;
-  if (tile_for(N) != 128) return DASH_ERR_UNSUPPORTED;
   std::vector<int> lens;
   std::vector<Sched> kinds;
   for (int b = 0; b < B; ++b) {
     if (seqlens[b] < 1 || seqlens[b] > N) return DASH_ERR_INVALID_ARG;
     lens.push_back(seqlens[b]);
-    const int nb = seqlens[b] < 512 ? 512 : seqlens[b];
+    const int nb = varlen_model_len(N, seqlens[b]);
     int sb = schedule;
     if (sb == DASH_SCHED_AUTO) {
       sb = dash_schedule_resolve(1, H, Hkv, nb, 128, mask, sb, num_xcd, cus_per_xcd);
       if (sb < 0) return sb;
-      if (sb == DASH_SCHED_SYM_SHIFT && cdiv(seqlens[b], 128) % 2) sb = DASH_SCHED_DESCENDING;
+      if (sb == DASH_SCHED_SYM_SHIFT && varlen_odd_tiles(N, seqlens[b])) sb = DASH_SCHED_DESCENDING;
     } else {
       const int c = check_sizes(1, H, Hkv, nb, 128, mask, sb);
       if (c != DASH_OK) return c;
-      if (sb == DASH_SCHED_SYM_SHIFT && cdiv(seqlens[b], 128) % 2) return DASH_ERR_UNSUPPORTED;
+      if (sb == DASH_SCHED_SYM_SHIFT && varlen_odd_tiles(N, seqlens[b])) return DASH_ERR_UNSUPPORTED;
     }
     kinds.push_back(static_cast<Sched>(sb));
   }
@@ -788,7 +788,7 @@ int dash_schedule_table_varlen(int B, int H, int Hkv, int N, const int* seqlens,
   sp.H = H;
   sp.Hkv = Hkv;
   sp.N = N;
-  sp.tile = 128;
+  sp.tile = tile_for(N);
   sp.causal = mask == DASH_MASK_CAUSAL;
   sp.num_xcd = num_xcd;
   sp.cus_per_xcd = cus_per_xcd;

@@ -31,6 +31,9 @@ CASES = [
     (2, 2, 1, 1024, 128, (1024, 512)),       # even tile counts (8, 4): symmetric shift allowed
     # More batches than CUs per XCD (the shared layout), lengths 1 .. 512 (single tiles too).
     (34, 1, 1, 512, 64, tuple(int(x) for x in np.random.default_rng(5).integers(1, 513, 34))),
+    # Padded length below 512: 64-row tiles (the one-wave kernel), ragged and single-tile batches.
+    (3, 2, 1, 448, 128, (448, 130, 64)),
+    (2, 2, 2, 320, 64, (1, 320)),
 ]
 
 
@@ -97,7 +100,8 @@ def test_varlen_parity(case, causal):
     bits, lse, scale, ref = _case(B, H, Hkv, N, d, lens, causal, seed=3000 + N + d)
     dev = _dev(bits, lse)
     mask = "causal" if causal else "full"
-    even = all(-(-nb // 128) % 2 == 0 for nb in lens)
+    tile = dash.dash_tile_size(N)
+    even = all(-(-nb // tile) % 2 == 0 for nb in lens)
     scheds = ["auto", "naive", "descending"] + (["sym_shift"] if causal and even else []) + \
         ([] if causal else ["shift"])
     for sched in scheds:
@@ -136,8 +140,33 @@ def test_varlen_argument_errors():
     assert call((513, 512)) == dash.DASH_ERR_INVALID_ARG
     assert call((512, 512), det=2) == dash.DASH_ERR_UNSUPPORTED
     assert call((512, 384), sched="sym_shift") == dash.DASH_ERR_UNSUPPORTED  # 3 tiles
+
+    small = {k: t[:, :, :256].contiguous() for k, t in dev.items()}
+    outs_s = [torch.empty_like(small[k]) for k in ("q", "k", "v")]
+    st = dash.dash_attn_bwd_varlen(small["q"], small["k"], small["v"], small["o"], small["do"], small["lse"], *outs_s,
+                                   (256, 192), 0.125, "causal", "sym_shift", 1, ws)
+    assert st == dash.DASH_ERR_UNSUPPORTED  # 3 tiles of 64 rows in batch 1
+
+
+@pytest.mark.parametrize("causal", [False, True], ids=["full", "causal"])
+def test_varlen_one_wave_kernel(causal):
+    """The one-wave kernel with per-batch lengths at 128-row tiles (chosen with
+    dash_set_kernel; it is also the kernel of chains that cross XCDs): parity and bitwise
+    repeats."""
+    B, H, Hkv, N, d, lens = CASES[0]
+    bits, lse, scale, ref = _case(B, H, Hkv, N, d, lens, causal, seed=77)
+    dev = _dev(bits, lse)
+    mask = "causal" if causal else "full"
     assert dash.dash_set_kernel("one_wave") == dash.DASH_OK
     try:
-        assert call((512, 512)) == dash.DASH_ERR_UNSUPPORTED
+        for sched in ("auto", "descending", "naive"):
+            for det in (1, 0):
+                print(f"varlen one_wave causal={causal} schedule={sched} det={det}", flush=True)
+                outs, ws = _run(dev, lens, scale, mask, sched, det)
+                _check(outs, ref, lens)
+                if det == 1:
+                    again, _ = _run(dev, lens, scale, mask, sched, det, ws)
+                    assert [t.view(torch.int16).cpu().numpy().tobytes() for t in again] == \
+                        [t.view(torch.int16).cpu().numpy().tobytes() for t in outs]
     finally:
         dash.dash_set_kernel("auto")

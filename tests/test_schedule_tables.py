@@ -272,28 +272,32 @@ def test_makespan_rejects_bad_costs():
 # Variable-length batches: one table per batch at its own length, merged per CU.
 # ---------------------------------------------------------------------------------
 
+@pytest.mark.parametrize("N,lens", [(2048, (2048, 1100, 512)), (448, (448, 200, 64))], ids=["tile128", "tile64"])
 @pytest.mark.parametrize("mask,schedule", [("full", "shift"), ("full", "naive"), ("causal", "descending"),
                                            ("causal", "auto"), ("full", "auto")])
-def test_varlen_table_is_the_per_batch_tables_merged(mask, schedule):
+def test_varlen_table_is_the_per_batch_tables_merged(mask, schedule, N, lens):
     """Each batch's part of the merged table passes the oracle validator at its own tile
-    count (coverage, KV contiguity, rank order, acyclicity); the whole merged DAG is
-    acyclic (the oracle simulator raises on a cycle); every CU runs its batches in order."""
-    B, H, Hkv, N, lens = 3, 4, 2, 2048, (2048, 1100, 512)
+    count (tiles of the padded length's size; coverage, KV contiguity, rank order,
+    acyclicity); the whole merged DAG is acyclic (the oracle simulator raises on a
+    cycle); every CU runs its batches in order."""
+    B, H, Hkv = 3, 4, 2
+    tile = dash.dash_tile_size(N)
     rec, local = dash.dash_schedule_table_varlen(B, H, Hkv, N, lens, mask, schedule, 8, 32)
     assert local
     for b, nb in enumerate(lens):
-        n_b = -(-nb // 128)
+        n_b = -(-nb // tile)
+        model_len = max(nb, 512) if tile == 128 else nb  # priced at the table's tile size
         kind = schedule
         if kind == "auto":
-            kind = NAMES[dash.dash_schedule_resolve(1, H, Hkv, max(nb, 512), 128, mask, "auto", 8, 32)]
+            kind = NAMES[dash.dash_schedule_resolve(1, H, Hkv, model_len, 128, mask, "auto", 8, 32)]
             if kind == "sym_shift" and n_b % 2:
                 kind = "descending"
         part = rec[rec[:, 1] == b].copy()
         part[:, 1] = 0
-        table = to_table(part, 1, H, Hkv, max(nb, 512), mask, kind, 256)
+        table = to_table(part, 1, H, Hkv, model_len, mask, kind, 256)
         table["n"] = n_b
         osch.validate(table)
-        assert {int(t) for t in part[:, 5]} <= set(range(-(-nb // 128)))
+        assert {int(t) for t in part[:, 5]} <= set(range(n_b))
     full = to_table(rec, B, H, Hkv, N, mask, "naive", 256)
     assert osch.simulate(full, 1.0, 0.5) > 0
     for w in range(256):
@@ -309,7 +313,7 @@ def test_varlen_table_argument_errors():
     with pytest.raises(dash.DashError):
         dash.dash_schedule_table_varlen(2, 2, 2, 1024, (1024, 384), "causal", "sym_shift", 8, 32)  # 3 tiles
     with pytest.raises(dash.DashError):
-        dash.dash_schedule_table_varlen(1, 2, 2, 256, (256,), "full", "shift", 8, 32)  # 64-row tiles
+        dash.dash_schedule_table_varlen(2, 2, 2, 256, (256, 192), "causal", "sym_shift", 8, 32)  # 3 tiles of 64
 
 
 @pytest.mark.parametrize("B,topology", [(3, (8, 32)), (6, (2, 4))], ids=["banded", "shared"])
