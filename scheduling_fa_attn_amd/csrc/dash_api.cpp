@@ -385,14 +385,13 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
   if (deterministic < 0 || deterministic > 2) return DASH_ERR_INVALID_ARG;
-  // Variable-length batches: lengths in [1, N]; the ordered or atomic reduction only.
+  // Variable-length batches: lengths in [1, N].
   std::vector<int> lens, scheds;
   if (seqlens && B > 0 && N > 0) {
     for (int b = 0; b < B; ++b) {
       if (seqlens[b] < 1 || seqlens[b] > N) return DASH_ERR_INVALID_ARG;
       lens.push_back(seqlens[b]);
     }
-    if (deterministic == 2) return DASH_ERR_UNSUPPORTED;
     for (int b = 0; b < B; ++b) {
       int sb = requested;
       if (sb != DASH_SCHED_AUTO) {
@@ -555,6 +554,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     dp.nlse2 = nlse2;
     dp.neg_delta = neg_delta;
     dp.dq = static_cast<__bf16*>(dq);
+    dp.seqlens = tab->seqlens;
     dp.B = B;
     dp.H = H;
     dp.Hkv = Hkv;

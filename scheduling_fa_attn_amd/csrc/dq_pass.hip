@@ -48,20 +48,24 @@ dq_pass_kernel(DqParams p) {
   const int b = bh / p.H, h = bh % p.H;
   const int64_t bg = static_cast<int64_t>(b) * p.Hkv + h / (p.H / p.Hkv);
   const int q0 = qt * BQ;
+  // Rows of this batch: N, or its length for variable-length batches (N stays the row
+  // stride; rows past the length are padding, never read as data or written).
+  const int nb = p.seqlens ? p.seqlens[b] : N;
+  if (q0 >= nb) return;  // a Q tile wholly past the batch's length (uniform: no barrier missed)
   const bf16* kg = p.k + bg * N * D;
   const bf16* vg = p.v + bg * N * D;
-  const int n_kv_all = (N + BK - 1) / BK;
+  const int n_kv_all = (nb + BK - 1) / BK;
   const int n_kv_causal = (q0 + BQ + BK - 1) / BK;
   const int n_kv = p.causal && n_kv_causal < n_kv_all ? n_kv_causal : n_kv_all;
 
   TileCopy<D, BK, NW> copy;
   copy.init(w, lane);
-  copy.issue(smem, kg, 0, N, w);
-  copy.issue(smem + 2 * KT, vg, 0, N, w);
+  copy.issue(smem, kg, 0, nb, w);
+  copy.issue(smem + 2 * KT, vg, 0, nb, w);
 
-  // This lane's query row (rows past N read row N - 1 and are never stored).
+  // This lane's query row (rows past the length read its last row and are never stored).
   const int qrow = q0 + 32 * w + l32;
-  const int qread = qrow < N ? qrow : N - 1;
+  const int qread = qrow < nb ? qrow : nb - 1;
   bf16x8 qreg[DK], doreg[DK];
 #pragma unroll
   for (int ks = 0; ks < DK; ++ks) {
@@ -70,7 +74,7 @@ dq_pass_kernel(DqParams p) {
     doreg[ks] = *reinterpret_cast<const bf16x8*>(p.dO + off);
   }
   // Row terms of this lane's row (row arrays are padded to the tile: -LSE*log2(e) is
-  // -inf and -D is 0 past N).
+  // -inf and -D is 0 past the length).
   const float nl = p.nlse2[static_cast<int64_t>(bh) * p.row_stride + qread];
   const float nd = p.neg_delta[static_cast<int64_t>(bh) * p.row_stride + qread];
   const float c = p.scale_log2;
@@ -86,8 +90,8 @@ dq_pass_kernel(DqParams p) {
     wait_mem_done();
     __syncthreads();
     if (t + 1 < n_kv) {
-      copy.issue(smem + (buf ^ 1) * KT, kg, (t + 1) * BK, N, w);
-      copy.issue(smem + (2 + (buf ^ 1)) * KT, vg, (t + 1) * BK, N, w);
+      copy.issue(smem + (buf ^ 1) * KT, kg, (t + 1) * BK, nb, w);
+      copy.issue(smem + (2 + (buf ^ 1)) * KT, vg, (t + 1) * BK, nb, w);
     }
     const LDS_AS char* sK = smem + buf * KT;
     const LDS_AS char* sV = smem + (2 + buf) * KT;
@@ -104,10 +108,10 @@ dq_pass_kernel(DqParams p) {
         dp[kb] = mfma32(lds_ld16(sV, off), doreg[ks], dp[kb]);
       }
     }
-    const bool ragged = kv0 + BK > N;
+    const bool ragged = kv0 + BK > nb;
     const bool diag = p.causal && kv0 + BK - 1 > q0;
     if (ragged || diag) {
-      const int lim = p.causal && qrow < N - 1 ? qrow : N - 1;  // last visible key
+      const int lim = p.causal && qrow < nb - 1 ? qrow : nb - 1;  // last visible key
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -141,7 +145,7 @@ dq_pass_kernel(DqParams p) {
   }
 
   // dQ = s dQ^T: elements 4 g4 .. 4 g4 + 3 of block db are d = 32 db + 8 g4 + 4 hi + 0 .. 3.
-  if (qrow < N) {
+  if (qrow < nb) {
     bf16* row = p.dq + (static_cast<int64_t>(bh) * N + qrow) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)

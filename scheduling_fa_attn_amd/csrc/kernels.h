@@ -85,6 +85,7 @@ struct DqParams {
   const float* nlse2;       // [B*H][row_stride] -LSE * log2(e)
   const float* neg_delta;   // [B*H][row_stride] -D
   __bf16* dq;               // [B, H, N, d]
+  const int* seqlens;       // rows of each batch (variable-length batches), or null: N
   int B, H, Hkv, N;
   int row_stride;
   int n_qt;                 // 128-row Q tiles per head

@@ -5,8 +5,8 @@ gradients must equal the oracle backward of its own truncated sequence (the text
 attention gradient, DASH paper section 2.1; causal masks top-left aligned within the
 batch), to max |GPU - oracle| / max |oracle| <= 1e-2 per tensor and batch. The padded
 input rows are NaN, so that any read of them as data would poison the result; the padded
-output rows must come back exactly as they were (a sentinel). Deterministic runs repeat
-bit for bit.
+output rows must come back exactly as they were (a sentinel). Deterministic runs (the ordered
+reduction and the two-pass variant) repeat bit for bit.
 """
 import math
 
@@ -105,7 +105,7 @@ def test_varlen_parity(case, causal):
     scheds = ["auto", "naive", "descending"] + (["sym_shift"] if causal and even else []) + \
         ([] if causal else ["shift"])
     for sched in scheds:
-        for det in (1, 0):
+        for det in (1, 0, 2):
             print(f"varlen {case} causal={causal} schedule={sched} det={det}", flush=True)
             outs, _ = _run(dev, lens, scale, mask, sched, det)
             _check(outs, ref, lens)
@@ -117,11 +117,12 @@ def test_varlen_bitwise_repeatable(causal):
     bits, lse, scale, _ = _case(B, H, Hkv, N, d, lens, causal, seed=31)
     dev = _dev(bits, lse)
     mask = "causal" if causal else "full"
-    ref, ws = _run(dev, lens, scale, mask, "auto", 1)
-    ref_bytes = [t.view(torch.int16).cpu().numpy().tobytes() for t in ref]
-    for rep in range(9):
-        out, ws = _run(dev, lens, scale, mask, "auto", 1, ws)
-        assert [t.view(torch.int16).cpu().numpy().tobytes() for t in out] == ref_bytes, rep
+    for det in (1, 2):
+        ref, ws = _run(dev, lens, scale, mask, "auto", det)
+        ref_bytes = [t.view(torch.int16).cpu().numpy().tobytes() for t in ref]
+        for rep in range(9):
+            out, ws = _run(dev, lens, scale, mask, "auto", det, ws)
+            assert [t.view(torch.int16).cpu().numpy().tobytes() for t in out] == ref_bytes, (det, rep)
 
 
 def test_varlen_argument_errors():
@@ -138,7 +139,7 @@ def test_varlen_argument_errors():
 
     assert call((0, 512)) == dash.DASH_ERR_INVALID_ARG
     assert call((513, 512)) == dash.DASH_ERR_INVALID_ARG
-    assert call((512, 512), det=2) == dash.DASH_ERR_UNSUPPORTED
+    assert call((512, 512), det=3) == dash.DASH_ERR_INVALID_ARG
     assert call((512, 384), sched="sym_shift") == dash.DASH_ERR_UNSUPPORTED  # 3 tiles
 
     small = {k: t[:, :, :256].contiguous() for k, t in dev.items()}
