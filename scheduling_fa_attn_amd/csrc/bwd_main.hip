@@ -97,8 +97,9 @@ struct BwdCfg {
 // DET: ordered reduction (p.deterministic != 0) or float atomics; one kernel each, so
 // that neither carries the other's code and registers. CROSS (ordered reduction only):
 // the contributors of one dQ tile may sit on different XCDs, whose L2s are not coherent
-// with each other, so the running sums and turns go through device-scope accesses and
-// fences; otherwise every chain stays inside one XCD's L2. NODQ (with !DET): dK and dV
+// with each other, so the running sums and turns go through device-scope loads and
+// stores (no whole-L2 write-back or invalidate); otherwise every chain stays inside one
+// XCD's L2. NODQ (with !DET): dK and dV
 // only, no dQ work at all (the two-pass variant computes dQ in a separate kernel).
 template <int D, int NW, bool DET, bool CROSS, bool NODQ>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -387,7 +388,9 @@ bwd_main_kernel(BwdParams p) {
     auto reduce_wait = [&](Pending& pd) __attribute__((always_inline)) {
       if (reduce_needs_turn(pd)) {
         if (cross) {
-          pd.go = wait_turn(pd.sem, pd.rank, p.err, p.timeout_ticks, true);
+          // No acquire fence after the wait: the running sums are read with device-scope
+          // loads, which see the other XCD's device-scope stores by themselves.
+          pd.go = wait_turn(pd.sem, pd.rank, p.err, p.timeout_ticks, false);
         } else {
           pd.go = wait_turn_local(pd.sem, pd.rank, p.err, p.timeout_ticks);
         }
@@ -472,26 +475,27 @@ bwd_main_kernel(BwdParams p) {
           const float f = v[4 * i + e];
           x[e] = __builtin_bit_cast(unsigned, f);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_off[t2] + 1024 * i, 0, 0);
+        // Chains that cross XCDs store with device scope (written through this XCD's L2);
+        // inside one XCD the L2 is the coherence point and a plain store suffices.
+        __builtin_amdgcn_raw_buffer_store_b128(x, pd.acc_rs, acc_off[t2] + 1024 * i, 0, cross ? kSC1 : 0);
       }
     };
     auto reduce_store = [&](const Pending& pd, int t2, const floatx16& v) __attribute__((always_inline)) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) reduce_store_part(pd, t2, i, v);
     };
-    // Call after wait_mem_done(): this wave's accumulator stores are in the L2.
+    // Call after wait_mem_done(): this wave's accumulator stores have been acknowledged
+    // (in the L2, or past it for device-scope stores), so the turn can be passed on.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
       if (!DET || !pd.go || pd.last) return;
-      if (cross) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       if (lane == 0) {
-        if (cross) {
-          __hip_atomic_store(pd.sem, pd.rank + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        } else {
-          // Writer and reader share this XCD's L2, where the acknowledged stores already
-          // are: a plain store into the L2 suffices, and the next contributor's poll
-          // then hits in the L2 instead of going past it.
-          __builtin_amdgcn_raw_buffer_store_b32(static_cast<unsigned>(pd.rank + 1), make_rsrc(pd.sem, 4), 0, 0, 0);
-        }
+        // Writer and reader share this XCD's L2, where the acknowledged stores already
+        // are: a plain store into the L2 suffices, and the next contributor's poll then
+        // hits in the L2 instead of going past it. Across XCDs the running sums were
+        // stored with device scope, so no L2 write-back is needed before the flag, which
+        // is itself a device-scope store.
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<unsigned>(pd.rank + 1), make_rsrc(pd.sem, 4), 0, 0,
+                                              cross ? kSC1 : 0);
       }
     };
 
@@ -829,10 +833,7 @@ bwd_main_kernel(BwdParams p) {
           const int sem_seen = __builtin_amdgcn_readfirstlane(sem_now);
           loaded = !reduce_needs_turn(pd_n) || sem_seen == pd_n.rank;
           PROF_MARK(kProfPoll);
-          if (loaded) {
-            if (cross && reduce_needs_turn(pd_n)) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-            reduce_load(pd_n, ld);
-          }
+          if (loaded) reduce_load(pd_n, ld);  // (device-scope loads across XCDs: no fence)
         }
         SLOT();
       }

@@ -75,8 +75,8 @@ int resolve_schedule(int schedule, int N, int mask) {
 //  - d = 64: causal mask, B=4, H=32, N=4096: main kernel 0.962 ms for 264 tasks per CU,
 //    split in the same proportion: c = 3.2, r_local = 0.45;
 //  - r_remote: dQ chains across XCDs (causal mask, B=1, H=16, N=16384, d=128, symmetric shift)
-//    ran at 49.7 TFLOPS against 853.7 inside one XCD, 104 us instead of 6.1 us per task:
-//    r_remote = 98, independent of d (an L2 write-back and invalidate per step).
+//    ran at 688 TFLOPS against 861 inside one XCD, 7.8 us instead of 6.2 us per task:
+//    r_remote = 0.9 + 1.6 = 2.5, taken for both d (device-scope running sums and flags).
 // 64-row tiles (N < 512) do a quarter of the contraction work and half of the dQ
 // traffic per task. The same kernel binary runs every schedule (the table is data), so
 // the model has no schedule-dependent register term.
@@ -84,7 +84,7 @@ dash::CostModel measured_costs(int d, int tile) {
   dash::CostModel m;
   m.c = d == 128 ? 5.6 : 3.2;
   m.r_local = d == 128 ? 0.9 : 0.45;
-  m.r_remote = 98.0;
+  m.r_remote = 2.5;
   if (tile == 64) {
     m.c *= 0.25;
     m.r_local *= 0.5;
