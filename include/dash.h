@@ -194,9 +194,10 @@ int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
  * aligned within the batch); rows at or past seqlens[b] of dq, dk and dv are left
  * unchanged, and those rows of the inputs are never read as data. The schedule applies
  * per batch (DASH_SCHED_AUTO: the model's choice at each batch's length).
- * Every deterministic mode, tile size and main kernel is supported. The workspace is dash_attn_bwd_workspace_size(B, H,
- * Hkv, N, d). Errors: as dash_attn_bwd, and DASH_ERR_INVALID_ARG for a null seqlens or
- * a length outside [1, N]; symmetric shift needs an even tile count in every batch. */
+ * Every deterministic mode, tile size and main kernel is supported. The workspace is
+ * dash_attn_bwd_workspace_size(B, H, Hkv, N, d). Errors: as dash_attn_bwd, and
+ * DASH_ERR_INVALID_ARG for a null seqlens or a length outside [1, N]; symmetric shift
+ * needs an even tile count (of the padded length's tile size) in every batch. */
 int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,
                          const float* lse, void* dq, void* dk, void* dv,
                          int B, int H, int Hkv, int N, int d, const int* seqlens,
