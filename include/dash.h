@@ -60,9 +60,11 @@ typedef enum { DASH_MASK_FULL = 0, DASH_MASK_CAUSAL = 1 } dash_mask;
 
 /* Tile-to-CU schedules (DASH, section 3). shift is defined for the full mask only,
  * sym_shift for the causal mask only (with an even number of KV tiles per head).
- * DASH_SCHED_AUTO picks, per call, the schedule this library measured fastest on MI355X
- * at every point of the paper's benchmark grid: shift for the full mask, sym_shift for
- * the causal mask, descending for a causal mask with an odd tile count. */
+ * DASH_SCHED_AUTO runs the valid schedule (naive, descending, and shift for the full
+ * mask or sym_shift for the causal mask) with the smallest makespan under a DAG cost
+ * model of the tables for the device's topology (section 3.1 graph, per-task costs
+ * measured on MI355X, cross-XCD reductions priced apart); dash_schedule_resolve names
+ * it. On the paper's benchmark grid that is shift (full) and sym_shift (causal). */
 typedef enum {
   DASH_SCHED_NAIVE = 0,
   DASH_SCHED_DESCENDING = 1,
@@ -90,10 +92,10 @@ int dash_set_placement(int placement);
  * to a pair of waves that split the contractions by role (S, P, dV and dP, dS, dK; one
  * dQ block each), so that two waves share every SIMD. The latter covers 128-row tiles
  * (N >= 512) with deterministic = 0 or 1 (dQ chains inside one XCD); other calls use the
- * former under every setting. DASH_KERNEL_AUTO picks the one measured faster: the two-waves
- * kernel wherever it applies. Both give results
- * within the same tolerance; their bits differ (dS is formed from the bf16 P in the
- * two-waves kernel), and each is bitwise reproducible on its own. */
+ * former under every setting. DASH_KERNEL_AUTO picks the one measured faster: the
+ * two-waves kernel wherever it applies. Both give results within the same tolerance;
+ * their bits differ (dS is formed from the bf16 P in the two-waves kernel), and each is
+ * bitwise reproducible on its own. */
 typedef enum {
   DASH_KERNEL_AUTO = 0,
   DASH_KERNEL_ONE_WAVE_PER_SIMD = 1,
