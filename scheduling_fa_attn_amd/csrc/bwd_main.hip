@@ -388,9 +388,9 @@ bwd_main_kernel(BwdParams p) {
     auto reduce_wait = [&](Pending& pd) __attribute__((always_inline)) {
       if (reduce_needs_turn(pd)) {
         if (cross) {
-          // No acquire fence after the wait: the running sums are read with device-scope
-          // loads, which see the other XCD's device-scope stores by themselves.
-          pd.go = wait_turn(pd.sem, pd.rank, p.err, p.timeout_ticks, false);
+          // The running sums are then read with device-scope loads, which see the other
+          // XCD's device-scope stores without a fence.
+          pd.go = wait_turn(pd.sem, pd.rank, p.err, p.timeout_ticks);
         } else {
           pd.go = wait_turn_local(pd.sem, pd.rank, p.err, p.timeout_ticks);
         }

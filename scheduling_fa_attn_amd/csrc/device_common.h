@@ -143,10 +143,10 @@ __device__ __forceinline__ void wait_mem_done() {
 // wait timed out or another wave reported an error; the caller then skips its
 // reduction step but keeps going, so that every barrier is still reached and the
 // kernel drains. Semaphores are read with agent-scope loads, which skip the CU's L1
-// and are served by the L2. With `cross_xcd` the contributors of one dQ tile may sit
-// on different XCDs, whose L2s are not coherent with each other: then an
-// agent-scope acquire fence (L2 invalidate) follows the wait.
-__device__ bool wait_turn(const int* sem, int want, int* err, long long timeout_ticks, bool cross_xcd) {
+// and see the latest device-scope store from any XCD. No fence follows: the data the
+// turn guards must itself be read with device-scope loads when the writer may sit on
+// another XCD (whose L2 is not coherent with this one's).
+__device__ bool wait_turn(const int* sem, int want, int* err, long long timeout_ticks) {
   const long long t0 = wall_clock64();
   int iter = 0;
   while (true) {
@@ -161,7 +161,6 @@ __device__ bool wait_turn(const int* sem, int want, int* err, long long timeout_
     }
     __builtin_amdgcn_s_sleep(1);
   }
-  if (cross_xcd) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return true;
 }
