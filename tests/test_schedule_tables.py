@@ -316,14 +316,18 @@ def test_varlen_table_argument_errors():
         dash.dash_schedule_table_varlen(2, 2, 2, 256, (256, 192), "causal", "sym_shift", 8, 32)  # 3 tiles of 64
 
 
+@pytest.mark.parametrize("N,lens", [(1024, [1024, 600, 513, 1000, 777, 512]), (448, [448, 130, 64, 1, 320, 65])],
+                         ids=["tile128", "tile64"])
 @pytest.mark.parametrize("B,topology", [(3, (8, 32)), (6, (2, 4))], ids=["banded", "shared"])
-def test_varlen_layouts_valid(B, topology):
+def test_varlen_layouts_valid(B, topology, N, lens):
     """Up to one batch per slot of a domain: batches on disjoint bands of slots (no CU
     runs two batches); more batches than slots: shared CUs, batches in order. Both merged
-    tables pass the per-batch validator and are acyclic."""
+    tables pass the per-batch validator (at the padded length's tile size) and are
+    acyclic."""
     X, S = topology
-    H, Hkv, N = 2, 1, 1024
-    lens = [1024, 600, 513, 1000, 777, 512][:B]
+    H, Hkv = 2, 1
+    lens = lens[:B]
+    tile = dash.dash_tile_size(N)
     rec, _ = dash.dash_schedule_table_varlen(B, H, Hkv, N, lens, "causal", "descending", X, S)
     per_cu = {}
     for w, b in rec[:, :2].tolist():
@@ -335,7 +339,7 @@ def test_varlen_layouts_valid(B, topology):
     for b, nb in enumerate(lens):
         part = rec[rec[:, 1] == b].copy()
         part[:, 1] = 0
-        table = to_table(part, 1, H, Hkv, max(nb, 512), "causal", "descending", X * S)
-        table["n"] = -(-nb // 128)
+        table = to_table(part, 1, H, Hkv, max(nb, 512) if tile == 128 else nb, "causal", "descending", X * S)
+        table["n"] = -(-nb // tile)
         osch.validate(table)
     assert osch.simulate(to_table(rec, B, H, Hkv, N, "causal", "descending", X * S), 1.0, 0.5) > 0
