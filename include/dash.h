@@ -106,6 +106,16 @@ typedef enum {
  * or DASH_ERR_INVALID_ARG for another value. */
 int dash_set_kernel(int kernel);
 
+/* Sets the bound of every wait inside the backward kernels of later calls (the ordered
+ * reduction's turn waits and the two-waves kernel's in-step handoff), in microseconds,
+ * 0 .. 3.6e9 (default 5 000 000 = 5 s; library-wide, thread-safe). A wait that runs past
+ * it (checked every few dozen polls, so 0 means "a few dozen polls") records
+ * DASH_ERR_TIMEOUT for dash_last_kernel_error and gives up; every other wave then stops
+ * waiting too, the kernels drain, and the outputs of that call are undefined. For
+ * callers with a watchdog of their own and for tests of the error path. Returns DASH_OK,
+ * or DASH_ERR_INVALID_ARG for a value outside the range. */
+int dash_set_wait_timeout(long long microseconds);
+
 /* Bytes of caller-provided device workspace dash_attn_bwd needs for this shape:
  * an fp32 dQ accumulator of B*H*R*d floats and two fp32 row-term arrays of B*H*R
  * floats (-D with D = rowsum(dO*O), and -LSE*log2(e)), where R is N rounded up to the

@@ -176,6 +176,7 @@ std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
 int g_kernel = DASH_KERNEL_AUTO;  // main-kernel choice of later calls
+long long g_wait_timeout_us = 5000000;  // bound of every in-kernel wait (5 s)
 // DASH_SCHED_AUTO resolutions, per (B, H, Hkv, N, d, mask, XCDs, CUs per XCD, placement).
 std::map<std::tuple<int, int, int, int, int, int, int, int, int>, int> g_auto;
 // What DASH_KERNEL_AUTO resolves to where the two-waves-per-SIMD kernel applies: that
@@ -511,7 +512,11 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.xcd_local = (tab->xcd_local && st->num_xcd > 1) ? 1 : 0;
   bp.num_xcd = st->num_xcd;
   bp.cus_per_xcd = st->cus_per_xcd;
-  bp.timeout_ticks = st->ticks_per_second * 5;  // 5 seconds per wait
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    // ticks = ticks/s * us / 1e6, without overflow for any accepted timeout
+    bp.timeout_ticks = st->ticks_per_second / 1000 * g_wait_timeout_us / 1000;
+  }
   bp.prof = g_prof;
   bp.replay = nullptr;
   bp.replay_ranks = 0;
@@ -695,6 +700,13 @@ int dash_set_kernel(int kernel) {
     return DASH_ERR_INVALID_ARG;
   std::lock_guard<std::mutex> lock(g_mu);
   g_kernel = kernel;
+  return DASH_OK;
+}
+
+int dash_set_wait_timeout(long long microseconds) {
+  if (microseconds < 0 || microseconds > 3600LL * 1000000LL) return DASH_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_wait_timeout_us = microseconds;
   return DASH_OK;
 }
 

@@ -40,6 +40,7 @@ EXPORTED = (
     "dash_schedule_resolve",
     "dash_set_placement",
     "dash_set_kernel",
+    "dash_set_wait_timeout",
     "dash_attn_fwd",
 )
 
@@ -100,6 +101,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_set_placement.restype = i
     lib.dash_set_kernel.argtypes = [i]
     lib.dash_set_kernel.restype = i
+    lib.dash_set_wait_timeout.argtypes = [ctypes.c_longlong]
+    lib.dash_set_wait_timeout.restype = i
     lib.dash_attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, i, vp]
     lib.dash_attn_fwd.restype = i
     if hasattr(lib, "dash_profile_attach"):
@@ -144,6 +147,11 @@ def dash_set_kernel(kernel, lib=None) -> int:
     SIMD, every configuration) or "two_waves" (two waves per SIMD, 128-row tiles with the
     ordered or atomic reduction; other calls keep the one-wave kernel)."""
     return int((lib or load()).dash_set_kernel(KERNELS.get(kernel, kernel)))
+
+
+def dash_set_wait_timeout(microseconds, lib=None) -> int:
+    """Bound of every in-kernel wait of later calls, in microseconds (default 5 s)."""
+    return int((lib or load()).dash_set_wait_timeout(int(microseconds)))
 
 
 def dash_schedule_makespan(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd, c, r_local, r_remote, lib=None):

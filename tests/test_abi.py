@@ -149,6 +149,18 @@ def test_kernel_selection_arguments():
         dash.dash_set_kernel("auto")
 
 
+def test_wait_timeout_arguments():
+    """dash_set_wait_timeout accepts 0 .. 3.6e9 microseconds and rejects values outside;
+    restored here to the default (5 s)."""
+    try:
+        for us in (0, 1, 5_000_000, 3_600_000_000):
+            assert dash.dash_set_wait_timeout(us) == dash.DASH_OK
+        for bad in (-1, 3_600_000_001, -(1 << 40)):
+            assert dash.dash_set_wait_timeout(bad) == dash.DASH_ERR_INVALID_ARG
+    finally:
+        assert dash.dash_set_wait_timeout(5_000_000) == dash.DASH_OK
+
+
 def test_schedule_model_arguments():
     """The host-only model calls check their arguments like the table export."""
     assert dash.dash_schedule_resolve(1, 2, 2, 256, 64, "full", "shift", 1, 4) == 2
