@@ -29,11 +29,19 @@
  * - `stream` is a hipStream_t (0 = the null stream). Calls return after enqueueing.
  * - All argument checks run before anything is enqueued: on an error return no
  *   kernel is launched and the outputs are untouched.
- * - The library owns, per device, a schedule-table cache (built on the first call
- *   for a given shape, mask and schedule; the build copies the table to the
- *   device synchronously) and a 4-byte device error word. Both live until the
- *   process ends. The cache is guarded by a mutex; calls from several host
- *   threads are safe, but two calls that share a workspace must not overlap.
+ * - The library owns, per device: a schedule-table cache for dash_attn_bwd (built on
+ *   the first call for a given shape, mask, schedule and placement; that first call
+ *   allocates the table and copies it to the device synchronously, later calls with the
+ *   same key neither allocate nor synchronise); a pinned host staging ring (64 MiB,
+ *   allocated on the first call on the device) from which dash_attn_bwd_varlen copies
+ *   its per-call table into the caller's workspace in stream order; and a pinned host
+ *   word for dash_last_kernel_error. All live until the process ends. Host state is
+ *   guarded by a mutex; calls from several host threads are safe, but two calls that
+ *   share a workspace must not overlap.
+ * - Kernel-side errors (a bounded wait that timed out, a workgroup on an unexpected
+ *   XCD slot) are written to an error word inside the call's workspace, which the call
+ *   itself clears in stream order before its kernels run: an error never leaks into a
+ *   later call. dash_last_kernel_error(stream) reads it.
  */
 #ifndef DASH_H
 #define DASH_H
@@ -119,10 +127,16 @@ int dash_set_wait_timeout(long long microseconds);
 /* Bytes of caller-provided device workspace dash_attn_bwd needs for this shape:
  * an fp32 dQ accumulator of B*H*R*d floats and two fp32 row-term arrays of B*H*R
  * floats (-D with D = rowsum(dO*O), and -LSE*log2(e)), where R is N rounded up to the
- * tile (dash_tile_size), plus the int32 ordering semaphores and XCD slot counters.
- * The contents are the library's own between calls (the accumulator is kept in the
- * matrix-core accumulator order, not row-major). Returns 0 for invalid sizes. */
+ * tile (dash_tile_size), plus the int32 ordering semaphores, XCD slot counters and the
+ * call's error word. The contents are the library's own between calls (the accumulator
+ * is kept in the matrix-core accumulator order, not row-major). Returns 0 for invalid
+ * sizes. */
 size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
+
+/* Bytes of workspace dash_attn_bwd_varlen needs for a padded batch of these sizes: the
+ * dash_attn_bwd workspace plus a region for the call's schedule table (an upper bound
+ * for any batch lengths: B*H*ceil(N/tile)^2 tasks). Returns 0 for invalid sizes. */
+size_t dash_attn_bwd_varlen_workspace_size(int B, int H, int Hkv, int N, int d);
 
 /* The backward pass (DASH, section 2.1; the schedules of section 3).
  * deterministic = 1: dQ partial sums are added in the schedule's fixed order; the
@@ -138,7 +152,7 @@ size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
  * softmax_scale must be finite and > 0 (1/sqrt(d) for standard attention).
  * B == 0 or N == 0 is a no-op that returns DASH_OK.
  * Errors: DASH_ERR_INVALID_ARG, _UNSUPPORTED, _WORKSPACE, _NOT_CORESIDENT, _HIP.
- * Kernel-side failures (a timed-out wait) are reported by dash_last_kernel_error. */
+ * Kernel-side failures (a timed-out wait) are reported by dash_last_kernel_error(stream). */
 int dash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                   const void* dO, const float* lse,
                   void* dq, void* dk, void* dv,
@@ -169,10 +183,14 @@ int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void*
  * if the launch fails. */
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Hkv, int N, int d, float softmax_scale, int mask, void* stream);
-/* Synchronizes the current device, returns the device error word left by the
- * kernels since the last call (DASH_OK, DASH_ERR_TIMEOUT or DASH_ERR_PLACEMENT)
- * and clears it. Returns DASH_ERR_HIP if the synchronization itself fails. */
-int dash_last_kernel_error(void);
+/* Kernel-side status of the last backward call (dash_attn_bwd, _timed or _varlen)
+ * enqueued on `stream` (a hipStream_t; 0 = the null stream) on the current device:
+ * synchronizes that stream only, then returns the error word in that call's workspace
+ * (DASH_OK, DASH_ERR_TIMEOUT or DASH_ERR_PLACEMENT). That workspace must still be
+ * allocated and must not have been handed to another call since. DASH_OK when no
+ * backward call was enqueued on the stream; DASH_ERR_HIP if the copy or the
+ * synchronization fails. Reading does not clear the word (the next call clears it). */
+int dash_last_kernel_error(void* stream);
 
 /* Human-readable name of a status code (static storage; never null). */
 const char* dash_status_string(int status);
@@ -207,7 +225,12 @@ int dash_schedule_table(int B, int H, int Hkv, int N, int mask, int schedule,
  * unchanged, and those rows of the inputs are never read as data. The schedule applies
  * per batch (DASH_SCHED_AUTO: the model's choice at each batch's length).
  * Every deterministic mode, tile size and main kernel is supported. The workspace is
- * dash_attn_bwd_workspace_size(B, H, Hkv, N, d). Errors: as dash_attn_bwd, and
+ * dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d): the call's table (built on the
+ * host, its image cached for the 64 most recent length vectors) is copied into it on
+ * `stream` from the library's pinned staging ring, so the call allocates no device
+ * memory and does not wait for the device (except when more tables than the ring holds
+ * are still queued, or one table is larger than the ring, which then grows).
+ * Errors: as dash_attn_bwd, and
  * DASH_ERR_INVALID_ARG for a null seqlens or a length outside [1, N]; symmetric shift
  * needs an even tile count (of the padded length's tile size) in every batch. */
 int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const void* dO,

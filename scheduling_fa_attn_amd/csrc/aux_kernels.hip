@@ -12,8 +12,9 @@ namespace dash {
 // ---------------------------------------------------------------------------------
 // Preprocess: -D[row] = -sum_e dO[row, e] * O[row, e] in fp32 with a fixed reduction
 // tree and nl[row] = -LSE[row] * log2(e), stored with the head's rows padded to the
-// tile (padding: -D = 0, nl = -inf); clears the ordering semaphores and the XCD
-// slot counters; for the atomic variant also clears the fp32 dQ accumulator.
+// tile (padding: -D = 0, nl = -inf); clears the ordering semaphores, the XCD slot
+// counters and the call's error word; for the atomic variant also clears the fp32 dQ
+// accumulator.
 // (-D is stored negated because the main kernel starts its dP = dO V^T accumulation
 // from it, which yields dP - D directly.)
 // ---------------------------------------------------------------------------------
@@ -56,6 +57,7 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   }
   for (int64_t x = tid; x < p.sem_count; x += nthreads) p.sem[x] = 0;
   for (int64_t x = tid; x < p.ctr_count; x += nthreads) p.ctr[x] = 0;
+  if (tid == 0) *p.err = 0;
   if (p.dqacc_zero) {
     floatx4* z = reinterpret_cast<floatx4*>(p.dqacc_zero);
     const floatx4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -183,8 +185,7 @@ hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;
   void* args[] = {&out};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(topology_probe_kernel), dim3(grid), dim3(64),
-                                    args, shmem, stream);
+  return launch_resident(reinterpret_cast<const void*>(topology_probe_kernel), grid, 64, shmem, args, stream);
 }
 
 }  // namespace dash

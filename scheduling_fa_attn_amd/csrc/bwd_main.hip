@@ -101,7 +101,7 @@ struct BwdCfg {
 // stores (no whole-L2 write-back or invalidate); otherwise every chain stays inside one
 // XCD's L2. NODQ (with !DET): dK and dV
 // only, no dQ work at all (the two-pass variant computes dQ in a separate kernel).
-template <int D, int NW, bool DET, bool CROSS, bool NODQ>
+template <int D, int NW, bool DET, bool CROSS, bool NODQ, bool PART>
 __global__ void __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 bwd_main_kernel(BwdParams p) {
   using C = BwdCfg<D, NW>;
@@ -142,6 +142,7 @@ bwd_main_kernel(BwdParams p) {
   constexpr bool cross = CROSS;
   static_assert(DET || !CROSS, "device-scope chains exist only in the ordered reduction");
   static_assert(!(DET && NODQ), "the ordered reduction reduces dQ");
+  static_assert(!PART || (DET && !CROSS), "per-tile partials: stores into slots, no chains");
   bool failed = false;  // this wave gave up waiting (error reported); it keeps going without reducing
   // The schedule table is read-only for the whole launch: reading it through the
   // constant address space turns its uniform loads into scalar loads, which are
@@ -286,7 +287,7 @@ bwd_main_kernel(BwdParams p) {
 #ifdef DASH_REPLAY
     constexpr bool kZeroStart = true;
 #else
-    constexpr bool kZeroStart = !DET;
+    constexpr bool kZeroStart = !DET || PART;
 #endif
     auto dq_mma = [&](floatx16& acc, int kk, const bf16x8& a, const bf16x8& b) __attribute__((always_inline)) {
       if (kZeroStart && kk == 0)
@@ -367,7 +368,13 @@ bwd_main_kernel(BwdParams p) {
       const int q0s = rec.y;
       const int64_t bh = rec.x;
       // Accumulator rows are padded to the tile, so the step's blocks always exist.
-      pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
+      if (PART) {
+        // Per-tile partials: the step's own slot, (b * H + h, step, rank), in the compact
+        // layout described at kDqBlock.
+        pd.acc_blk = p.dqacc + partial_slot(bh, q0s, pd.rank, p.row_stride / BC, BC, p.causal) * (2 * DB) * kDqBlock;
+      } else {
+        pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
+      }
       pd.go = !failed;
       pd.acc_rs = DET ? make_rsrc(pd.acc_blk, pd.go ? 2 * DB * kBlkBytes : 0)
                       : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, pd.go ? 64 * D * 4 : 0);
@@ -382,7 +389,7 @@ bwd_main_kernel(BwdParams p) {
     };
     // Does this contribution have to wait for its turn at all?
     auto reduce_needs_turn = [&](const Pending& pd) __attribute__((always_inline)) {
-      return DET && pd.go && pd.rank > 0;
+      return DET && !PART && pd.go && pd.rank > 0;
     };
     // Blocking wait for the turn.
     auto reduce_wait = [&](Pending& pd) __attribute__((always_inline)) {
@@ -402,7 +409,7 @@ bwd_main_kernel(BwdParams p) {
     // atomic variant) reads through an empty descriptor, which returns zeros without
     // touching memory.
     auto reduce_load = [&](const Pending& pd, floatx16 (&ld)[C::NBLK]) __attribute__((always_inline)) {
-      if (!DET) {
+      if (!DET || PART) {
         // The atomic variant adds partials from zero (kZeroStart) and issues no load: a
         // load would make the next wait for it also wait for every float atomic issued
         // before it.
@@ -435,7 +442,7 @@ bwd_main_kernel(BwdParams p) {
 #ifdef DASH_REPLAY
       if (!pd.go) return;
       floatx16 v = v_in;
-      if (DET) {
+      if (DET && !PART) {
         if (pd.dump) {
           u32x4 x;
 #pragma unroll
@@ -487,7 +494,7 @@ bwd_main_kernel(BwdParams p) {
     // Call after wait_mem_done(): this wave's accumulator stores have been acknowledged
     // (in the L2, or past it for device-scope stores), so the turn can be passed on.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
-      if (!DET || !pd.go || pd.last) return;
+      if (!DET || PART || !pd.go || pd.last) return;
       if (lane == 0) {
         // Writer and reader share this XCD's L2, where the acknowledged stores already
         // are: a plain store into the L2 suffices, and the next contributor's poll then
@@ -929,17 +936,17 @@ static hipError_t launch_main_t(const BwdParams& prm, int grid, hipStream_t stre
   using C = BwdCfg<D, NW>;
   // At least 81 KiB of LDS so that exactly one workgroup fits on a CU.
   const int shmem = C::BYTES > 83 * 1024 ? C::BYTES : 83 * 1024;
-  auto fn = prm.deterministic == 2 ? bwd_main_kernel<D, NW, false, false, true>
-            : !prm.deterministic     ? bwd_main_kernel<D, NW, false, false, false>
-            : prm.xcd_local          ? bwd_main_kernel<D, NW, true, false, false>
-                                     : bwd_main_kernel<D, NW, true, true, false>;
+  auto fn = prm.deterministic == 2 ? bwd_main_kernel<D, NW, false, false, true, false>
+            : prm.deterministic == 3 ? bwd_main_kernel<D, NW, true, false, false, true>
+            : !prm.deterministic     ? bwd_main_kernel<D, NW, false, false, false, false>
+            : prm.xcd_local          ? bwd_main_kernel<D, NW, true, false, false, false>
+                                     : bwd_main_kernel<D, NW, true, true, false, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;
   BwdParams local = prm;
   void* args[] = {&local};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(NW * 64), args,
-                                    shmem, stream);
+  return launch_resident(reinterpret_cast<const void*>(fn), grid, NW * 64, shmem, args, stream);
 }
 
 // One (d, waves) instantiation per translation unit, selected by DASH_MAIN_D and

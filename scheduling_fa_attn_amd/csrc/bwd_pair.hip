@@ -105,7 +105,7 @@ struct PairCfg {
 // Body of the kernel for one role (ROLE_A: waves 0-3, else waves 4-7). Each role is
 // its own inlined copy, so that the register allocator never sees the values of one
 // role live in the other's code.
-template <int D, bool DET, bool ROLE_A>
+template <int D, bool DET, bool ROLE_A, bool PART>
 __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem, int worker, int w) {
   using C = PairCfg<D>;
   constexpr int BC = C::BC, BQ = C::BQ, SUBS = C::SUBS, DB = C::DB, DK = C::DK, KK = C::KK, ST = C::ST;
@@ -252,7 +252,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #ifdef DASH_REPLAY
     constexpr bool kZeroStart = true;
 #else
-    constexpr bool kZeroStart = !DET;
+    constexpr bool kZeroStart = !DET || PART;
 #endif
     auto dq_mma = [&](floatx16& a, int kk, const bf16x8& x, const bf16x8& y) __attribute__((always_inline)) {
       if (kZeroStart && kk == 0)
@@ -285,7 +285,13 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       pd.last = rec.w;
       const int q0s = rec.y;
       const int64_t bh = rec.x;
-      pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
+      if (PART) {
+        // Per-tile partials: the step's own slot, (b * H + h, step, rank), in the compact
+        // layout described at kDqBlock.
+        pd.acc_blk = p.dqacc + partial_slot(bh, q0s, pd.rank, p.row_stride / BC, BC, p.causal) * (2 * DB) * kDqBlock;
+      } else {
+        pd.acc_blk = p.dqacc + ((bh * (p.row_stride / 32) + q0s / 32) * DB) * kDqBlock;
+      }
       pd.go = !failed;
       pd.acc_rs = DET ? make_rsrc(pd.acc_blk, pd.go ? 2 * DB * kBlkBytes : 0)
                       : make_rsrc(p.dqacc + (bh * p.row_stride + q0s) * D, pd.go ? 64 * D * 4 : 0);
@@ -298,7 +304,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       return pd;
     };
     auto reduce_needs_turn = [&](const Pending& pd) __attribute__((always_inline)) {
-      return HAS_DQ && DET && pd.go && pd.rank > 0;
+      return HAS_DQ && DET && !PART && pd.go && pd.rank > 0;
     };
     auto reduce_wait = [&](Pending& pd) __attribute__((always_inline)) {
       if (reduce_needs_turn(pd)) {
@@ -309,7 +315,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     };
     // Running sum so far; the first contributor reads through an empty descriptor (zeros).
     auto reduce_load = [&](const Pending& pd, floatx16& ld) __attribute__((always_inline)) {
-      if (!DET || !HAS_DQ) return;
+      if (!DET || PART || !HAS_DQ) return;
       const rsrc_t lrs = make_rsrc(pd.acc_blk, reduce_needs_turn(pd) ? 2 * DB * kBlkBytes : 0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -329,7 +335,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #ifdef DASH_REPLAY
       if (!pd.go) return;
       floatx16 v = v_in;
-      if (DET) {
+      if (DET && !PART) {
         if (pd.dump) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -375,14 +381,14 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     };
     // After wait_mem_done(): this wave's accumulator stores are in the L2.
     auto reduce_signal = [&](const Pending& pd) __attribute__((always_inline)) {
-      if (!HAS_DQ || !DET || !pd.go || pd.last) return;
+      if (!HAS_DQ || !DET || PART || !pd.go || pd.last) return;
       if (lane == 0)
         __builtin_amdgcn_raw_buffer_store_b32(static_cast<unsigned>(pd.rank + 1), make_rsrc(pd.sem, 4), 0, 0, 0);
     };
     // Poll of the turn: a plain load whose value is read later (issued on every step,
     // through an empty descriptor when no turn is needed).
     auto reduce_poll = [&](const Pending& pd) __attribute__((always_inline)) -> int {
-      if (!DET || !HAS_DQ) return 0;
+      if (!DET || PART || !HAS_DQ) return 0;
       const rsrc_t srs = make_rsrc(pd.sem, reduce_needs_turn(pd) ? 4 : 0);
       return static_cast<int>(__builtin_amdgcn_raw_buffer_load_b32(srs, 0, 0, kSC0));
     };
@@ -803,8 +809,9 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 }
 
 // DET: ordered reduction inside one XCD's L2 (every dQ tile's contributors share an
-// XCD), or float atomics. One kernel each.
-template <int D, bool DET>
+// XCD), or float atomics; PART (with DET): every contribution to its own slot of the
+// per-tile partials buffer, no turns (a separate kernel adds them). One kernel each.
+template <int D, bool DET, bool PART>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_pair_kernel(BwdParams p) {
   using C = PairCfg<D>;
@@ -829,23 +836,24 @@ bwd_pair_kernel(BwdParams p) {
   const int worker = sMisc[0];
   if (worker < 0) return;
   if (w < 4)
-    pair_body<D, DET, true>(p, smem, worker, w);
+    pair_body<D, DET, true, PART>(p, smem, worker, w);
   else
-    pair_body<D, DET, false>(p, smem, worker, w);
+    pair_body<D, DET, false, PART>(p, smem, worker, w);
 }
 
 template <int D>
 static hipError_t launch_pair_t(const BwdParams& prm, int grid, hipStream_t stream) {
   using C = PairCfg<D>;
   const int shmem = C::BYTES;
-  auto fn = prm.deterministic ? bwd_pair_kernel<D, true> : bwd_pair_kernel<D, false>;
+  auto fn = prm.deterministic == 3 ? bwd_pair_kernel<D, true, true>
+            : prm.deterministic   ? bwd_pair_kernel<D, true, false>
+                                  : bwd_pair_kernel<D, false, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;
   BwdParams local = prm;
   void* args[] = {&local};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(grid), dim3(C::NT), args, shmem,
-                                    stream);
+  return launch_resident(reinterpret_cast<const void*>(fn), grid, C::NT, shmem, args, stream);
 }
 
 hipError_t launch_pair_d128(const BwdParams& prm, int grid, hipStream_t stream) {

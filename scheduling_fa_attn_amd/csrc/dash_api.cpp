@@ -8,6 +8,8 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <deque>
+#include <list>
 #include <map>
 #include <mutex>
 #include <string>
@@ -23,6 +25,9 @@ using dash::Sched;
 
 constexpr int kCtrInts = 16 * 64;  // one 256-byte line per XCD slot counter
 constexpr int64_t kMaxTasks = int64_t(1) << 30;
+// Initial size of a device's pinned staging ring for variable-length tables (the table
+// of 16 384 tokens at hidden size 2048 is about 2 MB).
+constexpr size_t kStagingBytes = size_t(64) << 20;
 
 int tile_for(int N) { return N < 512 ? 64 : 128; }
 
@@ -31,7 +36,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct WsLayout {
-  size_t dqacc = 0, neg_delta = 0, nlse2 = 0, sem = 0, ctr = 0, total = 0;
+  size_t dqacc = 0, neg_delta = 0, nlse2 = 0, sem = 0, ctr = 0, err = 0, total = 0;
   int sem_stride = 0;
   int row_stride = 0;  // rows per head of -D, -LSE*log2(e) and the dQ accumulator: N rounded up to the tile
 };
@@ -51,7 +56,8 @@ WsLayout ws_layout(int B, int H, int N, int d) {
   L.nlse2 = L.neg_delta + row_bytes;
   L.sem = L.nlse2 + row_bytes;
   L.ctr = L.sem + sem_bytes;
-  L.total = L.ctr + kCtrInts * sizeof(int);
+  L.err = L.ctr + kCtrInts * sizeof(int);  // the call's error word, on a 256-byte line of its own
+  L.total = L.err + 256;
   return L;
 }
 
@@ -165,13 +171,28 @@ struct DeviceState {
   int cus = 0;
   int num_xcd = 1;
   int cus_per_xcd = 1;
-  int* err = nullptr;
   long long ticks_per_second = 100000000LL;
+  // Error word of the last backward call enqueued on each stream (in that call's
+  // workspace), for dash_last_kernel_error; host bookkeeping only.
+  std::map<void*, const int*> last_err;
+  int* err_host = nullptr;  // pinned word that dash_last_kernel_error copies into (g_err_mu)
   std::map<std::tuple<int, int, int, int, int, int, int, int>, DevTable> tables;
-  std::map<std::vector<int>, DevTable> varlen_tables;  // variable-length batches
+  // Variable-length batches: pinned staging for the stream-ordered table copies into the
+  // caller's workspace (allocated at device set-up, grown only for a table larger than it).
+  struct Staging {
+    char* buf = nullptr;
+    size_t cap = 0;
+    struct Seg {
+      size_t off, size;
+      hipEvent_t done;  // recorded on the call's stream after the copy
+    };
+    std::deque<Seg> inflight;  // in enqueue order
+    std::vector<hipEvent_t> idle_events;
+  } staging;
 };
 
 std::mutex g_mu;
+std::mutex g_err_mu;  // the pinned words of dash_last_kernel_error
 std::map<int, DeviceState> g_devices;
 unsigned long long* g_prof = nullptr;  // profiling builds: device buffer for the phase counters
 int g_placement = DASH_PLACEMENT_AGGREGATE;  // CU-group placement of later tables
@@ -194,14 +215,14 @@ int init_device(int dev, DeviceState* st) {
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return DASH_ERR_HIP;
   st->cus = prop.multiProcessorCount;
-  int coop = 0;
-  if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop)
-    return DASH_ERR_NOT_CORESIDENT;
   int rate_khz = 0;
   if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && rate_khz > 0)
     st->ticks_per_second = static_cast<long long>(rate_khz) * 1000LL;
-  if (hipMalloc(reinterpret_cast<void**>(&st->err), 256) != hipSuccess) return DASH_ERR_HIP;
-  if (hipMemset(st->err, 0, 256) != hipSuccess) return DASH_ERR_HIP;
+  if (hipHostMalloc(reinterpret_cast<void**>(&st->err_host), sizeof(int), hipHostMallocDefault) != hipSuccess)
+    return DASH_ERR_HIP;
+  if (hipHostMalloc(reinterpret_cast<void**>(&st->staging.buf), kStagingBytes, hipHostMallocDefault) != hipSuccess)
+    return DASH_ERR_HIP;
+  st->staging.cap = kStagingBytes;
   int* probe = nullptr;
   if (hipMalloc(reinterpret_cast<void**>(&probe), sizeof(int) * st->cus) != hipSuccess) return DASH_ERR_HIP;
   hipError_t e = dash::launch_topology_probe(probe, st->cus, nullptr);
@@ -286,8 +307,18 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   return DASH_OK;
 }
 
-// Device copy of a table: worker_begin | items | tasks | step records | batch lengths.
-int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* lens, DevTable* out) {
+// Host image of a device table: worker_begin | items | tasks | step records | batch lengths,
+// each part 256-byte aligned.
+struct TableImage {
+  std::vector<char> bytes;
+  size_t it_off = 0, tk_off = 0, st_off = 0, ln_off = 0;
+  bool has_lens = false;
+  int workers = 0;
+  int tile = 0;
+  bool xcd_local = true;
+};
+
+void make_image(const dash::Table& t, int H, int tile, const std::vector<int>* lens, TableImage* img) {
   const size_t wb_bytes = align256(sizeof(int32_t) * t.worker_begin.size());
   const size_t it_bytes = align256(sizeof(dash::Item) * t.items.size());
   const size_t tk_bytes = align256(sizeof(dash::Task) * (t.tasks.size() + 1));
@@ -308,29 +339,50 @@ int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* 
   steps.push_back(int4{0, 0, 0, 0});
   const size_t st_bytes = align256(sizeof(int4) * steps.size());
   const size_t ln_bytes = lens ? align256(sizeof(int) * lens->size()) : 0;
-  std::vector<char> host(wb_bytes + it_bytes + tk_bytes + st_bytes + ln_bytes, 0);
-  if (lens) std::memcpy(host.data() + wb_bytes + it_bytes + tk_bytes + st_bytes, lens->data(), sizeof(int) * lens->size());
-  std::memcpy(host.data(), t.worker_begin.data(), sizeof(int32_t) * t.worker_begin.size());
-  std::memcpy(host.data() + wb_bytes, t.items.data(), sizeof(dash::Item) * t.items.size());
-  if (!t.tasks.empty())
-    std::memcpy(host.data() + wb_bytes + it_bytes, t.tasks.data(), sizeof(dash::Task) * t.tasks.size());
-  std::memcpy(host.data() + wb_bytes + it_bytes + tk_bytes, steps.data(), sizeof(int4) * steps.size());
+  img->it_off = wb_bytes;
+  img->tk_off = wb_bytes + it_bytes;
+  img->st_off = img->tk_off + tk_bytes;
+  img->ln_off = img->st_off + st_bytes;
+  img->has_lens = lens != nullptr;
+  img->bytes.assign(img->ln_off + ln_bytes, 0);
+  char* h = img->bytes.data();
+  std::memcpy(h, t.worker_begin.data(), sizeof(int32_t) * t.worker_begin.size());
+  std::memcpy(h + img->it_off, t.items.data(), sizeof(dash::Item) * t.items.size());
+  if (!t.tasks.empty()) std::memcpy(h + img->tk_off, t.tasks.data(), sizeof(dash::Task) * t.tasks.size());
+  std::memcpy(h + img->st_off, steps.data(), sizeof(int4) * steps.size());
+  if (lens) std::memcpy(h + img->ln_off, lens->data(), sizeof(int) * lens->size());
+  img->workers = t.workers;
+  img->tile = tile;
+  img->xcd_local = t.xcd_local;
+}
+
+// The table's device pointers once its image sits at `base` in device memory.
+DevTable table_at(const TableImage& img, void* base) {
   DevTable dt;
-  if (hipMalloc(&dt.buf, host.size()) != hipSuccess) return DASH_ERR_HIP;
-  if (hipMemcpy(dt.buf, host.data(), host.size(), hipMemcpyHostToDevice) != hipSuccess) {
-    (void)hipFree(dt.buf);
+  char* b = static_cast<char*>(base);
+  dt.buf = base;
+  dt.worker_begin = reinterpret_cast<const int*>(b);
+  dt.items = reinterpret_cast<const int4*>(b + img.it_off);
+  dt.tasks = reinterpret_cast<const int4*>(b + img.tk_off);
+  dt.steps = reinterpret_cast<const int4*>(b + img.st_off);
+  dt.seqlens = img.has_lens ? reinterpret_cast<const int*>(b + img.ln_off) : nullptr;
+  dt.workers = img.workers;
+  dt.tile = img.tile;
+  dt.xcd_local = img.xcd_local;
+  return dt;
+}
+
+// Device copy of a table in library-owned memory (the per-shape cache; built once).
+int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* lens, DevTable* out) {
+  TableImage img;
+  make_image(t, H, tile, lens, &img);
+  void* buf = nullptr;
+  if (hipMalloc(&buf, img.bytes.size()) != hipSuccess) return DASH_ERR_HIP;
+  if (hipMemcpy(buf, img.bytes.data(), img.bytes.size(), hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(buf);
     return DASH_ERR_HIP;
   }
-  char* base = static_cast<char*>(dt.buf);
-  dt.worker_begin = reinterpret_cast<const int*>(base);
-  dt.items = reinterpret_cast<const int4*>(base + wb_bytes);
-  dt.tasks = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes);
-  dt.steps = reinterpret_cast<const int4*>(base + wb_bytes + it_bytes + tk_bytes);
-  dt.seqlens = lens ? reinterpret_cast<const int*>(base + wb_bytes + it_bytes + tk_bytes + st_bytes) : nullptr;
-  dt.workers = t.workers;
-  dt.tile = tile;
-  dt.xcd_local = t.xcd_local;
-  *out = dt;
+  *out = table_at(img, buf);
   return DASH_OK;
 }
 
@@ -340,16 +392,39 @@ int upload_table(const dash::Table& t, int H, int tile, const std::vector<int>* 
 int varlen_model_len(int N, int len) { return tile_for(N) == 128 && len < 512 ? 512 : len; }
 bool varlen_odd_tiles(int N, int len) { return cdiv(len, tile_for(N)) % 2 != 0; }
 
-// Variable-length batches: the table of dash::build_table_varlen, cached per lengths.
-int get_table_varlen(DeviceState* st, int B, int H, int Hkv, int N, bool causal, const std::vector<int>& lens,
-                     const std::vector<int>& scheds, const DevTable** out) {
-  std::vector<int> key = {B, H, Hkv, N, causal ? 1 : 0, g_placement};
+// Workers a variable-length table is built for at most (compute units of the device; an
+// MI355X has 256).
+constexpr int kMaxWorkers = 1024;
+
+// Bytes of the workspace region that holds a variable-length batch's table: an upper
+// bound of the image of any such table for these sizes (every batch at the padded length
+// and the full mask: B * H * n^2 tasks, B * Hkv * n items).
+size_t varlen_table_bound(int B, int H, int Hkv, int N) {
+  const int tile = tile_for(N);
+  const int64_t n = cdiv(N, tile);
+  const int64_t tasks = int64_t(B) * H * n * n;
+  const int64_t items = int64_t(B) * Hkv * n + 1;
+  const int64_t steps = tasks * (tile / 64) + 2;
+  return align256(sizeof(int32_t) * (kMaxWorkers + 1)) + align256(16 * items) + align256(16 * (tasks + 1)) +
+         align256(16 * steps) + align256(sizeof(int) * size_t(B));
+}
+
+// Host images of variable-length tables, most recently used first (bounded; an image is
+// rebuilt when its lengths come back after eviction).
+constexpr size_t kVarlenImages = 64;
+std::list<std::pair<std::vector<int>, TableImage>> g_varlen_images;
+
+int varlen_image(DeviceState* st, int B, int H, int Hkv, int N, bool causal, const std::vector<int>& lens,
+                 const std::vector<int>& scheds, const TableImage** out) {
+  std::vector<int> key = {st->num_xcd, st->cus_per_xcd, B, H, Hkv, N, causal ? 1 : 0, g_placement};
   key.insert(key.end(), lens.begin(), lens.end());
   key.insert(key.end(), scheds.begin(), scheds.end());
-  auto found = st->varlen_tables.find(key);
-  if (found != st->varlen_tables.end()) {
-    *out = &found->second;
-    return DASH_OK;
+  for (auto it = g_varlen_images.begin(); it != g_varlen_images.end(); ++it) {
+    if (it->first == key) {
+      g_varlen_images.splice(g_varlen_images.begin(), g_varlen_images, it);
+      *out = &g_varlen_images.front().second;
+      return DASH_OK;
+    }
   }
   dash::SchedParams sp;
   sp.B = B;
@@ -367,11 +442,80 @@ int get_table_varlen(DeviceState* st, int B, int H, int Hkv, int N, bool causal,
   std::string err;
   const int s = dash::build_table_varlen(sp, lens, kinds, &t, &err);
   if (s != 0) return s < 0 ? DASH_ERR_INVALID_ARG : s;
-  DevTable dt;
-  const int u = upload_table(t, H, sp.tile, &lens, &dt);
-  if (u != DASH_OK) return u;
-  auto ins = st->varlen_tables.emplace(key, dt);
-  *out = &ins.first->second;
+  if (t.workers > kMaxWorkers) return DASH_ERR_UNSUPPORTED;
+  g_varlen_images.emplace_front(key, TableImage());
+  make_image(t, H, sp.tile, &lens, &g_varlen_images.front().second);
+  if (g_varlen_images.size() > kVarlenImages) g_varlen_images.pop_back();
+  *out = &g_varlen_images.front().second;
+  return DASH_OK;
+}
+
+// Copies `img` to `dst` (device memory) on `stream` through the device's pinned staging
+// ring: the image goes into a free part of the ring and an asynchronous copy, ordered on
+// the stream, moves it; an event marks the part free again once the copy has run. The
+// host waits only when the ring holds no free part of this size (copies of earlier calls
+// still queued behind other work). Caller holds g_mu.
+int stage_table(DeviceState* st, const TableImage& img, void* dst, hipStream_t stream) {
+  auto& R = st->staging;
+  const size_t size = align256(img.bytes.size());
+  auto retire_front = [&](bool wait) -> bool {
+    if (R.inflight.empty()) return false;
+    const hipError_t q = wait ? hipEventSynchronize(R.inflight.front().done) : hipEventQuery(R.inflight.front().done);
+    if (q != hipSuccess) return false;
+    R.idle_events.push_back(R.inflight.front().done);
+    R.inflight.pop_front();
+    return true;
+  };
+  while (retire_front(false)) {
+  }
+  if (size > R.cap) {
+    // A table larger than the ring: wait for the copies in flight and grow it.
+    while (retire_front(true)) {
+    }
+    if (!R.inflight.empty()) return DASH_ERR_HIP;
+    if (R.buf) (void)hipHostFree(R.buf);
+    R.buf = nullptr;
+    R.cap = 0;
+    if (hipHostMalloc(reinterpret_cast<void**>(&R.buf), size, hipHostMallocDefault) != hipSuccess) return DASH_ERR_HIP;
+    R.cap = size;
+  }
+  // The parts in flight occupy the ring from the oldest part's offset onward, in enqueue
+  // order, wrapping to 0 at most once: free space is after the newest part and, while the
+  // newest part lies after the oldest, also before the oldest.
+  size_t off = 0;
+  while (!R.inflight.empty()) {
+    const auto& first = R.inflight.front();
+    const auto& last = R.inflight.back();
+    const size_t end = last.off + last.size;
+    if (last.off >= first.off) {
+      if (end + size <= R.cap) {
+        off = end;
+        break;
+      }
+      if (size <= first.off) {
+        off = 0;
+        break;
+      }
+    } else if (end + size <= first.off) {
+      off = end;
+      break;
+    }
+    if (!retire_front(true)) return DASH_ERR_HIP;
+  }
+  std::memcpy(R.buf + off, img.bytes.data(), img.bytes.size());
+  hipEvent_t ev = nullptr;
+  if (!R.idle_events.empty()) {
+    ev = R.idle_events.back();
+    R.idle_events.pop_back();
+  } else if (hipEventCreateWithFlags(&ev, hipEventDisableTiming) != hipSuccess) {
+    return DASH_ERR_HIP;
+  }
+  if (hipMemcpyAsync(dst, R.buf + off, img.bytes.size(), hipMemcpyHostToDevice, stream) != hipSuccess ||
+      hipEventRecord(ev, stream) != hipSuccess) {
+    R.idle_events.push_back(ev);
+    return DASH_ERR_HIP;
+  }
+  R.inflight.push_back({off, size, ev});
   return DASH_OK;
 }
 
@@ -411,12 +555,15 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   if (lse == nullptr || !aligned(lse, 4)) return DASH_ERR_INVALID_ARG;
   if (workspace == nullptr || !aligned(workspace, 256)) return DASH_ERR_INVALID_ARG;
   const WsLayout L = ws_layout(B, H, N, d);
-  if (workspace_bytes < L.total) return DASH_ERR_WORKSPACE;
+  // Variable-length batches: the call's table goes into the workspace after the base part.
+  const size_t table_bytes = seqlens ? varlen_table_bound(B, H, Hkv, N) : 0;
+  if (workspace_bytes < L.total + table_bytes) return DASH_ERR_WORKSPACE;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
   const bool causal = mask == DASH_MASK_CAUSAL;
   DeviceState* st = nullptr;
   const DevTable* tab = nullptr;
+  DevTable varlen_tab;
   {
     std::lock_guard<std::mutex> lock(g_mu);
     s = get_device(&st);
@@ -448,7 +595,15 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
         scheds[b] = it->second;
         if (scheds[b] == DASH_SCHED_SYM_SHIFT && varlen_odd_tiles(N, lens[b])) scheds[b] = DASH_SCHED_DESCENDING;
       }
-      s = get_table_varlen(st, B, H, Hkv, N, causal, lens, scheds, &tab);
+      const TableImage* img = nullptr;
+      s = varlen_image(st, B, H, Hkv, N, causal, lens, scheds, &img);
+      if (s != DASH_OK) return s;
+      if (img->bytes.size() > table_bytes) return DASH_ERR_WORKSPACE;  // (the bound holds for every table)
+      void* dst = static_cast<char*>(workspace) + L.total;
+      s = stage_table(st, *img, dst, stream);
+      if (s != DASH_OK) return s;
+      varlen_tab = table_at(*img, dst);
+      tab = &varlen_tab;
     } else {
       s = get_table(st, B, H, Hkv, N, causal, schedule, &tab);
     }
@@ -460,6 +615,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   float* nlse2 = reinterpret_cast<float*>(ws + L.nlse2);
   int* sem = reinterpret_cast<int*>(ws + L.sem);
   int* ctr = reinterpret_cast<int*>(ws + L.ctr);
+  int* err = reinterpret_cast<int*>(ws + L.err);
 
   dash::PreParams pp;
   pp.o = static_cast<const __bf16*>(o);
@@ -474,6 +630,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   pp.sem_count = int64_t(B) * H * L.sem_stride;
   pp.ctr = ctr;
   pp.ctr_count = kCtrInts;
+  pp.err = err;
   pp.seqlens = tab->seqlens;
   pp.H = H;
   pp.dqacc_zero = deterministic == 0 ? dqacc : nullptr;
@@ -494,7 +651,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.dqacc = dqacc;
   bp.sem = sem;
   bp.ctr = ctr;
-  bp.err = st->err;
+  bp.err = err;
   bp.worker_begin = tab->worker_begin;
   bp.items = tab->items;
   bp.tasks = tab->tasks;
@@ -516,6 +673,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     std::lock_guard<std::mutex> lock(g_mu);
     // ticks = ticks/s * us / 1e6, without overflow for any accepted timeout
     bp.timeout_ticks = st->ticks_per_second / 1000 * g_wait_timeout_us / 1000;
+    st->last_err[stream_ptr] = err;
   }
   bp.prof = g_prof;
   bp.replay = nullptr;
@@ -589,6 +747,12 @@ size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d) {
   return ws_layout(B, H, N, d).total;
 }
 
+size_t dash_attn_bwd_varlen_workspace_size(int B, int H, int Hkv, int N, int d) {
+  const size_t base = dash_attn_bwd_workspace_size(B, H, Hkv, N, d);
+  if (base == 0) return 0;
+  return base + varlen_table_bound(B, H, Hkv, N);
+}
+
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Hkv, int N,
                   int d, float softmax_scale, int mask, void* stream) {
   if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0) return DASH_ERR_INVALID_ARG;
@@ -644,17 +808,28 @@ int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void*
                  workspace, workspace_bytes, stream, main_start, main_stop);
 }
 
-int dash_last_kernel_error(void) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-  auto found = g_devices.find(dev);
-  if (found == g_devices.end() || !found->second.ready) return DASH_OK;
-  if (hipDeviceSynchronize() != hipSuccess) return DASH_ERR_HIP;
-  int v = 0;
-  if (hipMemcpy(&v, found->second.err, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess) return DASH_ERR_HIP;
-  if (hipMemset(found->second.err, 0, sizeof(int)) != hipSuccess) return DASH_ERR_HIP;
-  return v;
+int dash_last_kernel_error(void* stream) {
+  const int* word = nullptr;
+  int* host = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+    auto found = g_devices.find(dev);
+    if (found == g_devices.end() || !found->second.ready) return DASH_OK;
+    auto w = found->second.last_err.find(stream);
+    if (w == found->second.last_err.end()) return DASH_OK;
+    word = w->second;
+    host = found->second.err_host;
+  }
+  // Only this stream is waited for: the word is copied into pinned host memory by a copy
+  // ordered after the stream's work (hipMemcpy would run on the null stream, which waits
+  // for every blocking stream of the device).
+  std::lock_guard<std::mutex> lock(g_err_mu);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(host, word, sizeof(int), hipMemcpyDeviceToHost, s) != hipSuccess) return DASH_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return DASH_ERR_HIP;
+  return *host;
 }
 
 const char* dash_status_string(int status) {

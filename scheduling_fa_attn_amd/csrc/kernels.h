@@ -4,6 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace dash {
 
 // Device error word values (match dash_status in include/dash.h).
@@ -23,6 +27,7 @@ struct PreParams {
   int64_t sem_count;
   int* ctr;            // XCD slot counters to clear
   int64_t ctr_count;
+  int* err;            // the call's device error word, cleared here
   float* dqacc_zero;   // non-null: clear this fp32 buffer (atomic variant)
   int64_t zero_count;  // elements, multiple of 4
   const int* seqlens;  // non-null: rows of batch b at or past seqlens[b] are padding
@@ -41,7 +46,7 @@ struct BwdParams {
   float* dqacc;        // fp32 dQ accumulator (layouts described at kDqBlock)
   int* sem;
   int* ctr;
-  int* err;
+  int* err;            // the call's device error word (in the workspace; 0 = no error)
   const int* worker_begin;
   const int4* items;
   const int4* tasks;
@@ -104,7 +109,25 @@ struct DqParams {
 //   operand visits them.) A wave then moves one block with four 1 KiB accesses.
 // - Atomic variant: row-major [bh][row_stride][d], so that the per-element float atomics
 //   of a wave hit whole cache lines.
+// - Per-tile partials (deterministic = 3): no accumulator; every contribution has its own
+//   slot of 2 (64 / 32) x (d / 32) blocks (one 64-row step of one Q tile from one KV tile),
+//   in the same block order. Slots of a (b, h) are ordered by Q tile j, then the step's
+//   place in the tile, then the contribution's rank; Q tile j has n contributions (full
+//   mask) or j + 1 (causal), so a head has steps_per_tile x n^2 or steps_per_tile x
+//   n (n + 1) / 2 slots (partial_slot below).
 constexpr int kDqBlock = 32 * 32;
+
+// Slot of the per-tile partial of head bh (= b * H + h), 64-row step starting at Q row
+// q0, contribution `rank`, for n tiles of `tile` rows per head.
+__host__ __device__ inline int64_t partial_slot(int64_t bh, int q0, int rank, int n, int tile, int causal) {
+  const int subs = tile / 64;
+  const int j = q0 / tile;
+  const int sub = (q0 % tile) / 64;
+  const int64_t per_head = (causal ? int64_t(n) * (n + 1) / 2 : int64_t(n) * n) * subs;
+  const int64_t before = causal ? int64_t(j) * (j + 1) / 2 : int64_t(j) * n;  // slots of earlier Q tiles / subs
+  const int cnt = causal ? j + 1 : n;
+  return bh * per_head + before * subs + int64_t(sub) * cnt + rank;
+}
 
 // Ordering semaphores per 64-row Q step of a (b, h): one per wave of the largest
 // workgroup (each wave reduces its own dQ blocks and passes its own turn).
@@ -136,6 +159,41 @@ enum ProfSlot {
   kProfFlush = 17,   // the item's last reduction
   kProfEpi = 18,     // item epilogue (dK, dV stores)
 };
+
+// Launches a persistent grid whose workgroups wait for each other (the ordered dQ
+// reduction), so all `grid` workgroups must be resident at once. The device must hold
+// that many workgroups of `fn` at a time (occupancy per CU times CUs, cached per kernel
+// and device), else hipErrorCooperativeLaunchTooLarge is returned and nothing is
+// launched. The launch itself is an ordinary one: on an otherwise idle device every
+// workgroup is placed at once; a kernel of another stream that holds CUs only delays
+// the start of some workgroups, which the kernels' bounded waits tolerate up to their
+// timeout. (A cooperative launch would add nothing the kernels use: they never
+// synchronise the whole grid.)
+inline hipError_t launch_resident(const void* fn, int grid, int threads, int shmem, void** args,
+                                  hipStream_t stream) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> capacity;  // (kernel, device) -> workgroups
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  int cap = 0;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = capacity.find({fn, dev});
+    if (it != capacity.end()) {
+      cap = it->second;
+    } else {
+      int per_cu = 0, cus = 0;
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, threads, shmem);
+      if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      if (e != hipSuccess) return e;
+      cap = per_cu * cus;
+      capacity.emplace(std::make_pair(fn, dev), cap);
+    }
+  }
+  if (grid > cap) return hipErrorCooperativeLaunchTooLarge;
+  return hipLaunchKernel(fn, dim3(grid), dim3(threads), args, shmem, stream);
+}
 
 // Main kernel for head dimension d and a workgroup of nw waves (one translation unit each).
 hipError_t launch_main_d64_nw2(const BwdParams& prm, int grid, hipStream_t stream);

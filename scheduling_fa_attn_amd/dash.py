@@ -28,6 +28,7 @@ SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "sym_shift": 3, "auto": 4}
 
 EXPORTED = (
     "dash_attn_bwd_workspace_size",
+    "dash_attn_bwd_varlen_workspace_size",
     "dash_attn_bwd",
     "dash_attn_bwd_timed",
     "dash_attn_bwd_varlen",
@@ -72,6 +73,8 @@ def open_library(path: str) -> ctypes.CDLL:
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.dash_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]
     lib.dash_attn_bwd_workspace_size.restype = sz
+    lib.dash_attn_bwd_varlen_workspace_size.argtypes = [i, i, i, i, i]
+    lib.dash_attn_bwd_varlen_workspace_size.restype = sz
     common = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.dash_attn_bwd.argtypes = common
     lib.dash_attn_bwd.restype = i
@@ -79,7 +82,7 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_attn_bwd_timed.restype = i
     lib.dash_attn_bwd_varlen.argtypes = common[:14] + [ctypes.POINTER(ctypes.c_int)] + common[14:]
     lib.dash_attn_bwd_varlen.restype = i
-    lib.dash_last_kernel_error.argtypes = []
+    lib.dash_last_kernel_error.argtypes = [vp]
     lib.dash_last_kernel_error.restype = i
     lib.dash_status_string.argtypes = [i]
     lib.dash_status_string.restype = ctypes.c_char_p
@@ -126,8 +129,18 @@ def dash_tile_size(N: int) -> int:
     return int(load().dash_tile_size(N))
 
 
-def dash_last_kernel_error(lib=None) -> int:
-    return int((lib or load()).dash_last_kernel_error())
+def dash_attn_bwd_varlen_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
+    return int(load().dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d))
+
+
+def dash_last_kernel_error(stream=None, lib=None) -> int:
+    """Kernel-side status of the last backward call enqueued on `stream` (default: torch's
+    current stream); synchronizes that stream."""
+    if stream is None:
+        import torch
+
+        stream = torch.cuda.current_stream().cuda_stream
+    return int((lib or load()).dash_last_kernel_error(ctypes.c_void_p(stream)))
 
 
 PLACEMENTS = {"aggregate": 0, "spread": 1}

@@ -71,6 +71,22 @@ def test_workspace_size():
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64) >= 1 * 2 * 256 * 64 * 4
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 96) == 0
     assert dash.dash_attn_bwd_workspace_size(1, 3, 2, 256, 64) == 0
+    assert dash.dash_attn_bwd_varlen_workspace_size(1, 3, 2, 256, 64) == 0
+
+
+@pytest.mark.parametrize("B,H,Hkv,N", [(3, 4, 2, 1024), (34, 1, 1, 512), (2, 2, 2, 320), (1, 16, 16, 16384)])
+def test_varlen_workspace_holds_the_table(B, H, Hkv, N):
+    """The variable-length workspace adds a table region at least as large as the step
+    records (16 bytes per 64-row step) plus the task records (16 bytes per task) of the
+    largest table any length vector gives (every batch at the padded length, full mask)."""
+    d = 64
+    base = dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d)
+    extra = dash.dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d) - base
+    tile = dash.dash_tile_size(N)
+    rec, _ = dash.dash_schedule_table_varlen(B, H, Hkv, N, [N] * B, "full", "auto", 8, 32)
+    tasks = len(rec)
+    assert tasks == B * H * (-(-N // tile)) ** 2
+    assert extra >= 16 * tasks * (tile // 64 + 1) + 16 * B * Hkv * (-(-N // tile)), (extra, tasks)
 
 
 def _call(**kw):

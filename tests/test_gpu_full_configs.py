@@ -6,8 +6,8 @@ afford every head at these sizes, so the check samples (batch, query head) units
 for a sampled unit the GPU receives the O and LSE of the oracle forward, and the
 oracle backward of that unit (dQ of its query heads, dK/dV of its KV head, summed
 over the KV head's whole query-head group) is compared element by element with the
-GPU result. Other heads get O/LSE from a torch fp32 forward (input preparation only;
-their gradients are not compared).
+GPU result. Other heads get O/LSE from the library's forward (dash_attn_fwd); their
+gradients are not compared.
 
 Bars: max|GPU - oracle| / max|oracle| <= 1e-2 per tensor (dQ, dK, dV) of every
 sampled unit and every schedule, deterministic and atomic; dQ/dK/dV bitwise equal
@@ -54,9 +54,8 @@ def _bits_to_dev(bits):
 
 @pytest.fixture(scope="module", params=list(SAMPLES), ids=list(SAMPLES))
 def workload(request):
-    """Seeded inputs of a workload on the GPU, O/LSE of the sampled heads from the oracle."""
-    from scheduling_fa_attn_amd.forward_inputs import forward_stats
-
+    """Seeded inputs of a workload on the GPU, O/LSE of the sampled heads from the oracle
+    (the other heads get theirs from the library's forward, dash_attn_fwd)."""
     name = request.param
     B, H, Hkv, N, d, causal, best, others, ci = bench.WORKLOADS[name]
     seed = 1000 + ci
@@ -65,7 +64,10 @@ def workload(request):
     print(f"\n[{name}] inputs seed={seed}", flush=True)
     bits = inputs.make_qkvdo(B, H, Hkv, N, d, seed)
     dev = {k: _bits_to_dev(v) for k, v in bits.items()}
-    dev["o"], dev["lse"] = forward_stats(dev["q"], dev["k"], dev["v"], causal, scale)
+    dev["o"] = torch.empty_like(dev["q"])
+    dev["lse"] = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    st = dash.dash_attn_fwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["lse"], scale, "causal" if causal else "full")
+    assert st == dash.DASH_OK, dash.dash_status_string(st)
     refs = []
     for (b, g) in SAMPLES[name]:
         hs = slice(g * G, (g + 1) * G)
@@ -147,24 +149,56 @@ def test_atomic_run_to_run_deviation(workload):
             assert dev_max == 0.0
 
 
-def test_spread_placement_parity_and_determinism(workload):
-    """The long causal head (n = 128 KV tiles, 64 lanes for the symmetric shift) with the
-    spread placement: the group spans XCDs and its dQ chains cross L2 domains (device-
-    scope ordering). Same bars: parity on the sampled heads, bitwise repeats."""
-    w = workload
-    if w["name"] != "causal-d128-N16384":
-        pytest.skip("only this workload has groups larger than one XCD")
+def _spread_checks(w, schedules):
     assert dash.dash_set_placement("spread") == 0
     try:
-        for sched in ("sym_shift", "naive"):
-            print(f"[{w['name']}] spread placement, schedule={sched}", flush=True)
+        for sched in schedules:
+            print(f"[{w['name']}] spread placement, schedule={sched}, {REPEATS} runs", flush=True)
             first = [t.clone() for t in _run(w, sched, 1)]
             for (b, g, hs), (rq, rk, rv) in w["refs"]:
                 errs = (_rel(first[0][b, hs], rq), _rel(first[1][b, g], rk), _rel(first[2][b, g], rv))
                 assert max(errs) <= TOL, (sched, b, g, errs)
-            for rep in range(2):
+            for rep in range(REPEATS - 1):
                 out = _run(w, sched, 1)
                 for a, b_ in zip(first, out):
                     assert torch.equal(a.view(torch.int16), b_.view(torch.int16)), (sched, rep)
     finally:
         assert dash.dash_set_placement("aggregate") == 0
+
+
+def test_spread_placement_parity_and_determinism(workload):
+    """The long causal head (n = 128 KV tiles, 64 lanes for the symmetric shift) with the
+    spread placement: the group spans XCDs and its dQ chains cross L2 domains (device-
+    scope ordering). Same bars for every deterministic schedule: parity on the sampled
+    heads, 20 bitwise-identical runs."""
+    w = workload
+    if w["name"] != "causal-d128-N16384":
+        pytest.skip("only this workload has groups larger than one XCD")
+    _spread_checks(w, ("sym_shift", "descending", "naive"))
+
+
+@pytest.fixture(scope="module")
+def spread_full():
+    """A full-mask shape whose groups span XCDs under the spread placement: 64 KV tiles
+    per head (64 lanes for shift, naive and descending, two XCDs); both heads sampled."""
+    B, H, Hkv, N, d, causal = 1, 2, 2, 8192, 64, False
+    scale = 1.0 / math.sqrt(d)
+    bits = inputs.make_qkvdo(B, H, Hkv, N, d, 1234)
+    dev = {k: _bits_to_dev(v) for k, v in bits.items()}
+    f = {k: inputs.bf16_bits_to_f32(v).astype(np.float64) for k, v in bits.items()}
+    print("\n[spread-full-d64-N8192] oracle forward/backward", flush=True)
+    o, lse = oa.forward(f["q"], f["k"], f["v"], causal, scale)
+    o_bits = inputs.bf16_round_bits(o.astype(np.float32))
+    lse32 = lse.astype(np.float32)
+    dev["o"] = _bits_to_dev(o_bits)
+    dev["lse"] = torch.from_numpy(lse32).cuda()
+    dq, dk, dv = oa.backward(f["q"], f["k"], f["v"], inputs.bf16_bits_to_f32(o_bits).astype(np.float64), f["do"],
+                             lse32.astype(np.float64), causal, scale)
+    refs = [((0, g, slice(g, g + 1)), (dq[0, g:g + 1], dk[0, g], dv[0, g])) for g in range(H)]
+    ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    return {"name": "spread-full-d64-N8192", "shape": (B, H, Hkv, N, d), "causal": causal, "scale": scale,
+            "dev": dev, "refs": refs, "ws": ws}
+
+
+def test_spread_placement_full_mask(spread_full):
+    _spread_checks(spread_full, ("shift", "descending", "naive"))

@@ -87,7 +87,7 @@ def test_ordered_replay_bitwise(lib, case_args):
                                 case["scale"], "causal" if causal else "full", sched, 1, ws, lib=lib)
         assert st == 0, dash.dash_status_string(st)
         torch.cuda.synchronize()
-        assert dash.dash_last_kernel_error(lib) == 0
+        assert dash.dash_last_kernel_error(lib=lib) == 0
         lib.dash_replay_attach(None, 0)
         d_np = dump.cpu().numpy().reshape(B * H, steps, nblk, n_kv, 1024)
         acc = ws[: B * H * R * d * 4].cpu().numpy().view(np.float32).reshape(B * H, steps, nblk, 1024)
@@ -148,3 +148,31 @@ def test_replay_dump_too_small_is_rejected(lib):
                             1.0 / math.sqrt(d), "full", "shift", 1, ws, lib=lib)
     lib.dash_replay_attach(None, 0)
     assert st == dash.DASH_ERR_WORKSPACE
+
+
+# Spread placement (the paper's n-SM layout): groups whose lanes fill whole XCDs (64 or
+# 128 lanes on 32-CU XCDs) span XCDs, so consecutive contributors of a dQ tile sit on
+# different L2 domains and the chain runs on device-scope loads, stores and flags (the
+# one-wave kernel). 64 tiles of 128 rows: 64 lanes for naive, descending and shift;
+# 128 tiles: 64 lanes for the symmetric shift, 128 for naive and descending.
+SPREAD_CASES = [
+    (1, 1, 1, 8192, 64, False),
+    (1, 1, 1, 16384, 64, True),
+]
+
+
+@pytest.mark.parametrize("case_args", SPREAD_CASES,
+                         ids=[f"B{c[0]}H{c[1]}Hkv{c[2]}N{c[3]}d{c[4]}-{'causal' if c[5] else 'full'}"
+                              for c in SPREAD_CASES])
+def test_ordered_replay_bitwise_across_xcds(lib, case_args):
+    B, H, Hkv, N, d, causal = case_args
+    assert lib.dash_set_placement(1) == 0
+    assert dash.dash_set_placement("spread") == 0
+    try:
+        for sched in SCHEDULES[causal]:
+            _, local = dash.dash_schedule_table(B, H, Hkv, N, "causal" if causal else "full", sched, 8, 32)
+            assert not local, sched  # some dQ chain crosses an XCD
+        test_ordered_replay_bitwise(lib, case_args)
+    finally:
+        lib.dash_set_placement(0)
+        dash.dash_set_placement("aggregate")

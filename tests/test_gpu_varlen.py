@@ -73,7 +73,7 @@ def _run(dev, lens, scale, mask, schedule, det, ws=None):
         x.view(torch.int16).fill_(int(SENTINEL))
         outs.append(x)
     if ws is None:
-        ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(dash.dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
     st = dash.dash_attn_bwd_varlen(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs, lens, scale,
                                    mask, schedule, det, ws)
     assert st == dash.DASH_OK, dash.dash_status_string(st)
@@ -131,11 +131,15 @@ def test_varlen_argument_errors():
            for k, h in (("q", H), ("k", Hkv), ("v", Hkv), ("o", H), ("do", H))}
     dev["lse"] = torch.zeros(B, H, N, device="cuda")
     outs = [torch.empty_like(dev[k]) for k in ("q", "k", "v")]
-    ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    ws = torch.empty(dash.dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
 
-    def call(lens, det=1, sched="auto"):
+    def call(lens, det=1, sched="auto", w=ws):
         return dash.dash_attn_bwd_varlen(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs, lens,
-                                         0.125, "causal", sched, det, ws)
+                                         0.125, "causal", sched, det, w)
+
+    # The base workspace has no room for the call's table.
+    base = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    assert call((512, 512), w=base) == dash.DASH_ERR_WORKSPACE
 
     assert call((0, 512)) == dash.DASH_ERR_INVALID_ARG
     assert call((513, 512)) == dash.DASH_ERR_INVALID_ARG
@@ -171,3 +175,38 @@ def test_varlen_one_wave_kernel(causal):
                         [t.view(torch.int16).cpu().numpy().tobytes() for t in outs]
     finally:
         dash.dash_set_kernel("auto")
+
+
+def test_varlen_distinct_lengths_bounded_memory():
+    """100 calls, each with a length vector not seen before: the tables go into the
+    caller's workspace through the library's pinned staging ring, so the device memory
+    the library holds does not grow with the number of distinct vectors, and the results
+    keep matching the oracle (checked on the first and the last call)."""
+    B, H, Hkv, N, d = 3, 2, 1, 1024, 64
+    rng = np.random.default_rng(5)
+    vectors = []
+    seen = set()
+    while len(vectors) < 100:
+        lens = tuple(int(x) for x in rng.integers(1, N + 1, size=B))
+        if lens not in seen:
+            seen.add(lens)
+            vectors.append(lens)
+    bits, lse, scale, _ = _case(B, H, Hkv, N, d, vectors[0], True, seed=808)
+    dev = _dev(bits, lse)
+    ws = torch.empty(dash.dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    outs, _ = _run(dev, vectors[0], scale, "causal", "auto", 1, ws)
+    torch.cuda.synchronize()
+    free0, _ = torch.cuda.mem_get_info()
+    for i, lens in enumerate(vectors[1:]):
+        st = dash.dash_attn_bwd_varlen(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs, lens,
+                                       scale, "causal", "auto", 1, ws)
+        assert st == dash.DASH_OK, (i, dash.dash_status_string(st))
+    torch.cuda.synchronize()
+    assert dash.dash_last_kernel_error() == dash.DASH_OK
+    free1, _ = torch.cuda.mem_get_info()
+    print(f"device memory free before {free0}, after {free1} bytes", flush=True)
+    assert free0 - free1 <= 4 << 20, (free0, free1)
+    for lens in (vectors[0], vectors[-1]):
+        bits, lse, scale, ref = _case(B, H, Hkv, N, d, lens, True, seed=808)
+        outs, _ = _run(_dev(bits, lse), lens, scale, "causal", "auto", 1, ws)
+        _check(outs, ref, lens)
