@@ -64,6 +64,7 @@ def time_forward(dev, d, causal, steps, warmup):
         if st != dash.DASH_OK:
             raise dash.DashError(st, "dash_attn_fwd")
 
+    preroll(call)
     for _ in range(warmup):
         call()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -77,17 +78,44 @@ def time_forward(dev, d, causal, steps, warmup):
 
 
 def make_inputs(B, H, Hkv, N, d, causal, seed):
+    """Seeded bf16 Q, K, V, dO in HBM; O and LSE from the library's forward (dash_attn_fwd)."""
     import numpy as np
     import torch
 
-    from scheduling_fa_attn_amd import inputs
-    from scheduling_fa_attn_amd.forward_inputs import forward_stats
+    from scheduling_fa_attn_amd import dash, inputs
 
     bits = inputs.make_qkvdo(B, H, Hkv, N, d, seed)
     dev = {k: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for k, v in bits.items()}
-    dev["o"], dev["lse"] = forward_stats(dev["q"], dev["k"], dev["v"], causal)
+    dev["o"] = torch.empty_like(dev["q"])
+    dev["lse"] = torch.empty(B, H, N, dtype=torch.float32, device="cuda")
+    st = dash.dash_attn_fwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["lse"], 1.0 / math.sqrt(d),
+                            "causal" if causal else "full")
+    if st != dash.DASH_OK:
+        raise dash.DashError(st, "dash_attn_fwd")
     torch.cuda.synchronize()
     return dev
+
+
+# Back-to-back calls before every timed block, whatever --warmup says: the GPU clock needs
+# tens of milliseconds of load to settle after the host has been busy (input generation,
+# the previous workload's set-up), and a short warm-up leaves the first block timed
+# slower than the ones after it.
+PREROLL_MS = 150.0
+
+
+def preroll(call, min_ms=PREROLL_MS):
+    """Calls `call` until at least min_ms of wall time has passed; returns the call count."""
+    import torch
+
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        for _ in range(4):
+            call()
+            n += 1
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= min_ms:
+            return n
 
 
 def time_schedule(dev, shape, causal, schedule, deterministic, steps, warmup, workspace):
@@ -116,6 +144,7 @@ def time_schedule(dev, shape, causal, schedule, deterministic, steps, warmup, wo
         if st != dash.DASH_OK:
             raise dash.DashError(st, "dash_attn_bwd")
 
+    preroll(call)
     for _ in range(warmup):
         call()
     torch.cuda.synchronize()
@@ -167,9 +196,13 @@ def time_cold(dev, shape, causal, schedule, steps, warmup, workspace, flush_mib=
         if st != dash.DASH_OK:
             raise dash.DashError(st, "dash_attn_bwd")
 
-    for _ in range(warmup):
+    def flushed_call():
         flush.fill_(1.0)
         call()
+
+    preroll(flushed_call)
+    for _ in range(warmup):
+        flushed_call()
     torch.cuda.synchronize()
     for evs in calls:
         flush.fill_(1.0)
@@ -186,6 +219,101 @@ def time_cold(dev, shape, causal, schedule, steps, warmup, workspace, flush_mib=
     return whole[len(whole) // 2], whole[0], main[len(main) // 2]
 
 
+def run_to_run_deviation(dev, shape, causal, schedule, deterministic, workspace, runs=10):
+    """The DASH paper's Table 1 measure: `runs` identical backward passes; for each tensor,
+    the mean over runs 2..runs of max |g_r - g_1| (elementwise, in fp32 on the GPU)."""
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+
+    B, H, Hkv, N, d = shape
+    outs = [torch.empty_like(dev[k]) for k in ("q", "k", "v")]
+    first = None
+    dev_max = {"dq": [], "dk": [], "dv": []}
+    for r in range(runs):
+        st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs,
+                                1.0 / math.sqrt(d), "causal" if causal else "full", schedule, deterministic,
+                                workspace)
+        if st != dash.DASH_OK:
+            raise dash.DashError(st, "dash_attn_bwd")
+        if r == 0:
+            first = [t.clone() for t in outs]
+            continue
+        for name, a, b in zip(("dq", "dk", "dv"), outs, first):
+            dev_max[name].append(float((a.float() - b.float()).abs().max()))
+    err = dash.dash_last_kernel_error()
+    if err != dash.DASH_OK:
+        raise dash.DashError(err, "kernel")
+    return {k: sum(v) / len(v) for k, v in dev_max.items()}
+
+
+def _smi_numbers(obj, path=()):
+    """(key path, number) pairs of a parsed amd-smi JSON document."""
+    if isinstance(obj, dict):
+        for k, v in obj.items():
+            yield from _smi_numbers(v, path + (str(k).lower(),))
+    elif isinstance(obj, list):
+        for i, v in enumerate(obj):
+            yield from _smi_numbers(v, path + (str(i),))
+    elif isinstance(obj, (int, float)) and not isinstance(obj, bool):
+        yield path, float(obj)
+
+
+def smi_sample():
+    """One reading of the GPU's graphics clocks (MHz) and socket power (W) from
+    `amd-smi metric` (None where the tool or the field is not available)."""
+    import subprocess
+
+    try:
+        res = subprocess.run(["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], capture_output=True,
+                             text=True, timeout=20)
+        doc = json.loads(res.stdout)
+    except Exception as e:  # noqa: BLE001
+        return {"error": f"{type(e).__name__}: {e}"[:200]}
+    gfx, power = [], []
+    for path, val in _smi_numbers(doc):
+        joined = "/".join(path)
+        if "gfx" in joined and "clk" in joined and path[-1] in ("value", "clk") and "lock" not in joined \
+                and "min" not in joined and "max" not in joined:
+            gfx.append(val)
+        elif "power" in joined and path[-1] == "value" and "limit" not in joined:
+            power.append(val)
+    return {"gfx_clk_mhz": sorted(set(gfx)), "power_w": sorted(set(power))}
+
+
+def sustained_clock(call, seconds=1.5, samples=3):
+    """Runs `call` back to back for `seconds` while amd-smi reads the clocks `samples`
+    times from another thread; returns the readings."""
+    import threading
+
+    import torch
+
+    readings = []
+    stop = threading.Event()
+
+    def sampler():
+        for _ in range(samples):
+            if stop.wait(seconds / (samples + 1)):
+                return
+            readings.append(smi_sample())
+
+    t = threading.Thread(target=sampler)
+    t0 = time.perf_counter()
+    t.start()
+    n = 0
+    while time.perf_counter() - t0 < seconds or t.is_alive():
+        for _ in range(8):
+            call()
+            n += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 > seconds + 30:
+            break
+    stop.set()
+    t.join()
+    return {"calls": n, "seconds": round(time.perf_counter() - t0, 2), "readings": readings,
+            "source": "amd-smi metric -c -p during back-to-back calls of the headline step"}
+
+
 def cpu_baseline(shape, causal, seed, budget_s):
     """The fp64 oracle backward on the host cores, on whole heads of the same workload."""
     import numpy as np
@@ -194,11 +322,20 @@ def cpu_baseline(shape, causal, seed, budget_s):
     from scheduling_fa_attn_amd import inputs
 
     B, H, Hkv, N, d = shape
+    blas = []
     try:
         from threadpoolctl import threadpool_info
-        threads = max((x.get("num_threads", 0) for x in threadpool_info()), default=0) or os.cpu_count()
+        info = threadpool_info()
+        threads = max((x.get("num_threads", 0) for x in info), default=0) or os.cpu_count()
+        blas = [{k: x.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")}
+                for x in info if x.get("user_api") == "blas"]
     except Exception:  # pragma: no cover
         threads = os.cpu_count()
+    try:
+        import subprocess
+        nproc = int(subprocess.run(["nproc"], capture_output=True, text=True, timeout=10).stdout.strip())
+    except Exception:  # pragma: no cover
+        nproc = None
     G = H // Hkv
     scale = 1.0 / math.sqrt(d)
     heads = 0
@@ -217,6 +354,7 @@ def cpu_baseline(shape, causal, seed, budget_s):
         group += 1
     fl = flops_bwd(1, heads, N, d, causal)
     return {"value": fl / elapsed / 1e12, "unit": "TFLOPS", "cores": int(threads), "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "nproc": nproc, "blas": blas,
             "sample": f"{heads} of {B * H} (batch, query head) units at full N={N}, d={d}, seeded inputs of "
                       f"the workload's shape; fp64 numpy backward only, {elapsed:.1f} s"}
 
@@ -240,6 +378,7 @@ def measure_workload(name, schedule, steps, warmup, compare):
     tflops = fl / (ms * 1e-3) / 1e12
     log(f"  {schedule} det: {ms:.3f} ms/step ({tflops:.1f} TFLOPS), main kernel {main_ms:.3f} ms")
     extra = {schedule: round(tflops, 2)}
+    deviation = {}
     ratio = None
     if compare:
         for s in others:
@@ -266,6 +405,12 @@ def measure_workload(name, schedule, steps, warmup, compare):
         ratio = ms_a / ms
         log(f"  {schedule} atomic: {ms_a:.3f} ms/step ({extra['atomic_' + schedule]:.1f} TFLOPS); "
             f"det/non-det throughput ratio {ratio:.3f}")
+        # Table 1 analogue: run-to-run deviation over 10 identical calls per mode.
+        for s, det in [(schedule, 0), (schedule, 1)] + [(x, 1) for x in others] + [(schedule, 2)]:
+            key = {0: "atomic_", 1: "", 2: "two_pass_"}[det] + s
+            m_r = run_to_run_deviation(dev, shape, causal, s, det, ws)
+            deviation[key] = {k: float(f"{v:.3e}") for k, v in m_r.items()}
+            log(f"  run-to-run max deviation over 10 runs, {key}: {deviation[key]}")
     ms_f = time_forward(dev, d, causal, steps, warmup)
     fl_f = flops_fwd(B, H, N, d, causal)
     fwd = {"ms": round(ms_f, 4), "tflops": round(fl_f / (ms_f * 1e-3) / 1e12, 2),
@@ -275,7 +420,7 @@ def measure_workload(name, schedule, steps, warmup, compare):
     torch.cuda.empty_cache()
     return {"schedule": schedule, "tflops": round(tflops, 2), "ms_per_step": round(ms, 4),
             "main_kernel_ms": round(main_ms, 4), "det_nondet_ratio": None if ratio is None else round(ratio, 4),
-            "schedules_tflops": extra,
+            "schedules_tflops": extra, "run_to_run_max_dev": deviation or None,
             "roofline_frac": round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4), "forward": fwd}
 
 
@@ -376,6 +521,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache timing (L2 and memory-side cache flushed before every call)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock and power readings (amd-smi) during back-to-back headline calls")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--kernel", default="auto", choices=["auto", "one_wave", "two_waves"],
                     help="main backward kernel (dash_set_kernel); two_waves applies to 128-row tiles (N >= 512)")
@@ -422,7 +569,7 @@ def main():
                 r = measure_workload(name, None, args.steps, args.warmup, not args.no_compare)
                 others[name] = {k: r[k] for k in ("schedule", "tflops", "ms_per_step", "main_kernel_ms",
                                                   "det_nondet_ratio", "schedules_tflops", "roofline_frac",
-                                                  "forward")}
+                                                  "run_to_run_max_dev", "forward")}
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
@@ -445,19 +592,34 @@ def main():
                    "deterministic": True, "seed": 1000 + cfg_index},
         "det_nondet_ratio": main_res["det_nondet_ratio"],
         "schedules_tflops": main_res["schedules_tflops"],
+        "run_to_run_max_dev": main_res["run_to_run_max_dev"],
+        "preroll_ms": PREROLL_MS,
         "forward": main_res["forward"],
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_bytes(args.workload, kernel),
                      "kernel": kernel, "main_kernel_ms": round(main_ms, 4)},
     }
-    if not args.no_cold:
+    if not args.no_cold or not args.no_clock:
         import torch
 
         from scheduling_fa_attn_amd import dash
 
         dev = make_inputs(B, H, Hkv, N, d, causal, 1000 + cfg_index)
         ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    if not args.no_clock:
+        outs = [torch.empty_like(dev[k]) for k in ("q", "k", "v")]
+
+        def headline_call():
+            st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs,
+                                    1.0 / math.sqrt(d), "causal" if causal else "full", main_res["schedule"], 1, ws)
+            if st != dash.DASH_OK:
+                raise dash.DashError(st, "dash_attn_bwd")
+
+        result["clock"] = sustained_clock(headline_call)
+        log(f"  clock during back-to-back calls: {result['clock']['readings']}")
+        del outs
+    if not args.no_cold:
         med, mn, main_med = time_cold(dev, (B, H, Hkv, N, d), causal, main_res["schedule"], args.steps,
                                       min(args.warmup, 5), ws)
         result["cold_cache"] = {"flush": "512 MiB written before every call", "median_ms": round(med, 4),
