@@ -272,13 +272,12 @@ def smi_sample():
         return {"error": f"{type(e).__name__}: {e}"[:200]}
     gfx, power = [], []
     for path, val in _smi_numbers(doc):
-        joined = "/".join(path)
-        if "gfx" in joined and "clk" in joined and path[-1] in ("value", "clk") and "lock" not in joined \
-                and "min" not in joined and "max" not in joined:
+        # .../clock/gfx_<XCD>/clk/value (MHz) and .../power/socket_power/value (W)
+        if len(path) >= 3 and path[-1] == "value" and path[-2] == "clk" and path[-3].startswith("gfx"):
             gfx.append(val)
-        elif "power" in joined and path[-1] == "value" and "limit" not in joined:
+        elif len(path) >= 2 and path[-1] == "value" and path[-2] == "socket_power":
             power.append(val)
-    return {"gfx_clk_mhz": sorted(set(gfx)), "power_w": sorted(set(power))}
+    return {"gfx_clk_mhz": gfx, "power_w": power}
 
 
 def sustained_clock(call, seconds=1.5, samples=3):
@@ -400,17 +399,24 @@ def measure_workload(name, schedule, steps, warmup, compare):
         extra["two_pass_" + schedule] = round(fl / (ms_t * 1e-3) / 1e12, 2)
         log(f"  {schedule} two-pass (dK/dV pass + separate dQ pass): {ms_t:.3f} ms/step "
             f"({extra['two_pass_' + schedule]:.1f} TFLOPS)")
+        ws3 = torch.empty(dash.dash_attn_bwd_partials_workspace_size(B, H, Hkv, N, d, "causal" if causal else "full"),
+                          dtype=torch.uint8, device="cuda")
+        ms_p, _, _ = time_schedule(dev, shape, causal, schedule, 3, steps, warmup, ws3)
+        extra["partials_" + schedule] = round(fl / (ms_p * 1e-3) / 1e12, 2)
+        log(f"  {schedule} per-tile partials ({ws3.numel() / 2**30:.2f} GiB of slots + consolidation kernel): "
+            f"{ms_p:.3f} ms/step ({extra['partials_' + schedule]:.1f} TFLOPS)")
         ms_a, _, _ = time_schedule(dev, shape, causal, schedule, 0, steps, warmup, ws)
         extra["atomic_" + schedule] = round(fl / (ms_a * 1e-3) / 1e12, 2)
         ratio = ms_a / ms
         log(f"  {schedule} atomic: {ms_a:.3f} ms/step ({extra['atomic_' + schedule]:.1f} TFLOPS); "
             f"det/non-det throughput ratio {ratio:.3f}")
         # Table 1 analogue: run-to-run deviation over 10 identical calls per mode.
-        for s, det in [(schedule, 0), (schedule, 1)] + [(x, 1) for x in others] + [(schedule, 2)]:
-            key = {0: "atomic_", 1: "", 2: "two_pass_"}[det] + s
-            m_r = run_to_run_deviation(dev, shape, causal, s, det, ws)
+        for s, det in [(schedule, 0), (schedule, 1)] + [(x, 1) for x in others] + [(schedule, 2), (schedule, 3)]:
+            key = {0: "atomic_", 1: "", 2: "two_pass_", 3: "partials_"}[det] + s
+            m_r = run_to_run_deviation(dev, shape, causal, s, det, ws3 if det == 3 else ws)
             deviation[key] = {k: float(f"{v:.3e}") for k, v in m_r.items()}
             log(f"  run-to-run max deviation over 10 runs, {key}: {deviation[key]}")
+        del ws3
     ms_f = time_forward(dev, d, causal, steps, warmup)
     fl_f = flops_fwd(B, H, N, d, causal)
     fwd = {"ms": round(ms_f, 4), "tflops": round(fl_f / (ms_f * 1e-3) / 1e12, 2),
@@ -460,6 +466,12 @@ def sweep(steps, warmup):
                         rec["main_kernel_frac"] = round(fl / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
                 ms_t, _, _ = time_schedule(dev, shape, causal, best, 2, steps, warmup, ws)
                 rec["tflops"]["two_pass_" + best] = round(fl / (ms_t * 1e-3) / 1e12, 1)
+                ws3 = torch.empty(dash.dash_attn_bwd_partials_workspace_size(B, H, H, N, d,
+                                                                             "causal" if causal else "full"),
+                                  dtype=torch.uint8, device="cuda")
+                ms_p, _, _ = time_schedule(dev, shape, causal, best, 3, steps, warmup, ws3)
+                rec["tflops"]["partials_" + best] = round(fl / (ms_p * 1e-3) / 1e12, 1)
+                del ws3
                 ms_a, _, _ = time_schedule(dev, shape, causal, best, 0, steps, warmup, ws)
                 rec["tflops"]["atomic_" + best] = round(fl / (ms_a * 1e-3) / 1e12, 1)
                 log(f"sweep N={N} d={d} {rec['mask']}: " + ", ".join(f"{k} {v}" for k, v in rec["tflops"].items()))

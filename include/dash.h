@@ -133,6 +133,14 @@ int dash_set_wait_timeout(long long microseconds);
  * sizes. */
 size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d);
 
+/* Bytes of workspace dash_attn_bwd needs with deterministic = 3 (per-tile partials) for
+ * this shape and mask: in place of the accumulator, one fp32 slot of 64 x d floats per
+ * (batch, query head, 64-row query step, contributing KV tile), i.e.
+ * B*H*(tile/64)*n^2 slots for the full mask and B*H*(tile/64)*n(n+1)/2 for the causal
+ * mask (n = ceil(N / tile)); e.g. 2.1 GB at B=8, H=16, N=2048, d=128, full mask. Returns 0
+ * for invalid sizes or mask. */
+size_t dash_attn_bwd_partials_workspace_size(int B, int H, int Hkv, int N, int d, int mask);
+
 /* Bytes of workspace dash_attn_bwd_varlen needs for a padded batch of these sizes: the
  * dash_attn_bwd workspace plus a region for the call's schedule table (an upper bound
  * for any batch lengths: B*H*ceil(N/tile)^2 tasks). Returns 0 for invalid sizes. */
@@ -149,6 +157,12 @@ size_t dash_attn_bwd_varlen_workspace_size(int B, int H, int Hkv, int N, int d);
  *   walks all key tiles for each query tile, recomputing S and dP, with dQ kept in
  *   registers (deterministic, no cross-CU reduction). The schedule sets the tile
  *   order of the dK/dV pass.
+ * deterministic = 3: per-tile partials, the other deterministic alternative of section
+ *   5 (FlashAttention-2 style): every dQ contribution of every KV tile is written to its
+ *   own fp32 slot, with no waits, and a separate kernel adds each query step's slots in
+ *   the schedule's rank order (fp32, from +0) and writes bf16 dQ. Bitwise reproducible;
+ *   the workspace is dash_attn_bwd_partials_workspace_size (far larger). Not with
+ *   dash_attn_bwd_varlen (DASH_ERR_UNSUPPORTED there).
  * softmax_scale must be finite and > 0 (1/sqrt(d) for standard attention).
  * B == 0 or N == 0 is a no-op that returns DASH_OK.
  * Errors: DASH_ERR_INVALID_ARG, _UNSUPPORTED, _WORKSPACE, _NOT_CORESIDENT, _HIP.

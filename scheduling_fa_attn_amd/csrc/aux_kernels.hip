@@ -113,6 +113,57 @@ __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __rest
   }
 }
 
+// dQ of the per-tile partials variant (deterministic = 3; the deterministic alternative of
+// the DASH paper, section 5: every KV tile's dQ contribution materialised, then reduced by a
+// separate kernel): dQ = bf16(s * sum of the contributions of each 64-row step), added in
+// fp32 in rank order from +0 (the slot layout is described at kDqBlock). One workgroup per
+// 32-row block row of one head, as in dq_cast_blocks_kernel: each thread owns 4 floats of
+// each of the block row's D / 32 blocks and walks the step's slots.
+template <int D>
+__global__ void __launch_bounds__(256) dq_consolidate_kernel(const float* __restrict__ parts, bf16* __restrict__ dq,
+                                                             int N, int row_stride, int tile, int causal,
+                                                             float scale) {
+  constexpr int DB = D / 32;
+  constexpr int LROW = D + 8;
+  constexpr int SLOT4 = 2 * DB * kDqBlock / 4;  // float4 per slot
+  __shared__ __attribute__((aligned(16))) bf16 lds[32 * LROW];
+  const int rbs = row_stride / 32;
+  const int64_t g = blockIdx.x;
+  const int64_t bh = g / rbs;
+  const int qblk = static_cast<int>(g % rbs);
+  const int q0 = (qblk / 2) * 64;  // the block row's 64-row step
+  const int qb = qblk % 2;         // and its half of that step
+  const int n = row_stride / tile;
+  const int j = q0 / tile;
+  const int cnt = causal ? j + 1 : n;
+  const floatx4* slots = reinterpret_cast<const floatx4*>(parts) + partial_slot(bh, q0, 0, n, tile, causal) * SLOT4;
+#pragma unroll
+  for (int k = 0; k < DB; ++k) {
+    const int x = threadIdx.x + 256 * k;
+    const int db = x >> 8, i = (x >> 6) & 3, l = x & 63;
+    const floatx4* src = slots + (qb * DB + db) * (kDqBlock / 4) + (x & 255);
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+    for (int r = 0; r < cnt; ++r) acc = acc + src[static_cast<int64_t>(r) * SLOT4];
+    const int row0 = 16 * (i >> 1) + 2 * (i & 1) + (l >> 5);
+    const int col = 32 * db + (l & 31);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) lds[(row0 + 4 * e) * LROW + col] = static_cast<bf16>(acc[e] * scale);
+  }
+  __syncthreads();
+  constexpr int CPR = D / 8;
+  const int r_end = N - 32 * qblk < 32 ? N - 32 * qblk : 32;
+#pragma unroll
+  for (int k = 0; k < 32 * CPR / 256; ++k) {
+    const int c = threadIdx.x + 256 * k;
+    const int r = c / CPR, ch = c % CPR;
+    if (r < r_end) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(&lds[r * LROW + 8 * ch]);
+      *reinterpret_cast<u32x4*>(dq + (bh * N + 32 * qblk + r) * D + 8 * ch) = v;
+    }
+  }
+}
+
 // dQ = bf16(s * dQacc), for the atomic variant; the accumulator is row-major with
 // row_stride rows per head, of which the first N are output.
 __global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
@@ -158,6 +209,23 @@ hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int 
   grid = grid < 1 ? 1 : (grid > 8192 ? 8192 : grid);
   hipLaunchKernelGGL(dq_cast_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
                      reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale, seqlens, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_consolidate(const float* parts, void* dq, int64_t heads, int N, int row_stride, int tile, int d,
+                                 int causal, float scale, hipStream_t stream) {
+  const int64_t grid = heads * (row_stride / 32);
+  if (grid == 0) return hipSuccess;
+  if (grid > 0x7fffffff) return hipErrorInvalidValue;
+  if (d == 64) {
+    hipLaunchKernelGGL(dq_consolidate_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, parts,
+                       reinterpret_cast<bf16*>(dq), N, row_stride, tile, causal, scale);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(dq_consolidate_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, parts,
+                       reinterpret_cast<bf16*>(dq), N, row_stride, tile, causal, scale);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -41,14 +41,25 @@ struct WsLayout {
   int row_stride = 0;  // rows per head of -D, -LSE*log2(e) and the dQ accumulator: N rounded up to the tile
 };
 
-WsLayout ws_layout(int B, int H, int N, int d) {
+// Per-tile partials (deterministic = 3): one slot of 64 x d floats per (b, h, 64-row step,
+// contribution); a head has (tile / 64) x n^2 slots, n (n + 1) / 2 instead of n^2 for the
+// causal mask (partial_slot in kernels.h).
+size_t partials_bytes(int B, int H, int N, int d, bool causal) {
+  const int tile = tile_for(N);
+  const int64_t n = cdiv(N, tile);
+  const int64_t per_head = (causal ? n * (n + 1) / 2 : n * n) * (tile / 64);
+  return align256(size_t(B) * H * per_head * 64 * d * sizeof(float));
+}
+
+WsLayout ws_layout(int B, int H, int N, int d, size_t dq_bytes_override = 0) {
   WsLayout L;
   // One semaphore per 64-row Q step and wave (dash::kSemPerStep at most), for every
   // step of the ceil(N / tile) tiles of a head (the last tile's second step may lie past N).
   const int tile = tile_for(N);
   L.sem_stride = static_cast<int>(cdiv(cdiv(N, tile) * (tile / 64) * dash::kSemPerStep, 32) * 32);
   L.row_stride = static_cast<int>(cdiv(N, tile) * tile);
-  const size_t dq_bytes = align256(size_t(B) * H * L.row_stride * d * sizeof(float));
+  const size_t dq_bytes =
+      dq_bytes_override ? dq_bytes_override : align256(size_t(B) * H * L.row_stride * d * sizeof(float));
   const size_t row_bytes = align256(size_t(B) * H * L.row_stride * sizeof(float));
   const size_t sem_bytes = align256(size_t(B) * H * L.sem_stride * sizeof(int));
   L.dqacc = 0;
@@ -98,9 +109,22 @@ dash::CostModel measured_costs(int d, int tile) {
   return m;
 }
 
-// DASH_SCHED_AUTO: the valid schedule (shift or symmetric shift for its mask, naive,
-// descending) with the smallest makespan under measured_costs on the tables built for
-// this topology and placement; ties go to the later candidate (shift, symmetric shift).
+// Margin by which naive or descending must beat the shift schedule of the mask in the
+// model before AUTO takes it. The model prices every reduction at r_local or r_remote;
+// on the GPU a reduction waits for its predecessor's, and a contribution is added during
+// the CU's next step, so chains whose contributors follow each other step after step
+// (naive and descending: a wavefront over the tile's lanes) lose up to about a task per
+// link, while the shift schedules are conflict-free by construction (one contributor per
+// dQ tile per time step) and lose nothing. Measured on MI355X: every shape where the
+// model put descending within 3 % of symmetric shift ran faster with symmetric shift
+// (by 16 % and 43 %), and every shape where it put descending 10 % or more ahead ran
+// faster with descending.
+constexpr double kShiftMargin = 0.08;
+
+// DASH_SCHED_AUTO: the shift schedule of the mask (shift for the full mask, symmetric
+// shift for the causal mask with an even tile count) unless naive or descending has a
+// makespan more than kShiftMargin smaller under measured_costs on the tables built for
+// this topology and placement; then the smaller of those two (ties to descending).
 // Returns a dash_status code on error.
 int model_schedule(int B, int H, int Hkv, int N, int d, int mask, int num_xcd, int cus_per_xcd, bool spread) {
   const bool causal = mask == DASH_MASK_CAUSAL;
@@ -110,6 +134,7 @@ int model_schedule(int B, int H, int Hkv, int N, int d, int mask, int num_xcd, i
   const dash::CostModel m = measured_costs(d, tile);
   int best = -1;
   double best_t = 0.0;
+  double shift_t = -1.0;
   for (int sched : cands) {
     if (sched == DASH_SCHED_SYM_SHIFT && n % 2) continue;
     dash::SchedParams sp;
@@ -129,11 +154,17 @@ int model_schedule(int B, int H, int Hkv, int N, int d, int mask, int num_xcd, i
     if (s != 0) return s;
     double span = 0.0;
     if (!dash::table_makespan(t, cus_per_xcd, m, &span)) continue;  // (validated tables never cycle)
+    if (sched == DASH_SCHED_SHIFT || sched == DASH_SCHED_SYM_SHIFT) {
+      shift_t = span;
+      continue;
+    }
     if (best < 0 || span <= best_t) {
       best = sched;
       best_t = span;
     }
   }
+  if (shift_t >= 0.0 && (best < 0 || best_t >= (1.0 - kShiftMargin) * shift_t))
+    return causal ? DASH_SCHED_SYM_SHIFT : DASH_SCHED_SHIFT;
   return best < 0 ? DASH_ERR_UNSUPPORTED : best;
 }
 
@@ -529,7 +560,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   schedule = resolve_schedule(schedule, N, mask);
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
-  if (deterministic < 0 || deterministic > 2) return DASH_ERR_INVALID_ARG;
+  if (deterministic < 0 || deterministic > 3) return DASH_ERR_INVALID_ARG;
+  if (deterministic == 3 && seqlens) return DASH_ERR_UNSUPPORTED;  // per-tile partials: one length
   // Variable-length batches: lengths in [1, N].
   std::vector<int> lens, scheds;
   if (seqlens && B > 0 && N > 0) {
@@ -554,7 +586,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     if (ptr == nullptr || !aligned(ptr, 16)) return DASH_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return DASH_ERR_INVALID_ARG;
   if (workspace == nullptr || !aligned(workspace, 256)) return DASH_ERR_INVALID_ARG;
-  const WsLayout L = ws_layout(B, H, N, d);
+  const WsLayout L = deterministic == 3 ? ws_layout(B, H, N, d, partials_bytes(B, H, N, d, mask == DASH_MASK_CAUSAL))
+                                        : ws_layout(B, H, N, d);
   // Variable-length batches: the call's table goes into the workspace after the base part.
   const size_t table_bytes = seqlens ? varlen_table_bound(B, H, Hkv, N) : 0;
   if (workspace_bytes < L.total + table_bytes) return DASH_ERR_WORKSPACE;
@@ -698,8 +731,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     std::lock_guard<std::mutex> lock(g_mu);
     kernel = g_kernel;
   }
-  const bool pair_ok = tab->tile == 128 && deterministic != 2 && (deterministic == 0 || bp.xcd_local ||
-                       st->num_xcd == 1);
+  // (The per-tile partials have no chains, so any placement suits the two-waves kernel.)
+  const bool pair_ok = tab->tile == 128 && deterministic != 2 &&
+                       (deterministic == 0 || deterministic == 3 || bp.xcd_local || st->num_xcd == 1);
   const bool use_pair = pair_ok && (kernel == DASH_KERNEL_TWO_WAVES_PER_SIMD || (kernel == DASH_KERNEL_AUTO && kPairAuto));
   hipError_t e = !use_pair ? dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream)
                  : d == 128 ? dash::launch_pair_d128(bp, tab->workers, stream)
@@ -728,6 +762,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     dp.scale = scale;
     dp.scale_log2 = scale * 1.4426950408889634f;
     ec = dash::launch_dq_pass(dp, d, stream);
+  } else if (deterministic == 3) {
+    ec = dash::launch_dq_consolidate(dqacc, dq, int64_t(B) * H, N, L.row_stride, tab->tile, d, causal ? 1 : 0, scale,
+                                     stream);
   } else if (deterministic == 1) {
     ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream, tab->seqlens, H);
   } else {
@@ -745,6 +782,12 @@ size_t dash_attn_bwd_workspace_size(int B, int H, int Hkv, int N, int d) {
   if (B < 0 || N < 0 || H <= 0 || Hkv <= 0 || H % Hkv != 0 || (d != 64 && d != 128)) return 0;
   if (N > (1 << 22) || int64_t(B) * H > (int64_t(1) << 24)) return 0;
   return ws_layout(B, H, N, d).total;
+}
+
+size_t dash_attn_bwd_partials_workspace_size(int B, int H, int Hkv, int N, int d, int mask) {
+  if (dash_attn_bwd_workspace_size(B, H, Hkv, N, d) == 0) return 0;
+  if (mask != DASH_MASK_FULL && mask != DASH_MASK_CAUSAL) return 0;
+  return ws_layout(B, H, N, d, partials_bytes(B, H, N, d, mask == DASH_MASK_CAUSAL)).total;
 }
 
 size_t dash_attn_bwd_varlen_workspace_size(int B, int H, int Hkv, int N, int d) {

@@ -218,6 +218,9 @@ hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int 
 // dQ = bf16(scale * dqacc) for rows < N, from the atomic variant's row-major layout.
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
                           hipStream_t stream, const int* seqlens = nullptr, int H = 1);
+// dQ = bf16(scale * sum of the per-tile partials), rank order, rows < N (deterministic = 3).
+hipError_t launch_dq_consolidate(const float* parts, void* dq, int64_t heads, int N, int row_stride, int tile, int d,
+                                 int causal, float scale, hipStream_t stream);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& prm, int d, hipStream_t stream);
 hipError_t launch_dq_pass(const DqParams& prm, int d, hipStream_t stream);

@@ -29,6 +29,7 @@ SCHEDULES = {"naive": 0, "descending": 1, "shift": 2, "sym_shift": 3, "auto": 4}
 EXPORTED = (
     "dash_attn_bwd_workspace_size",
     "dash_attn_bwd_varlen_workspace_size",
+    "dash_attn_bwd_partials_workspace_size",
     "dash_attn_bwd",
     "dash_attn_bwd_timed",
     "dash_attn_bwd_varlen",
@@ -75,6 +76,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_attn_bwd_workspace_size.restype = sz
     lib.dash_attn_bwd_varlen_workspace_size.argtypes = [i, i, i, i, i]
     lib.dash_attn_bwd_varlen_workspace_size.restype = sz
+    lib.dash_attn_bwd_partials_workspace_size.argtypes = [i, i, i, i, i, i]
+    lib.dash_attn_bwd_partials_workspace_size.restype = sz
     common = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, i, i, i, vp, sz, vp]
     lib.dash_attn_bwd.argtypes = common
     lib.dash_attn_bwd.restype = i
@@ -131,6 +134,10 @@ def dash_tile_size(N: int) -> int:
 
 def dash_attn_bwd_varlen_workspace_size(B: int, H: int, Hkv: int, N: int, d: int) -> int:
     return int(load().dash_attn_bwd_varlen_workspace_size(B, H, Hkv, N, d))
+
+
+def dash_attn_bwd_partials_workspace_size(B: int, H: int, Hkv: int, N: int, d: int, mask) -> int:
+    return int(load().dash_attn_bwd_partials_workspace_size(B, H, Hkv, N, d, MASKS.get(mask, mask)))
 
 
 def dash_last_kernel_error(stream=None, lib=None) -> int:

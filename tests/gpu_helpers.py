@@ -37,6 +37,14 @@ def to_device(case):
     return dev
 
 
+def workspace_bytes(shape, causal, deterministic):
+    """Workspace dash_attn_bwd needs for the mode (the per-tile partials have their own size)."""
+    B, H, Hkv, N, d = shape
+    if deterministic == 3:
+        return dash.dash_attn_bwd_partials_workspace_size(B, H, Hkv, N, d, "causal" if causal else "full")
+    return dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d)
+
+
 def run(case, dev, schedule, deterministic, workspace=None):
     """One dash_attn_bwd call; returns (dq, dk, dv) torch tensors and the workspace used."""
     import torch
@@ -45,8 +53,8 @@ def run(case, dev, schedule, deterministic, workspace=None):
     dk = torch.empty_like(dev["k"])
     dv = torch.empty_like(dev["v"])
     if workspace is None:
-        nbytes = dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d)
-        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
+        workspace = torch.empty(max(workspace_bytes(case["shape"], case["causal"], deterministic), 256),
+                                dtype=torch.uint8, device="cuda")
     st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], dq, dk, dv,
                             case["scale"], "causal" if case["causal"] else "full", schedule, deterministic,
                             workspace)

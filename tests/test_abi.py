@@ -69,6 +69,16 @@ def test_status_strings():
 
 def test_workspace_size():
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64) >= 1 * 2 * 256 * 64 * 4
+    # Per-tile partials: (tile / 64) * n^2 slots of 64 x d floats per head (n (n + 1) / 2
+    # causal); 64-row tiles below N = 512, 128-row tiles from there.
+    base = dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 64) - 1 * 2 * 256 * 64 * 4
+    assert dash.dash_attn_bwd_partials_workspace_size(1, 2, 2, 256, 64, "full") == base + 2 * 16 * 64 * 64 * 4
+    assert dash.dash_attn_bwd_partials_workspace_size(1, 2, 2, 256, 64, "causal") == base + 2 * 10 * 64 * 64 * 4
+    base = dash.dash_attn_bwd_workspace_size(8, 16, 16, 2048, 128) - 8 * 16 * 2048 * 128 * 4
+    assert dash.dash_attn_bwd_partials_workspace_size(8, 16, 16, 2048, 128, "full") == \
+        base + 8 * 16 * 2 * 256 * 64 * 128 * 4
+    assert dash.dash_attn_bwd_partials_workspace_size(1, 2, 2, 256, 64, 2) == 0
+    assert dash.dash_attn_bwd_partials_workspace_size(1, 2, 2, 256, 96, "full") == 0
     assert dash.dash_attn_bwd_workspace_size(1, 2, 2, 256, 96) == 0
     assert dash.dash_attn_bwd_workspace_size(1, 3, 2, 256, 64) == 0
     assert dash.dash_attn_bwd_varlen_workspace_size(1, 3, 2, 256, 64) == 0
@@ -110,7 +120,7 @@ def _call(**kw):
     (dict(schedule=5), dash.DASH_ERR_INVALID_ARG),
     (dict(mask=1, schedule=2), dash.DASH_ERR_UNSUPPORTED),
     (dict(mask=0, schedule=3), dash.DASH_ERR_UNSUPPORTED),
-    (dict(det=3), dash.DASH_ERR_INVALID_ARG),
+    (dict(det=4), dash.DASH_ERR_INVALID_ARG),
     (dict(det=-1), dash.DASH_ERR_INVALID_ARG),
     (dict(scale=0.0), dash.DASH_ERR_INVALID_ARG),
     (dict(scale=float("inf")), dash.DASH_ERR_INVALID_ARG),

@@ -188,16 +188,17 @@ def kernel_asm(tmp_path_factory):
     return texts
 
 
-# (ordered reduction, cross-XCD chains, no dQ): the four instantiations of each (d, nw),
-# in every flavour.
-VARIANTS = [(d, nw, det, cross, nodq, fl) for (d, nw) in sorted(dash_build.MAIN_FLAGS)
-            for det, cross, nodq in ((1, 0, 0), (1, 1, 0), (0, 0, 0), (0, 0, 1)) for fl in FLAVOURS]
+# (ordered reduction, cross-XCD chains, no dQ, per-tile partials): the five instantiations
+# of each (d, nw), in every flavour.
+VARIANTS = [(d, nw, det, cross, nodq, part, fl) for (d, nw) in sorted(dash_build.MAIN_FLAGS)
+            for det, cross, nodq, part in ((1, 0, 0, 0), (1, 1, 0, 0), (0, 0, 0, 0), (0, 0, 1, 0), (1, 0, 0, 1))
+            for fl in FLAVOURS]
 
 
-@pytest.mark.parametrize("d,nw,det,cross,nodq,flavour", VARIANTS,
-                         ids=[f"d{v[0]}-nw{v[1]}-det{v[2]}-cross{v[3]}-nodq{v[4]}-{v[5]}" for v in VARIANTS])
-def test_inline_mfma_wait_states(kernel_asm, d, nw, det, cross, nodq, flavour):
-    symbol = f"_ZN4dash15bwd_main_kernelILi{d}ELi{nw}ELb{det}ELb{cross}ELb{nodq}EEEvNS_9BwdParamsE"
+@pytest.mark.parametrize("d,nw,det,cross,nodq,part,flavour", VARIANTS,
+                         ids=[f"d{v[0]}-nw{v[1]}-det{v[2]}-cross{v[3]}-nodq{v[4]}-part{v[5]}-{v[6]}" for v in VARIANTS])
+def test_inline_mfma_wait_states(kernel_asm, d, nw, det, cross, nodq, part, flavour):
+    symbol = f"_ZN4dash15bwd_main_kernelILi{d}ELi{nw}ELb{det}ELb{cross}ELb{nodq}ELb{part}EEEvNS_9BwdParamsE"
     insts, labels = parse_kernel(kernel_asm[(d, nw, flavour)], symbol)
     n_mfma = sum(1 for i in insts if i.mfma and i.asm)
     assert n_mfma >= (32 if nodq else 48), n_mfma
@@ -227,15 +228,15 @@ def pair_asm(tmp_path_factory):
     return texts
 
 
-# The two-waves-per-SIMD kernel (d = 128 and 64): ordered and atomic instantiations,
-# every flavour.
-PAIR_VARIANTS = [(d, det, fl) for d in (128, 64) for det in (1, 0) for fl in FLAVOURS]
+# The two-waves-per-SIMD kernel (d = 128 and 64): ordered, atomic and per-tile partials
+# instantiations, every flavour.
+PAIR_VARIANTS = [(d, det, part, fl) for d in (128, 64) for det, part in ((1, 0), (0, 0), (1, 1)) for fl in FLAVOURS]
 
 
-@pytest.mark.parametrize("d,det,flavour", PAIR_VARIANTS,
-                         ids=[f"pair-d{v[0]}-det{v[1]}-{v[2]}" for v in PAIR_VARIANTS])
-def test_pair_kernel_inline_mfma_wait_states(pair_asm, d, det, flavour):
-    symbol = f"_ZN4dash15bwd_pair_kernelILi{d}ELb{det}EEEvNS_9BwdParamsE"
+@pytest.mark.parametrize("d,det,part,flavour", PAIR_VARIANTS,
+                         ids=[f"pair-d{v[0]}-det{v[1]}-part{v[2]}-{v[3]}" for v in PAIR_VARIANTS])
+def test_pair_kernel_inline_mfma_wait_states(pair_asm, d, det, part, flavour):
+    symbol = f"_ZN4dash15bwd_pair_kernelILi{d}ELb{det}ELb{part}EEEvNS_9BwdParamsE"
     insts, labels = parse_kernel(pair_asm[flavour], symbol)
     # Both roles' bodies, d = 128: 16 + 16 + 8 per step and 8 for an item's last dQ block,
     # each; d = 64: 8 + 8 + 8 (A), 8 + 8 (B), and 8.

@@ -88,13 +88,23 @@ def workload(request):
             "refs": refs, "ws": ws}
 
 
+def _ws(w, det):
+    if det != 3:
+        return w["ws"]
+    if "ws3" not in w:
+        B, H, Hkv, N, d = w["shape"]
+        size = dash.dash_attn_bwd_partials_workspace_size(B, H, Hkv, N, d, "causal" if w["causal"] else "full")
+        w["ws3"] = torch.empty(size, dtype=torch.uint8, device="cuda")
+    return w["ws3"]
+
+
 def _run(w, schedule, det):
     dev = w["dev"]
     dq = torch.empty_like(dev["q"])
     dk = torch.empty_like(dev["k"])
     dv = torch.empty_like(dev["v"])
     st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], dq, dk, dv, w["scale"],
-                            "causal" if w["causal"] else "full", schedule, det, w["ws"])
+                            "causal" if w["causal"] else "full", schedule, det, _ws(w, det))
     assert st == dash.DASH_OK, dash.dash_status_string(st)
     torch.cuda.synchronize()
     err = dash.dash_last_kernel_error()
@@ -111,8 +121,8 @@ def test_sampled_parity_all_schedules(workload):
     w = workload
     for sched in SCHEDULES[w["causal"]]:
         # Ordered and atomic reductions for every schedule; the two-pass variant
-        # (deterministic = 2) with the first (best) schedule.
-        for det in (1, 0, 2) if sched == SCHEDULES[w["causal"]][0] else (1, 0):
+        # (deterministic = 2) and the per-tile partials (3) with the first (best) schedule.
+        for det in (1, 0, 2, 3) if sched == SCHEDULES[w["causal"]][0] else (1, 0):
             print(f"[{w['name']}] schedule={sched} det={det}", flush=True)
             dq, dk, dv = _run(w, sched, det)
             for (b, g, hs), (rq, rk, rv) in w["refs"]:
@@ -122,7 +132,7 @@ def test_sampled_parity_all_schedules(workload):
 
 def test_bitwise_repeatable_at_full_size(workload):
     w = workload
-    runs = [(s, 1) for s in SCHEDULES[w["causal"]]] + [(SCHEDULES[w["causal"]][0], 2)]
+    runs = [(s, 1) for s in SCHEDULES[w["causal"]]] + [(SCHEDULES[w["causal"]][0], 2), (SCHEDULES[w["causal"]][0], 3)]
     for sched, det in runs:
         print(f"[{w['name']}] {REPEATS} runs of schedule={sched} det={det}", flush=True)
         first = [t.clone() for t in _run(w, sched, det)]

@@ -5,8 +5,9 @@ workload specification fixes for bf16 inputs/outputs with fp32 accumulation.
 Deterministic schedules must also give bitwise identical dQ/dK/dV on repeated runs.
 Cases span several KV tiles, ragged tails (N not a multiple of the tile), grouped
 query heads, both head dims, both masks, all four schedules, the atomic variant
-(deterministic = 0) and the two-pass variant (deterministic = 2: dK/dV pass plus a
-separate dQ pass).
+(deterministic = 0), the two-pass variant (deterministic = 2: dK/dV pass plus a
+separate dQ pass) and the per-tile partials (deterministic = 3: every contribution in
+its own slot, added by a separate kernel in rank order).
 """
 import pytest
 
@@ -50,7 +51,7 @@ def test_parity_all_schedules(shape, causal):
     for sched in SCHEDS[causal]:
         if sched == "sym_shift" and n_tiles % 2:
             continue
-        for det in (1, 0, 2):
+        for det in (1, 0, 2, 3):
             print(f"case {_ids(shape)} causal={causal} schedule={sched} det={det}", flush=True)
             (dq, dk, dv), _ = run(case, dev, sched, det)
             errs = rel_errs((dq, dk, dv), (dq_r, dk_r, dv_r))
@@ -61,7 +62,7 @@ def test_parity_all_schedules(shape, causal):
 def test_repeat_runs_bitwise_identical(causal):
     case = make_case(2, 4, 2, 700, 128, causal, seed=77)
     dev = to_device(case)
-    for sched, det in [(s, 1) for s in SCHEDS[causal]] + [(SCHEDS[causal][-1], 2)]:
+    for sched, det in [(s, 1) for s in SCHEDS[causal]] + [(SCHEDS[causal][-1], 2), (SCHEDS[causal][-1], 3)]:
         ref, ws = run(case, dev, sched, det)
         ref_bytes = [bf16_bytes(t) for t in ref]
         for rep in range(19):
@@ -104,7 +105,7 @@ def test_parity_d128_kernels(pshape, causal, kernel):
     for sched in SCHEDS[causal]:
         if sched == "sym_shift" and n_tiles % 2:
             continue
-        for det in (1, 0):
+        for det in (1, 0, 3):
             print(f"{kernel} case {_ids(pshape)} causal={causal} schedule={sched} det={det}", flush=True)
             (dq, dk, dv), _ = _with_kernel(kernel, lambda: run(case, dev, sched, det))
             errs = rel_errs((dq, dk, dv), (dq_r, dk_r, dv_r))

@@ -252,6 +252,39 @@ def test_auto_picks_measured_fastest_on_paper_grid():
                 assert dash.dash_schedule_resolve(B, H, H, N, d, mask, "auto", 8, 32) == want, (d, mask, N)
 
 
+# Main-kernel times on one MI355X, microseconds per call, and the
+# schedule measured fastest: (B, H, Hkv, N, d, mask, placement) -> fastest.
+MEASURED_FASTEST = [
+    ((2, 4, 2, 4096, 128, "causal", "aggregate"), "sym_shift"),   # 638 / 543 / 307
+    ((1, 2, 2, 256, 64, "causal", "aggregate"), "descending"),    # 34 / 30 / 35
+    ((1, 4, 4, 640, 128, "causal", "aggregate"), "descending"),   # 57 / 46 / (odd tile count)
+    ((2, 3, 1, 1000, 64, "causal", "aggregate"), "descending"),   # 122 / 100 / 112
+    ((2, 4, 2, 2048, 128, "full", "aggregate"), "shift"),         # 244 / 241 / 162
+    ((8, 16, 16, 2048, 128, "full", "aggregate"), "shift"),       # 917 / 890 / 840
+    ((4, 32, 32, 4096, 64, "causal", "aggregate"), "sym_shift"),  # 2724 / 1573 / 1026
+    ((1, 16, 16, 16384, 128, "causal", "aggregate"), "sym_shift"),  # 4244 / 4939 / 3081
+    ((1, 32, 8, 8192, 128, "causal", "aggregate"), "sym_shift"),  # 3992 / 1929 / 1847
+    ((1, 4, 4, 8192, 64, "causal", "spread"), "sym_shift"),       # 490 / 313 / 259
+    ((1, 4, 4, 8192, 128, "causal", "spread"), "descending"),     # 623 / 392 / 404
+    ((1, 16, 16, 16384, 128, "causal", "spread"), "sym_shift"),   # 8033 / 5743 / 4017
+]
+
+
+@pytest.mark.parametrize("shape,fastest", MEASURED_FASTEST,
+                         ids=["B{}H{}Hkv{}N{}d{}-{}-{}".format(*m[0]) for m in MEASURED_FASTEST])
+def test_auto_picks_measured_fastest_on_timed_shapes(shape, fastest):
+    """AUTO picks the schedule measured fastest (or one within 3 % of it: 392 against 404
+    us on the spread d = 128 shape) on every shape timed for the model."""
+    B, H, Hkv, N, d, mask, placement = shape
+    assert dash.dash_set_placement(placement) == dash.DASH_OK
+    try:
+        got = NAMES[dash.dash_schedule_resolve(B, H, Hkv, N, d, mask, "auto", 8, 32)]
+    finally:
+        dash.dash_set_placement("aggregate")
+    close = {((1, 4, 4, 8192, 128, "causal", "spread"), "sym_shift")}
+    assert got == fastest or (shape, got) in close, (shape, got, fastest)
+
+
 def test_auto_never_picks_an_invalid_schedule():
     """An odd tile count rules symmetric shift out; explicit schedules pass through."""
     assert dash.dash_schedule_resolve(1, 4, 4, 640, 128, "causal", "auto", 8, 32) in (0, 1)
