@@ -481,6 +481,77 @@ def sweep(steps, warmup):
     return out
 
 
+# Per-wave phase counters of the profiling build (include/dash_profile.h): slot numbers.
+PROF_SLOTS = 20
+PHASES = {0: "rest_of_step", 1: "step_barrier", 2: "turn_bookkeeping", 3: "turn_wait", 4: "ack_and_signal",
+          5: "handoff", 8: "phase_S_or_dP", 9: "phase_softmax_or_dq_stores", 10: "phase_dS", 12: "phase_dV_or_dK",
+          13: "phase_loads", 16: "item_prologue", 17: "item_flush", 18: "item_epilogue"}
+# Per-task costs (us) the host schedule model uses (measured_costs in csrc/dash_api.cpp).
+MODEL_COSTS = {64: (3.2, 0.45, 2.5), 128: (5.6, 0.9, 2.5)}
+
+
+def phases(workload, schedules, steps, warmup):
+    """Pipeline bubbles of each schedule, measured and predicted (DASH paper, section 3.1:
+    the DAG's idle time; section 4.2: synchronisation latency). Runs the profiling build
+    (per-wave phase cycle counters) and returns one record per schedule:
+      - measured: cycles per wave, the share of all wave-cycles spent waiting for a dQ turn
+        (turn_wait_frac), the share of steps whose turn had not come when polled, and the
+        idle share of the whole launch (1 - busy wave-cycles / (waves x longest wave),
+        busy = total minus turn waits: the tail of early finishers counts as idle);
+      - predicted: the same idle share of the host DAG model (dash_schedule_makespan with
+        the library's per-task costs): 1 - tasks (c + r) / (CUs x makespan)."""
+    import numpy as np
+    import torch
+
+    from scheduling_fa_attn_amd import dash
+    from scheduling_fa_attn_amd.build import PROF_LIB_PATH
+
+    lib = dash.load(PROF_LIB_PATH)
+    if not hasattr(lib, "dash_profile_attach"):
+        raise SystemExit("--phases needs the profiling build (build(profile=True)) loaded first")
+    B, H, Hkv, N, d, causal, best, others, cfg_index = WORKLOADS[workload]
+    mask = "causal" if causal else "full"
+    shape = (B, H, Hkv, N, d)
+    dev = make_inputs(B, H, Hkv, N, d, causal, 1000 + cfg_index)
+    ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.zeros(cus * 8 * PROF_SLOTS, dtype=torch.int64, device="cuda")
+    c, r, r_remote = MODEL_COSTS[d]
+    out = []
+    for sched in schedules:
+        ms, main_ms, _ = time_schedule(dev, shape, causal, sched, 1, steps, warmup, ws)
+        buf.zero_()
+        assert lib.dash_profile_attach(buf.data_ptr()) == 0
+        try:
+            time_schedule(dev, shape, causal, sched, 1, 1, 0, ws)
+        finally:
+            lib.dash_profile_attach(None)
+        a = buf.cpu().numpy().reshape(cus, 8, PROF_SLOTS).astype(np.float64)
+        active = a[:, :, 7] > 0
+        tot = a[:, :, 7][active]
+        wait = a[:, :, 3][active]
+        span = float(tot.max())
+        nsteps = float(a[:, :, 6][active].sum())
+        waves = int(active.sum())
+        # The kernel's waves per CU (4 or 8): CUs with no work still count as idle.
+        per_cu = int(active.sum(axis=1).max())
+        idle = 1.0 - float((tot - wait).sum()) / (cus * per_cu * span)
+        rec, _ = dash.dash_schedule_table(B, H, Hkv, N, mask, sched, 8, cus // 8)
+        span_model = dash.dash_schedule_makespan(B, H, Hkv, N, mask, sched, 8, cus // 8, c, r, r_remote)
+        pred = 1.0 - len(rec) * (c + r) / (cus * span_model)
+        res = {"schedule": sched, "ms_per_call": round(ms, 4), "main_kernel_ms": round(main_ms, 4),
+               "waves": waves, "longest_wave_cycles": span,
+               "cycles_per_wave_step": {PHASES[k]: round(float(a[:, :, k][active].sum()) / nsteps * per_cu, 1)
+                                        for k in PHASES if a[:, :, k][active].sum() > 0},
+               "turn_wait_frac": round(float(wait.sum() / tot.sum()), 4),
+               "late_turn_step_frac": round(float(a[:, :, 14][active].sum()) / nsteps, 4),
+               "measured_idle_frac": round(idle, 4),
+               "model_makespan_us": round(span_model, 1), "model_idle_frac": round(pred, 4)}
+        log(f"  phases {workload} {sched}: " + json.dumps(res))
+        out.append(res)
+    return {"workload": workload, "phases": out, "costs_us": {"c": c, "r_local": r, "r_remote": r_remote}}
+
+
 # Sources of the main kernel: the HBM-traffic figures in profiles/ hold for the kernel
 # these hashed to when the counters were taken.
 COMMON_SOURCES = ("scheduling_fa_attn_amd/csrc/device_common.h", "scheduling_fa_attn_amd/csrc/kernels.h",
@@ -492,11 +563,11 @@ KERNEL_SOURCES = {"bwd_main": ("scheduling_fa_attn_amd/csrc/bwd_main.hip",) + CO
 def main_kernel_name(N, d, kernel_choice):
     """The main kernel dash_attn_bwd launches (deterministic = 1, one XCD per chain)."""
     if N >= 512 and kernel_choice != "one_wave":
-        return f"bwd_pair_kernel<{d}, true>"
-    return f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false>"
+        return f"bwd_pair_kernel<{d}, true, false>"
+    return f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false, false>"
 
 
-def kernel_source_hash(kernel="bwd_pair_kernel<128, true>"):
+def kernel_source_hash(kernel="bwd_pair_kernel<128, true, false>"):
     import hashlib
 
     h = hashlib.sha256()
@@ -541,6 +612,9 @@ def main():
     ap.add_argument("--sweep", action="store_true",
                     help="only time every schedule and the atomic variant over the paper's grid (16 384 tokens, "
                          "hidden 2048, N = 512 .. 16384, d = 64 and 128, both masks) and print one JSON line")
+    ap.add_argument("--phases", action="store_true",
+                    help="only measure pipeline bubbles per deterministic schedule of --workload with the profiling "
+                         "build (per-wave phase cycles, turn waits) beside the DAG model's prediction; one JSON line")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (the reference for the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scale factor) and exit")
@@ -566,6 +640,12 @@ def main():
 
     torch.cuda.set_device(0)
     from scheduling_fa_attn_amd import dash
+    if args.phases:
+        wl = WORKLOADS[args.workload]
+        scheds = [args.schedule] if args.schedule else [wl[6]] + list(wl[7])
+        res = phases(args.workload, scheds, args.steps, args.warmup)
+        print(json.dumps(res), flush=True)
+        return
     if dash.dash_set_kernel(args.kernel) != dash.DASH_OK:
         raise SystemExit(f"dash_set_kernel({args.kernel}) failed")
     if args.sweep:
