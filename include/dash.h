@@ -185,6 +185,29 @@ int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void*
                         void* workspace, size_t workspace_bytes, void* stream,
                         void* main_start, void* main_stop);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): dash_attn_bwd without a workspace
+ * argument. Its workspace and its schedule table live in a static device array of the
+ * library, 64 MiB per device, held from the loading of the library until the process
+ * ends: 8 MiB for schedule tables and 56 MiB of workspace, so the call accepts shapes
+ * whose dash_attn_bwd_workspace_size is at most 56 MiB (B*H*ceil(N/tile)*tile*d*4 bytes
+ * of accumulator plus small row terms; e.g. B=2, H=16, N=2048, d=128) and returns
+ * DASH_ERR_WORKSPACE for larger ones. deterministic = 0, 1 or 2 (3, the per-tile
+ * partials, returns DASH_ERR_UNSUPPORTED). The call allocates nothing: no hipMalloc,
+ * hipFree or allocating HIP call. The first call for a shape builds its schedule table
+ * on the host and copies it into the array on `stream` (later calls with that shape copy
+ * nothing; tables of older shapes are dropped when the table part is full). Every call
+ * on a device shares that device's array, which keeps the last call's contents: calls
+ * that overlap on one device (e.g. on two streams) race and give undefined results;
+ * calls ordered on one stream are safe. Results are bitwise those of dash_attn_bwd with
+ * the same arguments. dash_last_kernel_error(stream) reports its kernel-side status.
+ * Other errors as dash_attn_bwd. */
+int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                          const void* dO, const float* lse,
+                          void* dq, void* dk, void* dv,
+                          int B, int H, int Hkv, int N, int d, float softmax_scale,
+                          int mask, int schedule, int deterministic, void* stream);
+
 /* The forward pass ("Writing an Attention Kernel", Steps 1 and 2): O = softmax(s Q K^T) V
  * and lse = the natural-log log-sum-exp of each query row's scaled scores s q.k, i.e.
  * the o and lse that dash_attn_bwd takes. Key tiles are visited in ascending order with

@@ -29,6 +29,16 @@ constexpr int64_t kMaxTasks = int64_t(1) << 30;
 // of 16 384 tokens at hidden size 2048 is about 2 MB).
 constexpr size_t kStagingBytes = size_t(64) << 20;
 
+// Device memory of dash_attn_bwd_noalloc, for callers that cannot allocate: every device
+// the library runs on holds one copy of this array from the loading of the library to
+// the end of the process. The first kScratchTableBytes hold schedule tables (and, once,
+// at device set-up, the topology probe's output), the rest is the call's workspace.
+// Host code never uses the array's name as an address: the per-device address comes
+// from hipGetSymbolAddress at set-up (DeviceState::scratch).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+constexpr size_t kScratchTableBytes = size_t(8) << 20;
+__device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+
 int tile_for(int N) { return N < 512 ? 64 : 128; }
 
 
@@ -184,6 +194,17 @@ int check_sizes(int B, int H, int Hkv, int N, int d, int mask, int schedule) {
   return DASH_OK;
 }
 
+// Host image of a device table: worker_begin | items | tasks | step records | batch lengths,
+// each part 256-byte aligned.
+struct TableImage {
+  std::vector<char> bytes;
+  size_t it_off = 0, tk_off = 0, st_off = 0, ln_off = 0;
+  bool has_lens = false;
+  int workers = 0;
+  int tile = 0;
+  bool xcd_local = true;
+};
+
 struct DevTable {
   void* buf = nullptr;  // worker_begin | items | tasks | steps
   const int* worker_begin = nullptr;
@@ -207,6 +228,11 @@ struct DeviceState {
   // workspace), for dash_last_kernel_error; host bookkeeping only.
   std::map<void*, const int*> last_err;
   int* err_host = nullptr;  // pinned word that dash_last_kernel_error copies into (g_err_mu)
+  // This device's copy of `scratch` (hipGetSymbolAddress at set-up), and the schedule
+  // tables dash_attn_bwd_noalloc has copied into its table part: key -> (offset, image).
+  char* scratch = nullptr;
+  size_t scratch_tables_used = 0;
+  std::map<std::tuple<int, int, int, int, int, int, int, int>, std::pair<size_t, TableImage>> scratch_tables;
   std::map<std::tuple<int, int, int, int, int, int, int, int>, DevTable> tables;
   // Variable-length batches: pinned staging for the stream-ordered table copies into the
   // caller's workspace (allocated at device set-up, grown only for a table larger than it).
@@ -249,18 +275,18 @@ int init_device(int dev, DeviceState* st) {
   int rate_khz = 0;
   if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && rate_khz > 0)
     st->ticks_per_second = static_cast<long long>(rate_khz) * 1000LL;
-  if (hipHostMalloc(reinterpret_cast<void**>(&st->err_host), sizeof(int), hipHostMallocDefault) != hipSuccess)
-    return DASH_ERR_HIP;
-  if (hipHostMalloc(reinterpret_cast<void**>(&st->staging.buf), kStagingBytes, hipHostMallocDefault) != hipSuccess)
-    return DASH_ERR_HIP;
-  st->staging.cap = kStagingBytes;
-  int* probe = nullptr;
-  if (hipMalloc(reinterpret_cast<void**>(&probe), sizeof(int) * st->cus) != hipSuccess) return DASH_ERR_HIP;
+  // This device's copy of the scratch array (its address differs per device). Set-up
+  // allocates nothing: the probe below writes into the scratch array's table part, which
+  // no call uses yet.
+  void* scr = nullptr;
+  if (hipGetSymbolAddress(&scr, HIP_SYMBOL(scratch)) != hipSuccess || scr == nullptr) return DASH_ERR_HIP;
+  st->scratch = static_cast<char*>(scr);
+  if (size_t(st->cus) * sizeof(int) > kScratchTableBytes) return DASH_ERR_UNSUPPORTED;
+  int* probe = reinterpret_cast<int*>(st->scratch);
   hipError_t e = dash::launch_topology_probe(probe, st->cus, nullptr);
   std::vector<int> ids(st->cus, -1);
   if (e == hipSuccess) e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(ids.data(), probe, sizeof(int) * st->cus, hipMemcpyDeviceToHost);
-  (void)hipFree(probe);
   if (e == hipErrorCooperativeLaunchTooLarge) return DASH_ERR_NOT_CORESIDENT;
   if (e != hipSuccess) return DASH_ERR_HIP;
   int max_id = -1;
@@ -337,17 +363,6 @@ int get_table(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int sc
   *out = &ins.first->second;
   return DASH_OK;
 }
-
-// Host image of a device table: worker_begin | items | tasks | step records | batch lengths,
-// each part 256-byte aligned.
-struct TableImage {
-  std::vector<char> bytes;
-  size_t it_off = 0, tk_off = 0, st_off = 0, ln_off = 0;
-  bool has_lens = false;
-  int workers = 0;
-  int tile = 0;
-  bool xcd_local = true;
-};
 
 void make_image(const dash::Table& t, int H, int tile, const std::vector<int>* lens, TableImage* img) {
   const size_t wb_bytes = align256(sizeof(int32_t) * t.worker_begin.size());
@@ -499,6 +514,12 @@ int stage_table(DeviceState* st, const TableImage& img, void* dst, hipStream_t s
   };
   while (retire_front(false)) {
   }
+  if (R.buf == nullptr) {
+    // First variable-length call on this device.
+    if (hipHostMalloc(reinterpret_cast<void**>(&R.buf), kStagingBytes, hipHostMallocDefault) != hipSuccess)
+      return DASH_ERR_HIP;
+    R.cap = kStagingBytes;
+  }
   if (size > R.cap) {
     // A table larger than the ring: wait for the copies in flight and grow it.
     while (retire_front(true)) {
@@ -552,10 +573,59 @@ int stage_table(DeviceState* st, const TableImage& img, void* dst, hipStream_t s
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// dash_attn_bwd_noalloc: the table of this shape in the scratch array's table part,
+// copied there on the call's stream the first time the shape comes (the tables of
+// earlier shapes are dropped when the part is full). The copy reads pageable host
+// memory, which HIP stages before hipMemcpyAsync returns; the image is kept all the same.
+// Caller holds g_mu.
+int get_table_scratch(DeviceState* st, int B, int H, int Hkv, int N, bool causal, int schedule, hipStream_t stream,
+                      DevTable* out) {
+  const int tile = tile_for(N);
+  const auto key = std::make_tuple(B, H, Hkv, N, tile, causal ? 1 : 0, schedule, g_placement);
+  auto found = st->scratch_tables.find(key);
+  if (found != st->scratch_tables.end()) {
+    *out = table_at(found->second.second, st->scratch + found->second.first);
+    return DASH_OK;
+  }
+  dash::SchedParams sp;
+  sp.B = B;
+  sp.H = H;
+  sp.Hkv = Hkv;
+  sp.N = N;
+  sp.tile = tile;
+  sp.causal = causal;
+  sp.kind = static_cast<Sched>(schedule);
+  sp.num_xcd = st->num_xcd;
+  sp.cus_per_xcd = st->cus_per_xcd;
+  sp.spread = g_placement == DASH_PLACEMENT_SPREAD;
+  dash::Table t;
+  std::string err;
+  const int s = dash::build_table(sp, &t, &err);
+  if (s != 0) return s;
+  TableImage img;
+  make_image(t, H, tile, nullptr, &img);
+  const size_t size = align256(img.bytes.size());
+  if (size > kScratchTableBytes) return DASH_ERR_WORKSPACE;
+  if (st->scratch_tables_used + size > kScratchTableBytes) {
+    st->scratch_tables.clear();
+    st->scratch_tables_used = 0;
+  }
+  const size_t off = st->scratch_tables_used;
+  if (hipMemcpyAsync(st->scratch + off, img.bytes.data(), img.bytes.size(), hipMemcpyHostToDevice, stream) !=
+      hipSuccess)
+    return DASH_ERR_HIP;
+  st->scratch_tables_used += size;
+  auto ins = st->scratch_tables.emplace(key, std::make_pair(off, std::move(img)));
+  *out = table_at(ins.first->second.second, st->scratch + off);
+  return DASH_OK;
+}
+
+// noalloc: the workspace and the table are the device's scratch array (the caller passes
+// no workspace); nothing is allocated.
 int run_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse, void* dq,
             void* dk, void* dv, int B, int H, int Hkv, int N, int d, float scale, int mask, int schedule,
             int deterministic, void* workspace, size_t workspace_bytes, void* stream_ptr, void* ev_start,
-            void* ev_stop, const int* seqlens = nullptr) {
+            void* ev_stop, const int* seqlens = nullptr, bool noalloc = false) {
   const int requested = schedule;
   schedule = resolve_schedule(schedule, N, mask);
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
@@ -585,7 +655,12 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   for (const void* ptr : ptrs)
     if (ptr == nullptr || !aligned(ptr, 16)) return DASH_ERR_INVALID_ARG;
   if (lse == nullptr || !aligned(lse, 4)) return DASH_ERR_INVALID_ARG;
-  if (workspace == nullptr || !aligned(workspace, 256)) return DASH_ERR_INVALID_ARG;
+  if (noalloc) {
+    if (seqlens || deterministic == 3) return DASH_ERR_UNSUPPORTED;
+    workspace_bytes = kScratchBytes - kScratchTableBytes;
+  } else if (workspace == nullptr || !aligned(workspace, 256)) {
+    return DASH_ERR_INVALID_ARG;
+  }
   const WsLayout L = deterministic == 3 ? ws_layout(B, H, N, d, partials_bytes(B, H, N, d, mask == DASH_MASK_CAUSAL))
                                         : ws_layout(B, H, N, d);
   // Variable-length batches: the call's table goes into the workspace after the base part.
@@ -601,6 +676,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     std::lock_guard<std::mutex> lock(g_mu);
     s = get_device(&st);
     if (s != DASH_OK) return s;
+    if (noalloc) workspace = st->scratch + kScratchTableBytes;
     if (requested == DASH_SCHED_AUTO) {
       const auto key = std::make_tuple(B, H, Hkv, N, d, mask, st->num_xcd, st->cus_per_xcd, g_placement);
       auto it = g_auto.find(key);
@@ -636,6 +712,9 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
       s = stage_table(st, *img, dst, stream);
       if (s != DASH_OK) return s;
       varlen_tab = table_at(*img, dst);
+      tab = &varlen_tab;
+    } else if (noalloc) {
+      s = get_table_scratch(st, B, H, Hkv, N, causal, schedule, stream, &varlen_tab);
       tab = &varlen_tab;
     } else {
       s = get_table(st, B, H, Hkv, N, causal, schedule, &tab);
@@ -843,6 +922,13 @@ int dash_attn_bwd_varlen(const void* q, const void* k, const void* v, const void
                  workspace, workspace_bytes, stream, nullptr, nullptr, seqlens);
 }
 
+int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                          const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
+                          float softmax_scale, int mask, int schedule, int deterministic, void* stream) {
+  return run_bwd(q, k, v, o, dO, lse, dq, dk, dv, B, H, Hkv, N, d, softmax_scale, mask, schedule, deterministic,
+                 nullptr, 0, stream, nullptr, nullptr, nullptr, true);
+}
+
 int dash_attn_bwd_timed(const void* q, const void* k, const void* v, const void* o, const void* dO,
                         const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int N, int d,
                         float softmax_scale, int mask, int schedule, int deterministic, void* workspace,
@@ -863,6 +949,10 @@ int dash_last_kernel_error(void* stream) {
     auto w = found->second.last_err.find(stream);
     if (w == found->second.last_err.end()) return DASH_OK;
     word = w->second;
+    if (found->second.err_host == nullptr &&
+        hipHostMalloc(reinterpret_cast<void**>(&found->second.err_host), sizeof(int), hipHostMallocDefault) !=
+            hipSuccess)
+      return DASH_ERR_HIP;
     host = found->second.err_host;
   }
   // Only this stream is waited for: the word is copied into pinned host memory by a copy

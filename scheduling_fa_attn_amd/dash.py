@@ -32,6 +32,7 @@ EXPORTED = (
     "dash_attn_bwd_partials_workspace_size",
     "dash_attn_bwd",
     "dash_attn_bwd_timed",
+    "dash_attn_bwd_noalloc",
     "dash_attn_bwd_varlen",
     "dash_last_kernel_error",
     "dash_status_string",
@@ -83,6 +84,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_attn_bwd.restype = i
     lib.dash_attn_bwd_timed.argtypes = common + [vp, vp]
     lib.dash_attn_bwd_timed.restype = i
+    lib.dash_attn_bwd_noalloc.argtypes = common[:18] + [vp]
+    lib.dash_attn_bwd_noalloc.restype = i
     lib.dash_attn_bwd_varlen.argtypes = common[:14] + [ctypes.POINTER(ctypes.c_int)] + common[14:]
     lib.dash_attn_bwd_varlen.restype = i
     lib.dash_last_kernel_error.argtypes = [vp]
@@ -276,6 +279,23 @@ def dash_attn_bwd(q, k, v, o, dO, lse, dq, dk, dv, softmax_scale, mask, schedule
         return int(lib.dash_attn_bwd_timed(*args, ctypes.c_void_p(main_start or 0),
                                            ctypes.c_void_p(main_stop or 0)))
     return int(lib.dash_attn_bwd(*args))
+
+
+def dash_attn_bwd_noalloc(q, k, v, o, dO, lse, dq, dk, dv, softmax_scale, mask, schedule, deterministic,
+                          stream=None, lib=None) -> int:
+    """Call dash_attn_bwd_noalloc (no workspace: the library's static device scratch) on
+    torch device tensors laid out as for dash_attn_bwd. Returns the status code."""
+    import torch
+
+    lib = lib or load()
+    B, H, N, d = q.shape
+    Hkv = k.shape[1]
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    return int(lib.dash_attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                         _ptr(dv), B, H, Hkv, N, d, float(softmax_scale), MASKS.get(mask, mask),
+                                         SCHEDULES.get(schedule, schedule), int(deterministic),
+                                         ctypes.c_void_p(stream)))
 
 
 def dash_attn_bwd_varlen(q, k, v, o, dO, lse, dq, dk, dv, seqlens, softmax_scale, mask, schedule, deterministic,
