@@ -399,6 +399,13 @@ def measure_workload(name, schedule, steps, warmup, compare):
         extra["two_pass_" + schedule] = round(fl / (ms_t * 1e-3) / 1e12, 2)
         log(f"  {schedule} two-pass (dK/dV pass + separate dQ pass): {ms_t:.3f} ms/step "
             f"({extra['two_pass_' + schedule]:.1f} TFLOPS)")
+        # Both automatic choices: the schedule (host cost model) and the reproducible mode
+        # (ordered reduction or two-pass) for this shape.
+        mode = dash.dash_deterministic_resolve(B, H, Hkv, N, d, "causal" if causal else "full", 4)
+        ms_aa, _, _ = time_schedule(dev, shape, causal, "auto", 4, steps, warmup, ws)
+        extra["auto_schedule_auto_mode"] = round(fl / (ms_aa * 1e-3) / 1e12, 2)
+        log(f"  schedule auto, deterministic auto (mode {mode}): {ms_aa:.3f} ms/step "
+            f"({extra['auto_schedule_auto_mode']:.1f} TFLOPS)")
         ws3 = torch.empty(dash.dash_attn_bwd_partials_workspace_size(B, H, Hkv, N, d, "causal" if causal else "full"),
                           dtype=torch.uint8, device="cuda")
         ms_p, _, _ = time_schedule(dev, shape, causal, schedule, 3, steps, warmup, ws3)

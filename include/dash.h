@@ -157,6 +157,11 @@ size_t dash_attn_bwd_varlen_workspace_size(int B, int H, int Hkv, int N, int d);
  *   walks all key tiles for each query tile, recomputing S and dP, with dQ kept in
  *   registers (deterministic, no cross-CU reduction). The schedule sets the tile
  *   order of the dK/dV pass.
+ * deterministic = 4: the bitwise-reproducible mode measured faster on MI355X for the
+ *   shape, 1 or 2 (dash_deterministic_resolve names it): the ordered reduction with one
+ *   query head per KV head, the two-pass variant for grouped-query attention (two or more
+ *   query heads per KV head at d = 128, four or more at d = 64), where the ordered
+ *   reduction has fewer lanes and a larger hot set per XCD. The workspace is the same.
  * deterministic = 3: per-tile partials, the other deterministic alternative of section
  *   5 (FlashAttention-2 style): every dQ contribution of every KV tile is written to its
  *   own fp32 slot, with no waits, and a separate kernel adds each query step's slots in
@@ -296,6 +301,11 @@ int dash_schedule_table_varlen(int B, int H, int Hkv, int N, const int* seqlens,
 int dash_schedule_makespan(int B, int H, int Hkv, int N, int mask, int schedule,
                            int num_xcd, int cus_per_xcd,
                            double c, double r_local, double r_remote, double* makespan);
+
+/* The mode dash_attn_bwd runs for `deterministic` (host-only): 0 .. 3 are returned
+ * unchanged after the argument checks; 4 becomes 1 or 2 as described at dash_attn_bwd.
+ * Returns the mode (>= 0) or a dash_status code (< 0) for invalid arguments. */
+int dash_deterministic_resolve(int B, int H, int Hkv, int N, int d, int mask, int deterministic);
 
 /* The schedule dash_attn_bwd runs for `schedule` (host-only): a concrete schedule is
  * returned unchanged after the argument checks; DASH_SCHED_AUTO becomes the valid

@@ -41,6 +41,7 @@ EXPORTED = (
     "dash_schedule_table_varlen",
     "dash_schedule_makespan",
     "dash_schedule_resolve",
+    "dash_deterministic_resolve",
     "dash_set_placement",
     "dash_set_kernel",
     "dash_set_wait_timeout",
@@ -106,6 +107,8 @@ def open_library(path: str) -> ctypes.CDLL:
     lib.dash_schedule_makespan.restype = i
     lib.dash_schedule_resolve.argtypes = [i, i, i, i, i, i, i, i, i]
     lib.dash_schedule_resolve.restype = i
+    lib.dash_deterministic_resolve.argtypes = [i, i, i, i, i, i, i]
+    lib.dash_deterministic_resolve.restype = i
     lib.dash_set_placement.argtypes = [i]
     lib.dash_set_placement.restype = i
     lib.dash_set_kernel.argtypes = [i]
@@ -194,6 +197,12 @@ def dash_schedule_resolve(B, H, Hkv, N, d, mask, schedule, num_xcd, cus_per_xcd,
     a negative value is an error status."""
     return int((lib or load()).dash_schedule_resolve(B, H, Hkv, N, d, MASKS.get(mask, mask),
                                                      SCHEDULES.get(schedule, schedule), num_xcd, cus_per_xcd))
+
+
+def dash_deterministic_resolve(B, H, Hkv, N, d, mask, deterministic, lib=None) -> int:
+    """The mode dash_attn_bwd runs for `deterministic` (4 = the faster reproducible mode for
+    the shape); a negative value is an error status."""
+    return int((lib or load()).dash_deterministic_resolve(B, H, Hkv, N, d, MASKS.get(mask, mask), int(deterministic)))
 
 
 def dash_schedule_table(B, H, Hkv, N, mask, schedule, num_xcd, cus_per_xcd):

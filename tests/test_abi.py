@@ -120,7 +120,7 @@ def _call(**kw):
     (dict(schedule=5), dash.DASH_ERR_INVALID_ARG),
     (dict(mask=1, schedule=2), dash.DASH_ERR_UNSUPPORTED),
     (dict(mask=0, schedule=3), dash.DASH_ERR_UNSUPPORTED),
-    (dict(det=4), dash.DASH_ERR_INVALID_ARG),
+    (dict(det=5), dash.DASH_ERR_INVALID_ARG),
     (dict(det=-1), dash.DASH_ERR_INVALID_ARG),
     (dict(scale=0.0), dash.DASH_ERR_INVALID_ARG),
     (dict(scale=float("inf")), dash.DASH_ERR_INVALID_ARG),

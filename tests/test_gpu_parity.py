@@ -159,3 +159,22 @@ def test_auto_runs_the_resolved_schedule(shape, causal):
     auto, _ = run(case, dev, "auto", 1)
     ref, _ = run(case, dev, names[resolved], 1)
     assert [bf16_bytes(t) for t in auto] == [bf16_bytes(t) for t in ref], names[resolved]
+
+
+@pytest.mark.parametrize("shape,causal", [((1, 4, 1, 1024, 128), True), ((1, 4, 4, 1024, 128), False),
+                                          ((1, 8, 2, 1024, 64), True), ((1, 4, 2, 1024, 64), False)],
+                         ids=["gqa4-d128", "mha-d128", "gqa4-d64", "gqa2-d64"])
+def test_deterministic_auto_runs_the_resolved_mode(shape, causal):
+    """deterministic = 4 runs exactly the mode dash_deterministic_resolve names (same bits),
+    and meets the oracle tolerance."""
+    from scheduling_fa_attn_amd import dash
+    B, H, Hkv, N, d = shape
+    case = make_case(B, H, Hkv, N, d, causal, seed=43)
+    dev = to_device(case)
+    mode = dash.dash_deterministic_resolve(B, H, Hkv, N, d, "causal" if causal else "full", 4)
+    assert mode in (1, 2)
+    auto, _ = run(case, dev, "auto", 4)
+    ref, _ = run(case, dev, "auto", mode)
+    assert [bf16_bytes(t) for t in auto] == [bf16_bytes(t) for t in ref], mode
+    errs = rel_errs(auto, oracle_grads(case))
+    assert max(errs) <= TOL, errs
