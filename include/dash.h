@@ -41,7 +41,8 @@
  * - Kernel-side errors (a bounded wait that timed out, a workgroup on an unexpected
  *   XCD slot) are written to an error word inside the call's workspace, which the call
  *   itself clears in stream order before its kernels run: an error never leaks into a
- *   later call. dash_last_kernel_error(stream) reads it.
+ *   later call. The call's last kernel copies the word into a status slot of the
+ *   stream, which dash_last_kernel_error(stream) reads.
  */
 #ifndef DASH_H
 #define DASH_H
@@ -158,10 +159,10 @@ size_t dash_attn_bwd_varlen_workspace_size(int B, int H, int Hkv, int N, int d);
  *   registers (deterministic, no cross-CU reduction). The schedule sets the tile
  *   order of the dK/dV pass.
  * deterministic = 4: the bitwise-reproducible mode measured faster on MI355X for the
- *   shape, 1 or 2 (dash_deterministic_resolve names it): the ordered reduction with one
- *   query head per KV head, the two-pass variant for grouped-query attention (two or more
- *   query heads per KV head at d = 128, four or more at d = 64), where the ordered
- *   reduction has fewer lanes and a larger hot set per XCD. The workspace is the same.
+ *   shape, 1 or 2 (dash_deterministic_resolve names it): the two-pass variant for
+ *   grouped-query attention with 8 or more query heads per KV head, or 4 or more with the
+ *   causal mask at d = 128 and N >= 4096 (where the ordered reduction has few lanes and a
+ *   large hot set per XCD); the ordered reduction otherwise. The workspace is the same.
  * deterministic = 3: per-tile partials, the other deterministic alternative of section
  *   5 (FlashAttention-2 style): every dQ contribution of every KV tile is written to its
  *   own fp32 slot, with no waits, and a separate kernel adds each query step's slots in
@@ -225,13 +226,14 @@ int dash_attn_bwd_noalloc(const void* q, const void* k, const void* v, const voi
  * if the launch fails. */
 int dash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Hkv, int N, int d, float softmax_scale, int mask, void* stream);
-/* Kernel-side status of the last backward call (dash_attn_bwd, _timed or _varlen)
- * enqueued on `stream` (a hipStream_t; 0 = the null stream) on the current device:
- * synchronizes that stream only, then returns the error word in that call's workspace
- * (DASH_OK, DASH_ERR_TIMEOUT or DASH_ERR_PLACEMENT). That workspace must still be
- * allocated and must not have been handed to another call since. DASH_OK when no
- * backward call was enqueued on the stream; DASH_ERR_HIP if the copy or the
- * synchronization fails. Reading does not clear the word (the next call clears it). */
+/* Kernel-side status of the last backward call (dash_attn_bwd and its variants) that
+ * ran kernels on `stream` (a hipStream_t; 0 = the null stream) on the current device:
+ * DASH_OK, DASH_ERR_TIMEOUT or DASH_ERR_PLACEMENT. Synchronizes that stream only. Each
+ * call's last kernel copies the call's error word into a library-owned status slot of
+ * its stream (4096 slots per device, handed out per stream in order and reused round
+ * robin beyond that), so the status survives the call's workspace. DASH_OK when no
+ * backward call ran on the stream; DASH_ERR_HIP if the copy or the synchronization
+ * fails. Reading does not clear the status (the stream's next call overwrites it). */
 int dash_last_kernel_error(void* stream);
 
 /* Human-readable name of a status code (static storage; never null). */

@@ -74,7 +74,8 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
 template <int D>
 __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
                                                              int N, int row_stride, float scale,
-                                                             const int* __restrict__ seqlens, int H) {
+                                                             const int* __restrict__ seqlens, int H, StatusCopy sc) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *sc.status_out = *sc.err_in;
   constexpr int DB = D / 32;
   constexpr int LROW = D + 8;  // bf16 per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) bf16 tile[32 * LROW];
@@ -122,7 +123,8 @@ __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __rest
 template <int D>
 __global__ void __launch_bounds__(256) dq_consolidate_kernel(const float* __restrict__ parts, bf16* __restrict__ dq,
                                                              int N, int row_stride, int tile, int causal,
-                                                             float scale) {
+                                                             float scale, StatusCopy sc) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *sc.status_out = *sc.err_in;
   constexpr int DB = D / 32;
   constexpr int LROW = D + 8;
   constexpr int SLOT4 = 2 * DB * kDqBlock / 4;  // float4 per slot
@@ -168,7 +170,8 @@ __global__ void __launch_bounds__(256) dq_consolidate_kernel(const float* __rest
 // row_stride rows per head, of which the first N are output.
 __global__ void __launch_bounds__(256) dq_cast_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
                                                       int64_t quads, int N, int row_stride, int d, float scale,
-                                                      const int* __restrict__ seqlens, int H) {
+                                                      const int* __restrict__ seqlens, int H, StatusCopy sc) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *sc.status_out = *sc.err_in;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t nthreads = static_cast<int64_t>(gridDim.x) * blockDim.x;
   const int qpr = d / 4;  // float4 per row
@@ -203,26 +206,26 @@ hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t 
 }
 
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                          hipStream_t stream, const int* seqlens, int H) {
+                          StatusCopy sc, hipStream_t stream, const int* seqlens, int H) {
   const int64_t quads = heads * N * (d / 4);
   int64_t grid = (quads + 255) / 256;
   grid = grid < 1 ? 1 : (grid > 8192 ? 8192 : grid);
   hipLaunchKernelGGL(dq_cast_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
-                     reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale, seqlens, H);
+                     reinterpret_cast<bf16*>(dq), quads, N, row_stride, d, scale, seqlens, H, sc);
   return hipGetLastError();
 }
 
 hipError_t launch_dq_consolidate(const float* parts, void* dq, int64_t heads, int N, int row_stride, int tile, int d,
-                                 int causal, float scale, hipStream_t stream) {
+                                 int causal, float scale, StatusCopy sc, hipStream_t stream) {
   const int64_t grid = heads * (row_stride / 32);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (d == 64) {
     hipLaunchKernelGGL(dq_consolidate_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, parts,
-                       reinterpret_cast<bf16*>(dq), N, row_stride, tile, causal, scale);
+                       reinterpret_cast<bf16*>(dq), N, row_stride, tile, causal, scale, sc);
   } else if (d == 128) {
     hipLaunchKernelGGL(dq_consolidate_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, parts,
-                       reinterpret_cast<bf16*>(dq), N, row_stride, tile, causal, scale);
+                       reinterpret_cast<bf16*>(dq), N, row_stride, tile, causal, scale, sc);
   } else {
     return hipErrorInvalidValue;
   }
@@ -230,16 +233,16 @@ hipError_t launch_dq_consolidate(const float* parts, void* dq, int64_t heads, in
 }
 
 hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                                 hipStream_t stream, const int* seqlens, int H) {
+                                 StatusCopy sc, hipStream_t stream, const int* seqlens, int H) {
   const int64_t grid = heads * (row_stride / 32);
   if (grid == 0) return hipSuccess;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
   if (d == 64) {
     hipLaunchKernelGGL(dq_cast_blocks_kernel<64>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
-                       reinterpret_cast<bf16*>(dq), N, row_stride, scale, seqlens, H);
+                       reinterpret_cast<bf16*>(dq), N, row_stride, scale, seqlens, H, sc);
   } else if (d == 128) {
     hipLaunchKernelGGL(dq_cast_blocks_kernel<128>, dim3(static_cast<unsigned>(grid)), dim3(256), 0, stream, acc,
-                       reinterpret_cast<bf16*>(dq), N, row_stride, scale, seqlens, H);
+                       reinterpret_cast<bf16*>(dq), N, row_stride, scale, seqlens, H, sc);
   } else {
     return hipErrorInvalidValue;
   }

@@ -31,9 +31,9 @@
 // Step of 64 Q rows (a pair-local handoff X and a workgroup barrier Y):
 //   A: S MFMAs of Q block 0, then of block 1 with block 0's softmax and the next step's
 //      Q-tile copies between them; block 1's softmax; P -> LDS      | flag X set |
-//      dV MFMAs with the previous step's dQ block (8 MFMAs) between those of the first
-//      half, its stores (acknowledged under the second half), its turn passed on; this
-//      step's turn polled and running sum loaded
+//      dV MFMAs with the previous step's dQ MFMAs between those of the first half (one
+//      per dV MFMA at d = 128, two at d = 64), their stores (acknowledged under the second
+//      half), the turn passed on; this step's turn polled and running sum loaded
 //                                                                   | barrier Y |
 //   B: dP MFMAs with the next step's dO-tile copies and the previous step's dQ block;
 //      its stores                                                   | flag X awaited |
@@ -44,10 +44,12 @@
 // step whose P is in the pair's exchange area; A writes it after its P stores have
 // completed, B polls it), so that pairs do not wait for each other mid-step; Y is the
 // workgroup barrier that publishes every pair's dS^T and the next step's tiles.
-// A waves copy the next step's Q tile (after their S MFMAs), B waves its dO tile (during
-// their dP MFMAs). The compiler does not see these copies (inline assembly), so a wave
-// waits for its running-sum loads before issuing them (the vector-memory counter is in
-// order) and for the copies themselves before the step-end barrier.
+// At d = 128 the A waves copy the next step's Q tile (after their S MFMAs) and the B waves
+// its dO tile (during their dP MFMAs); at d = 64, where the A waves own every dQ block
+// and the B waves have slack before the P handoff, the B waves copy both. The compiler
+// does not see these copies (inline assembly), so a wave waits for its running-sum loads
+// before issuing them (the vector-memory counter is in order) and for the copies
+// themselves before the step-end barrier.
 // Variable-length batches: every row limit (copy clamps, the zeroed K rows of a ragged
 // KV tile, the dK/dV stores) is the length of the item's or step's batch; N stays the
 // row stride.
@@ -221,7 +223,9 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       // columns adds nothing to dQ; their dK/dV rows are never stored.
       const int r0 = nb - kv0;
       LDS_AS floatx4* z = reinterpret_cast<LDS_AS floatx4*>(sK + r0 * ST);
-      for (int x = tid; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
+      int x0 = tid;
+      asm volatile("" : "+v"(x0));  // (computed here, not kept live from the kernel's start)
+      for (int x = x0; x < (BC - r0) * ST / 16; x += C::NT) z[x] = floatx4{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
     }
     bf16x8 kv[DK];  // A: K rows (B operand of S), B: V rows (B operand of dP)
@@ -444,7 +448,10 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       const int q0_n = rec_nxt.y;
       const int64_t bh_n = rec_nxt.x;
       const int nb_n = p.seqlens ? seqlens[rec_nxt.x / H] : N;  // rows of the next step's batch
-      auto copy_op = [&](int o, int lane_op) __attribute__((always_inline)) {
+      // At d = 64 the B waves copy both tiles (A's running sums then need not land
+      // before its S phase's copies, as the copies are invisible to the compiler).
+      constexpr bool kBCopiesAll = !C::kAllWavesDq;
+      auto copy_tile = [&](int o, int lane_op, bool qtile) __attribute__((always_inline)) {
         if (o < kPW) {
           const int blk = pr + 4 * o;
           if (o + 1 < kPW || blk < kQNI) {
@@ -455,14 +462,15 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
             c = c < TileGeom<D>::CPR ? c : 0;
             int row = q0_n + r;
             row = row < nb_n - 1 ? row : nb_n - 1;
-            dma16((roleA ? p.q : p.dO) + bh_n * N * D, static_cast<unsigned>(row * (2 * D) + 16 * c),
-                  smem + (roleA ? C::OFF_Q : C::OFF_DO) + (buf ^ 1) * C::QT + blk * 1024);
+            dma16((qtile ? p.q : p.dO) + bh_n * N * D, static_cast<unsigned>(row * (2 * D) + 16 * c),
+                  smem + (qtile ? C::OFF_Q : C::OFF_DO) + (buf ^ 1) * C::QT + blk * 1024);
           }
         } else if (pr == 0) {
-          dma4((roleA ? p.nlse2 : p.neg_delta) + bh_n * p.row_stride + q0_n, row_lane,
-               smem + (roleA ? C::OFF_NL : C::OFF_DL) + (buf ^ 1) * 256);
+          dma4((qtile ? p.nlse2 : p.neg_delta) + bh_n * p.row_stride + q0_n, row_lane,
+               smem + (qtile ? C::OFF_NL : C::OFF_DL) + (buf ^ 1) * 256);
         }
       };
+      auto copy_op = [&](int o, int lane_op) __attribute__((always_inline)) { copy_tile(o, lane_op, roleA); };
       Pending pd_n;
       int sem_now = 0;
       if constexpr (roleA) {
@@ -505,6 +513,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
           if (i + kR - 1 < 2 * DK) aq[(i + kR - 1) % kR] = lds_ld16(sQ, sdp_off((i + kR - 1) / DK, (i + kR - 1) % DK));
           if (i == 0) load_nl(0);
           if (i == DK / 2) load_nl(1);
+          SLOT();  // the operand reads ahead stay ahead of this slot's MFMA
           floatx16& S = i < DK ? S0 : S1;
           if (i % DK == 0)
             mfma32_vab_zero(S, aq[i % kR], kv[0]);
@@ -519,12 +528,14 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
             for (int r = 16 * (i - DK) / DK; r < 16 * (i - DK + 1) / DK; r += 2) softmax2(0, r, S0);
             // The running sums loaded at the end of the last step have landed before the
             // first copy is issued (the copies are invisible to the compiler's counters).
-            if (i == DK) {
-              asm volatile("" : "+v"(ld));
-              lane_op = opaque_lane();
-            }
+            if constexpr (!kBCopiesAll) {
+              if (i == DK) {
+                asm volatile("" : "+v"(ld));
+                lane_op = opaque_lane();
+              }
 #pragma unroll
-            for (int o = (i - DK) * kCopyOps / DK; o < (i - DK + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
+              for (int o = (i - DK) * kCopyOps / DK; o < (i - DK + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
+            }
           }
           SLOT();
         }
@@ -562,30 +573,37 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
         PROF_MARK(kProfDq);
         // The dQ MFMAs run in the first half, so that their stores are acknowledged
         // under the second half's dV MFMAs.
-        bf16x8 bo[kR], aqd[kR];
+        // QPI dQ MFMAs per dV MFMA over the first NQI dV MFMAs (d = 128: one each over
+        // the first half; d = 64: two each over the first half), operands one
+        // iteration ahead.
+        constexpr int QPI = 2 * KK > 2 * NIT ? 2 : 1;
+        constexpr int NQI = KK / QPI;
+        bf16x8 bo[kR], aqd[2][QPI];
 #pragma unroll
-        for (int i = 0; i < kR - 1; ++i) {
-          bo[i] = bt_load(sdO, i);
-          if (HAS_DQ) aqd[i] = dq_opnd(sdSprev, i);
-        }
+        for (int i = 0; i < kR - 1; ++i) bo[i] = bt_load(sdO, i);
+#pragma unroll
+        for (int u = 0; u < QPI; ++u)
+          if (HAS_DQ) aqd[0][u] = dq_opnd(sdSprev, u);
         SLOT();
 #pragma unroll
         for (int jj = 0; jj < 2 * NIT; ++jj) {
           if (jj + kR - 1 < 2 * NIT) bo[(jj + kR - 1) % kR] = bt_load(sdO, jj + kR - 1);
-          if (HAS_DQ && jj + kR - 1 < KK) aqd[(jj + kR - 1) % kR] = dq_opnd(sdSprev, jj + kR - 1);
+          if (HAS_DQ && jj + 1 < NQI) {
+#pragma unroll
+            for (int u = 0; u < QPI; ++u) aqd[(jj + 1) & 1][u] = dq_opnd(sdSprev, QPI * (jj + 1) + u);
+          }
+          SLOT();
           const int qb = jj / NIT, itr = jj % NIT;
           mfma32_acc(acc[itr % DB], as_bf16x8(P[qb][itr / DB]), bo[jj % kR]);
-          if (HAS_DQ && jj < KK) dq_mma(ld, jj, aqd[jj % kR], kT[jj]);
-          if (jj == KK) {
+          if (HAS_DQ && jj < NQI) {
+#pragma unroll
+            for (int u = 0; u < QPI; ++u) dq_mma(ld, QPI * jj + u, aqd[jj & 1][u], kT[QPI * jj + u]);
+          }
+          if (jj == NQI) {
             mfma_result_wait(ld);
             reduce_store(pd, ld);
           }
           SLOT();
-        }
-        if constexpr (2 * NIT <= KK) {
-          // (d = 64: the dQ MFMAs span the whole phase.)
-          mfma_result_wait(ld);
-          reduce_store(pd, ld);
         }
         PROF_MARK(kProfDv0);
         PROF_MARK(kProfLoads);
@@ -643,11 +661,15 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
           const int kk = i - (2 * DK - KK);
           if (HAS_DQ && kk + kR - 1 >= 0 && kk + kR - 1 < KK)
             aqd[(kk + kR - 1) % kR] = dq_opnd(sdSprev, kk + kR - 1);
+          SLOT();
           mfma32_vab(i < DK ? dP0 : dP1, ad[i % kR], kv[i % DK]);
           if (HAS_DQ && kk >= 0) dq_mma(ld, kk, aqd[kk % kR], kT[kk]);
           if (i < DK) {
 #pragma unroll
             for (int o = i * kCopyOps / DK; o < (i + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
+          } else if (kBCopiesAll) {
+#pragma unroll
+            for (int o = (i - DK) * kCopyOps / DK; o < (i - DK + 1) * kCopyOps / DK; ++o) copy_tile(o, lane_op, true);
           }
           SLOT();
         }
@@ -707,6 +729,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #pragma unroll
         for (int jj = 0; jj < 2 * NIT; ++jj) {
           if (jj + kR - 1 < 2 * NIT) bq[(jj + kR - 1) % kR] = bt_load(sQ, jj + kR - 1);
+          SLOT();
           const int qb = jj / NIT, itr = jj % NIT;
           mfma32_acc(acc[itr % DB], as_bf16x8(dS[qb][itr / DB]), bq[jj % kR]);
           if (jj < NIT) {

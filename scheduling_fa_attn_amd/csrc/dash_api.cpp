@@ -38,6 +38,12 @@ constexpr size_t kStagingBytes = size_t(64) << 20;
 constexpr size_t kScratchBytes = size_t(64) << 20;
 constexpr size_t kScratchTableBytes = size_t(8) << 20;
 __device__ __attribute__((aligned(256))) char scratch[kScratchBytes];
+// The first kStatusSlots ints of the array (inside its table part) are the per-stream
+// status slots of dash_last_kernel_error: each backward call's last kernel copies the
+// call's error word into its stream's slot. Tables start at kScratchTablesStart.
+constexpr int kStatusSlots = 4096;
+constexpr size_t kScratchTablesStart = size_t(64) << 10;
+static_assert(kStatusSlots * sizeof(int) <= kScratchTablesStart, "status slots fit before the tables");
 
 int tile_for(int N) { return N < 512 ? 64 : 128; }
 
@@ -180,19 +186,23 @@ int model_schedule(int B, int H, int Hkv, int N, int d, int mask, int num_xcd, i
 
 // deterministic = 4 (DASH_DET_AUTO): the bitwise-reproducible mode measured faster on
 // MI355X for the shape, between the ordered reduction (1) and the two-pass variant (2),
-// which take the same workspace. With grouped-query attention the ordered reduction has
-// B * Hkv * n lanes (half that for symmetric shift) for B * H * n Q tiles, and a KV item
-// visits every query head of its group, so the group's Q, dO and dQ tiles are all hot in
-// one XCD's L2 at once; the two-pass variant's dQ pass is parallel over query heads.
-// Measured (whole call, N = 2048 .. 8192, both masks): one query head per KV head: the
-// ordered reduction 4 - 11 % faster everywhere; two per KV head: two-pass faster at
-// d = 128 (up to 4 %), slower at d = 64 (4 %); four or eight: two-pass faster in all but
-// one shape (2 % slower there). 64-row tiles (N < 512) keep the ordered reduction.
-int resolve_deterministic(int H, int Hkv, int N, int d, int deterministic) {
+// which take the same workspace. With grouped-query attention of G query heads per KV
+// head the ordered reduction has B * Hkv * n lanes (half that for symmetric shift), a
+// KV item runs G times the tasks, and in the symmetric shift's phase-2 triangles the
+// group's Q, dO and dQ tiles are hot in one XCD's L2 at once; the two-pass variant's dQ
+// pass is parallel over query heads. Measured (whole call; N = 2048 .. 8192, d = 64 and
+// 128, both masks; heads outermost in the full mask's rows and phase 1): the ordered
+// reduction is faster for G <= 2 everywhere (1 - 11 %) and for G = 4 except the causal
+// mask at d = 128 and N = 8192 (two-pass 5 % faster there, 6 % slower at N = 2048); the
+// two-pass variant is faster for G = 8 everywhere (0.3 - 9 %). 64-row tiles (N < 512)
+// keep the ordered reduction.
+int resolve_deterministic(int H, int Hkv, int N, int d, int mask, int deterministic) {
   if (deterministic != 4) return deterministic;
   const int G = H / Hkv;
-  if (tile_for(N) == 64 || G == 1) return 1;
-  return (d == 128 || G >= 4) ? 2 : 1;
+  if (tile_for(N) == 64) return 1;
+  if (G >= 8) return 2;
+  if (G >= 4 && mask == DASH_MASK_CAUSAL && d == 128 && N >= 4096) return 2;
+  return 1;
 }
 
 int check_sizes(int B, int H, int Hkv, int N, int d, int mask, int schedule) {
@@ -241,9 +251,11 @@ struct DeviceState {
   int num_xcd = 1;
   int cus_per_xcd = 1;
   long long ticks_per_second = 100000000LL;
-  // Error word of the last backward call enqueued on each stream (in that call's
-  // workspace), for dash_last_kernel_error; host bookkeeping only.
-  std::map<void*, const int*> last_err;
+  // Status slot (index into the scratch array's first ints) of each stream that has run
+  // a backward call; slots are handed out in order and reused round robin past
+  // kStatusSlots streams.
+  std::map<void*, int> stream_slot;
+  int next_slot = 0;
   int* err_host = nullptr;  // pinned word that dash_last_kernel_error copies into (g_err_mu)
   // This device's copy of `scratch` (hipGetSymbolAddress at set-up), and the schedule
   // tables dash_attn_bwd_noalloc has copied into its table part: key -> (offset, image).
@@ -298,8 +310,8 @@ int init_device(int dev, DeviceState* st) {
   void* scr = nullptr;
   if (hipGetSymbolAddress(&scr, HIP_SYMBOL(scratch)) != hipSuccess || scr == nullptr) return DASH_ERR_HIP;
   st->scratch = static_cast<char*>(scr);
-  if (size_t(st->cus) * sizeof(int) > kScratchTableBytes) return DASH_ERR_UNSUPPORTED;
-  int* probe = reinterpret_cast<int*>(st->scratch);
+  if (kScratchTablesStart + size_t(st->cus) * sizeof(int) > kScratchTableBytes) return DASH_ERR_UNSUPPORTED;
+  int* probe = reinterpret_cast<int*>(st->scratch + kScratchTablesStart);
   hipError_t e = dash::launch_topology_probe(probe, st->cus, nullptr);
   std::vector<int> ids(st->cus, -1);
   if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -622,12 +634,12 @@ int get_table_scratch(DeviceState* st, int B, int H, int Hkv, int N, bool causal
   TableImage img;
   make_image(t, H, tile, nullptr, &img);
   const size_t size = align256(img.bytes.size());
-  if (size > kScratchTableBytes) return DASH_ERR_WORKSPACE;
-  if (st->scratch_tables_used + size > kScratchTableBytes) {
+  if (size > kScratchTableBytes - kScratchTablesStart) return DASH_ERR_WORKSPACE;
+  if (st->scratch_tables_used + size > kScratchTableBytes - kScratchTablesStart) {
     st->scratch_tables.clear();
     st->scratch_tables_used = 0;
   }
-  const size_t off = st->scratch_tables_used;
+  const size_t off = kScratchTablesStart + st->scratch_tables_used;
   if (hipMemcpyAsync(st->scratch + off, img.bytes.data(), img.bytes.size(), hipMemcpyHostToDevice, stream) !=
       hipSuccess)
     return DASH_ERR_HIP;
@@ -648,7 +660,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   int s = check_sizes(B, H, Hkv, N, d, mask, schedule);
   if (s != DASH_OK) return s;
   if (deterministic < 0 || deterministic > 4) return DASH_ERR_INVALID_ARG;
-  deterministic = resolve_deterministic(H, Hkv, N, d, deterministic);
+  deterministic = resolve_deterministic(H, Hkv, N, d, mask, deterministic);
   if (deterministic == 3 && seqlens) return DASH_ERR_UNSUPPORTED;  // per-tile partials: one length
   // Variable-length batches: lengths in [1, N].
   std::vector<int> lens, scheds;
@@ -746,6 +758,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   int* sem = reinterpret_cast<int*>(ws + L.sem);
   int* ctr = reinterpret_cast<int*>(ws + L.ctr);
   int* err = reinterpret_cast<int*>(ws + L.err);
+  dash::StatusCopy status;
+  status.err_in = err;
 
   dash::PreParams pp;
   pp.o = static_cast<const __bf16*>(o);
@@ -803,7 +817,12 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     std::lock_guard<std::mutex> lock(g_mu);
     // ticks = ticks/s * us / 1e6, without overflow for any accepted timeout
     bp.timeout_ticks = st->ticks_per_second / 1000 * g_wait_timeout_us / 1000;
-    st->last_err[stream_ptr] = err;
+    auto slot = st->stream_slot.find(stream_ptr);
+    if (slot == st->stream_slot.end()) {
+      slot = st->stream_slot.emplace(stream_ptr, st->next_slot).first;
+      st->next_slot = (st->next_slot + 1) % kStatusSlots;
+    }
+    status.status_out = reinterpret_cast<int*>(st->scratch) + slot->second;
   }
   bp.prof = g_prof;
   bp.replay = nullptr;
@@ -858,14 +877,17 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
     dp.causal = causal ? 1 : 0;
     dp.scale = scale;
     dp.scale_log2 = scale * 1.4426950408889634f;
+    dp.err_in = status.err_in;
+    dp.status_out = status.status_out;
     ec = dash::launch_dq_pass(dp, d, stream);
   } else if (deterministic == 3) {
     ec = dash::launch_dq_consolidate(dqacc, dq, int64_t(B) * H, N, L.row_stride, tab->tile, d, causal ? 1 : 0, scale,
-                                     stream);
+                                     status, stream);
   } else if (deterministic == 1) {
-    ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream, tab->seqlens, H);
+    ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, status, stream,
+                                     tab->seqlens, H);
   } else {
-    ec = dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, stream, tab->seqlens, H);
+    ec = dash::launch_dq_cast(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, status, stream, tab->seqlens, H);
   }
   if (ec != hipSuccess) return DASH_ERR_HIP;
   return DASH_OK;
@@ -964,9 +986,9 @@ int dash_last_kernel_error(void* stream) {
     if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
     auto found = g_devices.find(dev);
     if (found == g_devices.end() || !found->second.ready) return DASH_OK;
-    auto w = found->second.last_err.find(stream);
-    if (w == found->second.last_err.end()) return DASH_OK;
-    word = w->second;
+    auto w = found->second.stream_slot.find(stream);
+    if (w == found->second.stream_slot.end()) return DASH_OK;
+    word = reinterpret_cast<const int*>(found->second.scratch) + w->second;
     if (found->second.err_host == nullptr &&
         hipHostMalloc(reinterpret_cast<void**>(&found->second.err_host), sizeof(int), hipHostMallocDefault) !=
             hipSuccess)
@@ -1063,7 +1085,7 @@ int dash_deterministic_resolve(int B, int H, int Hkv, int N, int d, int mask, in
   const int s = check_sizes(B, H, Hkv, N, d, mask, resolve_schedule(DASH_SCHED_AUTO, N, mask));
   if (s != DASH_OK) return s;
   if (deterministic < 0 || deterministic > 4) return DASH_ERR_INVALID_ARG;
-  return resolve_deterministic(H, Hkv, N, d, deterministic);
+  return resolve_deterministic(H, Hkv, N, d, mask, deterministic);
 }
 
 int dash_schedule_makespan(int B, int H, int Hkv, int N, int mask, int schedule, int num_xcd, int cus_per_xcd,

@@ -118,7 +118,10 @@ __device__ __forceinline__ int load_flag_sys(const int* p) {
 }
 
 __device__ __forceinline__ void raise_error(int* err, int code) {
+  // The operands are made here (an empty asm hides them from the compiler), so that it
+  // does not keep them live from the kernel's start for this rarely taken path.
   int expected = 0;
+  asm volatile("" : "+v"(expected), "+v"(code));
   __hip_atomic_compare_exchange_strong(err, &expected, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_SYSTEM);
 }

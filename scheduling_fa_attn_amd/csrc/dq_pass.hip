@@ -30,6 +30,7 @@ namespace dash {
 template <int D>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 dq_pass_kernel(DqParams p) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *p.status_out = *p.err_in;
   constexpr int NW = 4, BQ = 32 * NW, BK = 64, ST = TileGeom<D>::STRIDE, KT = BK * ST, DK = D / 16, DB = D / 32;
   extern __shared__ __attribute__((aligned(1024))) char smem_raw[];
   LDS_AS char* smem = (LDS_AS char*)smem_raw;

@@ -97,6 +97,8 @@ struct DqParams {
   int causal;
   float scale;              // softmax scale s
   float scale_log2;         // s * log2(e)
+  const int* err_in;        // the call's error word, final once the main kernel is done
+  int* status_out;          // the stream's status slot: receives *err_in (block 0)
 };
 
 // fp32 dQ accumulator layouts (rows per (b, h) padded to row_stride).
@@ -212,15 +214,22 @@ inline hipError_t launch_main(const BwdParams& prm, int d, int nw, int grid, hip
   return hipErrorInvalidValue;
 }
 hipError_t launch_preprocess(const PreParams& prm, int d, int grid, hipStream_t stream);
+// The last kernel of a backward call copies the call's error word (final by then: the
+// main kernel precedes it on the stream) into the stream's status slot, which
+// dash_last_kernel_error reads.
+struct StatusCopy {
+  const int* err_in;
+  int* status_out;
+};
 // dQ = bf16(scale * dqacc) for rows < N, from the ordered variant's block layout.
 hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                                 hipStream_t stream, const int* seqlens = nullptr, int H = 1);
+                                 StatusCopy sc, hipStream_t stream, const int* seqlens = nullptr, int H = 1);
 // dQ = bf16(scale * dqacc) for rows < N, from the atomic variant's row-major layout.
 hipError_t launch_dq_cast(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
-                          hipStream_t stream, const int* seqlens = nullptr, int H = 1);
+                          StatusCopy sc, hipStream_t stream, const int* seqlens = nullptr, int H = 1);
 // dQ = bf16(scale * sum of the per-tile partials), rank order, rows < N (deterministic = 3).
 hipError_t launch_dq_consolidate(const float* parts, void* dq, int64_t heads, int N, int row_stride, int tile, int d,
-                                 int causal, float scale, hipStream_t stream);
+                                 int causal, float scale, StatusCopy sc, hipStream_t stream);
 hipError_t launch_topology_probe(int* out, int grid, hipStream_t stream);
 hipError_t launch_fwd(const FwdParams& prm, int d, hipStream_t stream);
 hipError_t launch_dq_pass(const DqParams& prm, int d, hipStream_t stream);

@@ -161,9 +161,10 @@ def test_auto_runs_the_resolved_schedule(shape, causal):
     assert [bf16_bytes(t) for t in auto] == [bf16_bytes(t) for t in ref], names[resolved]
 
 
-@pytest.mark.parametrize("shape,causal", [((1, 4, 1, 1024, 128), True), ((1, 4, 4, 1024, 128), False),
-                                          ((1, 8, 2, 1024, 64), True), ((1, 4, 2, 1024, 64), False)],
-                         ids=["gqa4-d128", "mha-d128", "gqa4-d64", "gqa2-d64"])
+@pytest.mark.parametrize("shape,causal", [((1, 8, 1, 1024, 128), True), ((1, 4, 1, 4096, 128), True),
+                                          ((1, 4, 4, 1024, 128), False), ((1, 8, 2, 1024, 64), True),
+                                          ((1, 8, 1, 1024, 64), False)],
+                         ids=["gqa8-d128", "gqa4-causal-d128-N4096", "mha-d128", "gqa4-d64", "gqa8-d64"])
 def test_deterministic_auto_runs_the_resolved_mode(shape, causal):
     """deterministic = 4 runs exactly the mode dash_deterministic_resolve names (same bits),
     and meets the oracle tolerance."""

@@ -143,7 +143,7 @@ def test_varlen_argument_errors():
 
     assert call((0, 512)) == dash.DASH_ERR_INVALID_ARG
     assert call((513, 512)) == dash.DASH_ERR_INVALID_ARG
-    assert call((512, 512), det=4) == dash.DASH_ERR_INVALID_ARG
+    assert call((512, 512), det=5) == dash.DASH_ERR_INVALID_ARG
     assert call((512, 512), det=3) == dash.DASH_ERR_UNSUPPORTED  # per-tile partials: one length only
     assert call((512, 384), sched="sym_shift") == dash.DASH_ERR_UNSUPPORTED  # 3 tiles
 

@@ -289,25 +289,25 @@ def test_auto_picks_measured_fastest_on_timed_shapes(shape, fastest):
 # 1) and the two-pass variant (2) by query heads per KV head G: (B, H, N, d, mask) ->
 # {G: (ordered, two-pass)}.
 MODES_MEASURED = {
-    (1, 32, 8192, 128, "causal"): {1: (802.7, 767.5), 2: (760.2, 787.6), 4: (730.8, 753.4), 8: (471.3, 502.2)},
-    (1, 32, 8192, 128, "full"): {1: (853.2, 812.8), 2: (816.8, 813.5), 4: (733.8, 773.7), 8: (476.6, 516.0)},
-    (2, 32, 4096, 64, "causal"): {1: (671.3, 601.8), 2: (639.7, 616.9), 4: (605.2, 621.9), 8: (378.1, 409.1)},
-    (4, 16, 2048, 128, "causal"): {1: (644.8, 600.6), 2: (619.4, 629.9), 4: (486.6, 474.8), 8: (265.9, 296.7)},
-    (2, 16, 4096, 128, "full"): {1: (821.3, 788.7), 2: (762.0, 793.0), 4: (740.7, 758.7), 8: (492.1, 506.5)},
+    (1, 32, 8192, 128, "causal"): {1: (842.4, 785.8), 2: (818.9, 807.9), 4: (762.5, 800.4), 8: (477.5, 509.3)},
+    (1, 32, 8192, 128, "full"): {1: (895.4, 832.6), 2: (899.8, 836.9), 4: (897.5, 838.0), 8: (513.1, 525.6)},
+    (2, 32, 4096, 64, "causal"): {1: (704.8, 615.0), 2: (694.7, 633.5), 4: (678.3, 630.5), 8: (394.9, 412.9)},
+    (4, 16, 2048, 128, "causal"): {1: (667.3, 618.9), 2: (667.3, 650.7), 4: (509.2, 479.5), 8: (274.6, 299.4)},
+    (2, 16, 4096, 128, "full"): {1: (859.5, 807.6), 2: (882.9, 815.8), 4: (899.6, 819.4), 8: (516.5, 518.2)},
 }
 
 
 @pytest.mark.parametrize("shape", list(MODES_MEASURED), ids=["B{}H{}N{}d{}-{}".format(*k) for k in MODES_MEASURED])
 def test_deterministic_auto_within_5_percent_of_the_faster_mode(shape):
     """deterministic = 4 resolves to the ordered reduction or the two-pass variant; on every
-    measured shape the pick is within 5 % of the faster of the two (and the ordered
+    measured shape the pick is the faster of the two, or within 1 % of it (and the ordered
     reduction whenever there is one query head per KV head)."""
     B, H, N, d, mask = shape
     for G, (ordered, two_pass) in MODES_MEASURED[shape].items():
         mode = dash.dash_deterministic_resolve(B, H, H // G, N, d, mask, 4)
         assert mode in (1, 2), mode
         got = ordered if mode == 1 else two_pass
-        assert got >= 0.95 * max(ordered, two_pass), (shape, G, mode)
+        assert got >= 0.99 * max(ordered, two_pass), (shape, G, mode)
         if G == 1:
             assert mode == 1
 
