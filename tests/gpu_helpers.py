@@ -7,9 +7,12 @@ from oracle import attention as oa
 from scheduling_fa_attn_amd import dash, inputs
 
 
-def make_case(B, H, Hkv, N, d, causal, seed):
-    """Seeded bf16 inputs plus O (bf16) and LSE (fp32) from the fp64 oracle forward."""
+def make_case(B, H, Hkv, N, d, causal, seed, q_scale=1.0):
+    """Seeded bf16 inputs plus O (bf16) and LSE (fp32) from the fp64 oracle forward.
+    q_scale multiplies Q before its bf16 rounding (sharp attention: scores far from 0)."""
     bits = inputs.make_qkvdo(B, H, Hkv, N, d, seed)
+    if q_scale != 1.0:
+        bits["q"] = inputs.bf16_round_bits(inputs.bf16_bits_to_f32(bits["q"]) * np.float32(q_scale))
     f64 = {k: inputs.bf16_bits_to_f32(v).astype(np.float64) for k, v in bits.items()}
     scale = 1.0 / math.sqrt(d)
     o, lse = oa.forward(f64["q"], f64["k"], f64["v"], causal, scale)
