@@ -29,8 +29,9 @@
 // l of A); dS goes to LDS transposed, as the dQ contraction needs it anyway.
 //
 // Step of 64 Q rows (a pair-local handoff X and a workgroup barrier Y):
-//   A: S MFMAs of Q block 0, then of block 1 with block 0's softmax and the next step's
-//      Q-tile copies between them; block 1's softmax; P -> LDS      | flag X set |
+//   A: S MFMAs of Q block 0 with the next step's Q-tile copies between them, then of
+//      block 1 with block 0's softmax between them; block 1's softmax; P -> LDS
+//                                                                   | flag X set |
 //      dV MFMAs with the previous step's dQ MFMAs between those of the first half (one
 //      per dV MFMA at d = 128, two at d = 64), their stores (acknowledged under the second
 //      half), the turn passed on; this step's turn polled and running sum loaded
@@ -44,8 +45,9 @@
 // step whose P is in the pair's exchange area; A writes it after its P stores have
 // completed, B polls it), so that pairs do not wait for each other mid-step; Y is the
 // workgroup barrier that publishes every pair's dS^T and the next step's tiles.
-// At d = 128 the A waves copy the next step's Q tile (after their S MFMAs) and the B waves
-// its dO tile (during their dP MFMAs); at d = 64, where the A waves own every dQ block
+// At d = 128 the A waves copy the next step's Q tile (during their first S MFMAs, as early
+// as the step allows: the buffer was last read in the step before) and the B waves its dO
+// tile (during their dP MFMAs); at d = 64, where the A waves own every dQ block
 // and the B waves have slack before the P handoff, the B waves copy both. The compiler
 // does not see these copies (inline assembly), so a wave waits for its running-sum loads
 // before issuing them (the vector-memory counter is in order) and for the copies
@@ -501,8 +503,11 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
           for (int t = 0; t < 4; ++t)
             nl[qb][t] = *reinterpret_cast<const LDS_AS floatx4*>(sNL + (qb * 32 + 8 * t + 4 * hi) * 4);
         };
-        // S of block 0, then S of block 1 with block 0's softmax and the copies between its
-        // MFMAs (two elements per slot), then block 1's softmax.
+        // S of block 0 with the next step's Q-tile copies between its MFMAs (issued as early
+        // as possible: a copy that misses the L2 then still lands before the step ends), S
+        // of block 1 with block 0's softmax between its MFMAs (two elements per slot), then
+        // block 1's softmax. (Copies placed after block 0 split the loop at a branch, and
+        // the compiler then sank block 0's softmax below block 1's MFMAs.)
         int lane_op = 0;
         bf16x8 aq[kR];
 #pragma unroll
@@ -526,15 +531,16 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
           if (i >= DK) {
 #pragma unroll
             for (int r = 16 * (i - DK) / DK; r < 16 * (i - DK + 1) / DK; r += 2) softmax2(0, r, S0);
+          } else {
             // The running sums loaded at the end of the last step have landed before the
             // first copy is issued (the copies are invisible to the compiler's counters).
             if constexpr (!kBCopiesAll) {
-              if (i == DK) {
+              if (i == 0) {
                 asm volatile("" : "+v"(ld));
                 lane_op = opaque_lane();
               }
 #pragma unroll
-              for (int o = (i - DK) * kCopyOps / DK; o < (i - DK + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
+              for (int o = i * kCopyOps / DK; o < (i + 1) * kCopyOps / DK; ++o) copy_op(o, lane_op);
             }
           }
           SLOT();
