@@ -567,14 +567,15 @@ KERNEL_SOURCES = {"bwd_main": ("scheduling_fa_attn_amd/csrc/bwd_main.hip",) + CO
                   "bwd_pair": ("scheduling_fa_attn_amd/csrc/bwd_pair.hip",) + COMMON_SOURCES}
 
 
-def main_kernel_name(N, d, kernel_choice):
-    """The main kernel dash_attn_bwd launches (deterministic = 1, one XCD per chain)."""
+def main_kernel_name(N, d, kernel_choice, causal):
+    """The main kernel dash_attn_bwd launches (deterministic = 1, one XCD per chain); the
+    two-waves kernel writes bf16 dQ itself under the full mask (last template argument)."""
     if N >= 512 and kernel_choice != "one_wave":
-        return f"bwd_pair_kernel<{d}, true, false>"
+        return f"bwd_pair_kernel<{d}, true, false, {'false' if causal else 'true'}>"
     return f"bwd_main_kernel<{d}, {4 if N >= 512 else 2}, true, false, false, false>"
 
 
-def kernel_source_hash(kernel="bwd_pair_kernel<128, true, false>"):
+def kernel_source_hash(kernel="bwd_pair_kernel<128, true, false, true>"):
     import hashlib
 
     h = hashlib.sha256()
@@ -672,7 +673,7 @@ def main():
     fl = flops_bwd(B, H, N, d, causal)
     main_ms = main_res["main_kernel_ms"]
     achieved = fl / (main_ms * 1e-3) / 1e12
-    kernel = main_kernel_name(N, d, args.kernel)
+    kernel = main_kernel_name(N, d, args.kernel, causal)
     result = {
         "metric": METRIC,
         "value": round(main_res["tflops"], 3),

@@ -65,12 +65,22 @@ __global__ void __launch_bounds__(256) preprocess_kernel(PreParams p) {
   }
 }
 
-// dQ = bf16(s * dQacc), for the ordered variant: the accumulator holds the final fp32
-// sums in the block layout described at kDqBlock. One workgroup per 32-row block row
-// of one head reads its D / 32 blocks with 16-byte loads, rounds them, puts them in row
-// order in LDS and writes rows < N in 16-byte chunks. (The last contributor of a tile
-// could write bf16 itself, but its step would then be slower than every other step,
-// and in the shift schedules every step of one CU holds up the steps that wait for it.)
+// The call's error word into the stream's status slot, for calls with no cast kernel
+// (the two-waves kernel writes dQ itself in the ordered variant).
+__global__ void __launch_bounds__(64) status_copy_kernel(StatusCopy sc) {
+  if (threadIdx.x == 0) *sc.status_out = *sc.err_in;
+}
+
+hipError_t launch_status_copy(StatusCopy sc, hipStream_t stream) {
+  hipLaunchKernelGGL(status_copy_kernel, dim3(1), dim3(64), 0, stream, sc);
+  return hipGetLastError();
+}
+
+// dQ = bf16(s * dQacc), for the ordered variant of the one-wave kernel: the accumulator
+// holds the final fp32 sums in the block layout described at kDqBlock. One workgroup per
+// 32-row block row of one head reads its D / 32 blocks with 16-byte loads, rounds them,
+// puts them in row order in LDS and writes rows < N in 16-byte chunks. (The two-waves
+// kernel's last contributors write bf16 dQ themselves, transposed in registers.)
 template <int D>
 __global__ void __launch_bounds__(256) dq_cast_blocks_kernel(const float* __restrict__ acc, bf16* __restrict__ dq,
                                                              int N, int row_stride, float scale,

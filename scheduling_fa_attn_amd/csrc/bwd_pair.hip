@@ -104,12 +104,49 @@ struct PairCfg {
   static_assert(QT % 1024 == 0 && DST % 1024 == 0 && (BC * ST) % 1024 == 0, "1 KiB-aligned tiles");
 };
 
+// The value of lane l ^ B (B = 1, 2, 4: inside the lane's group of 8) by data-parallel
+// primitives (no LDS): quad permutations for 1 and 2; for 4, a row shift by 4 in the
+// direction that stays inside the group (row_shl: lane l reads lane l + 4).
+template <int B>
+__device__ __forceinline__ unsigned lane_xor(unsigned x, int ln) {
+  const int v = static_cast<int>(x);
+  if constexpr (B == 1) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false));  // quad_perm [1,0,3,2]
+  } else if constexpr (B == 2) {
+    return static_cast<unsigned>(__builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false));  // quad_perm [2,3,0,1]
+  } else {
+    static_assert(B == 4, "lane distance 1, 2 or 4");
+    const int from_hi = __builtin_amdgcn_mov_dpp(v, 0x104, 0xF, 0xF, false);  // row_shl:4
+    const int from_lo = __builtin_amdgcn_mov_dpp(v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    return static_cast<unsigned>((ln & 4) ? from_lo : from_hi);
+  }
+}
+
+// One round of the 8 x 8 transpose of u32 across 8 lanes (lane distance B): lanes with
+// bit B set send their slot m and take the partner's slot m ^ B into slot m; the others
+// send slot m ^ B and take the partner's slot m into it (m with bit B clear). The selects
+// are written with a mask: as a ? b : c on the array elements the compiler turns them
+// into dynamic indexing over all eight slots.
+template <int B>
+__device__ __forceinline__ void xchg_stage(unsigned (&P)[8], int ln) {
+  const unsigned up = 0u - ((static_cast<unsigned>(ln) / B) & 1u);
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+    if (m & B) continue;
+    const unsigned lo_m = P[m], hi_m = P[m ^ B];
+    const unsigned x = hi_m ^ ((lo_m ^ hi_m) & up);
+    const unsigned y = lane_xor<B>(x, ln);
+    P[m] = lo_m ^ ((lo_m ^ y) & up);
+    P[m ^ B] = y ^ ((y ^ hi_m) & up);
+  }
+}
+
 // (B's dQ MFMAs, at D = 128, run in the last KK slots of its 2 DK dP slots, with their
 // operands prefetched from the slot before.)
 // Body of the kernel for one role (ROLE_A: waves 0-3, else waves 4-7). Each role is
 // its own inlined copy, so that the register allocator never sees the values of one
 // role live in the other's code.
-template <int D, bool DET, bool ROLE_A, bool PART>
+template <int D, bool DET, bool ROLE_A, bool PART, bool FUSED>
 __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem, int worker, int w) {
   using C = PairCfg<D>;
   constexpr int BC = C::BC, BQ = C::BQ, SUBS = C::SUBS, DB = C::DB, DK = C::DK, KK = C::KK, ST = C::ST;
@@ -280,6 +317,7 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       int* sem;
       float* acc_blk;  // the step's first fp32 accumulator block
       rsrc_t acc_rs;   // stores (atomic variant: rows q0 .. q0 + 63, row-major); empty if none
+      int bhq[FUSED ? 2 : 0];  // FUSED: the step's b * H + h and first Q row (the bf16 dQ rows)
       bool go;
 #ifdef DASH_REPLAY
       float* dump;
@@ -291,6 +329,10 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
       pd.last = rec.w;
       const int q0s = rec.y;
       const int64_t bh = rec.x;
+      if constexpr (FUSED) {
+        pd.bhq[0] = rec.x;
+        pd.bhq[1] = rec.y;
+      }
       if (PART) {
         // Per-tile partials: the step's own slot, (b * H + h, step, rank), in the compact
         // layout described at kDqBlock.
@@ -336,6 +378,55 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #ifdef DASH_REPLAY
     floatx16 run;  // replay builds: running sum loaded for the partial being reduced
 #endif
+    // The final sum of this wave's 32x32 dQ block as bf16 rows of dq. Element 4 i + e of
+    // lane l is row 16 (i / 2) + 2 (i % 2) + l / 32 + 4 e, column l % 32 of the block, so
+    // each group of 8 lanes holds 8 adjacent columns of the same 16 rows: elements 0-7
+    // (rows R(m) = 2 (m / 4) + 4 (m % 4) + l / 32) and 8-15 (rows 16 + R(m)) are packed
+    // in pairs (one u32 per m), the 8 x 8 block of u32 is transposed across the 8 lanes
+    // (three exchange rounds, lane distances 4, 2, 1), and lane k of the group then holds
+    // rows R(k) and 16 + R(k), 8 columns each: two 16-byte stores. Rows at or past the
+    // batch's length fall outside the descriptor and are dropped.
+    auto store_dq_final = [&](const Pending& pd, const floatx16& v) __attribute__((always_inline)) {
+      // (Lane-derived values from an opaque lane index, so that the compiler computes them
+      // here instead of keeping them live from the kernel's start.)
+      const int ln = opaque_lane();
+      unsigned P[8];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) P[m] = pack_bf16(v[m] * p.scale, v[8 + m] * p.scale);
+      xchg_stage<4>(P, ln);
+      xchg_stage<2>(P, ln);
+      xchg_stage<1>(P, ln);
+      u32x4 lo, hi4;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        lo[t] = __builtin_amdgcn_perm(P[2 * t + 1], P[2 * t], 0x05040100u);
+        hi4[t] = __builtin_amdgcn_perm(P[2 * t + 1], P[2 * t], 0x07060302u);
+      }
+      // A failed wait leaves the descriptor empty; a step of a ragged last tile may start
+      // at or past the length (no rows then).
+      const int bh = pd.bhq[0], q0s = pd.bhq[1];
+      const int nrow = (p.seqlens ? seqlens[bh / H] : N) - q0s;
+      const int rows = !pd.go || nrow <= 0 ? 0 : (nrow < 64 ? nrow : 64);
+      const rsrc_t rs = make_rsrc(p.dq + (static_cast<int64_t>(bh) * N + q0s) * D, rows * D * 2);
+      const int k = ln & 7;
+      const int row = 32 * qbq + 2 * (k >> 2) + 4 * (k & 3) + (ln >> 5);
+      const int off = (row * D + 32 * dbq + 8 * ((ln & 31) >> 3)) * 2;
+      __builtin_amdgcn_raw_buffer_store_b128(lo, rs, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(hi4, rs, off + 16 * D * 2, 0, 0);
+    };
+    // Whether this step's contribution is the last of its dQ block and goes to dq as bf16
+    // (FUSED). The flag goes through an empty asm: otherwise the compiler sees the same
+    // test again in reduce_signal and duplicates the code between the two for each
+    // outcome.
+    auto writes_dq = [&](const Pending& pd) __attribute__((always_inline)) {
+      if constexpr (!(FUSED && DET && !PART && HAS_DQ)) {
+        return false;
+      } else {
+        int last = __builtin_amdgcn_readfirstlane(pd.last);
+        asm volatile("" : "+s"(last));
+        return last != 0;
+      }
+    };
     auto reduce_store = [&](const Pending& pd, const floatx16& v_in) __attribute__((always_inline)) {
       if (!HAS_DQ) return;
 #ifdef DASH_REPLAY
@@ -361,6 +452,12 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 #else
       const floatx16& v = v_in;
 #endif
+      if (writes_dq(pd)) {
+        store_dq_final(pd, v);
+#ifndef DASH_REPLAY
+        return;  // (replay builds also keep the final fp32 sum for the exact check)
+#endif
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (!DET) {
@@ -405,6 +502,10 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
     pd.sem = p.sem;
     pd.acc_blk = p.dqacc;
     pd.acc_rs = make_rsrc(p.dqacc, 0);
+    if constexpr (FUSED) {
+      pd.bhq[0] = 0;
+      pd.bhq[1] = 0;
+    }
     pd.go = false;
 #ifdef DASH_REPLAY
     pd.dump = nullptr;
@@ -839,8 +940,10 @@ __device__ __forceinline__ void pair_body(const BwdParams& p, LDS_AS char* smem,
 
 // DET: ordered reduction inside one XCD's L2 (every dQ tile's contributors share an
 // XCD), or float atomics; PART (with DET): every contribution to its own slot of the
-// per-tile partials buffer, no turns (a separate kernel adds them). One kernel each.
-template <int D, bool DET, bool PART>
+// per-tile partials buffer, no turns (a separate kernel adds them); FUSED (with DET, not
+// PART): the last contributor of every dQ block writes bf16 dQ (p.dq) instead of its
+// final fp32 sum. One kernel each, so that no instance carries another's code.
+template <int D, bool DET, bool PART, bool FUSED>
 __global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 bwd_pair_kernel(BwdParams p) {
   using C = PairCfg<D>;
@@ -865,18 +968,19 @@ bwd_pair_kernel(BwdParams p) {
   const int worker = sMisc[0];
   if (worker < 0) return;
   if (w < 4)
-    pair_body<D, DET, true, PART>(p, smem, worker, w);
+    pair_body<D, DET, true, PART, FUSED>(p, smem, worker, w);
   else
-    pair_body<D, DET, false, PART>(p, smem, worker, w);
+    pair_body<D, DET, false, PART, FUSED>(p, smem, worker, w);
 }
 
 template <int D>
 static hipError_t launch_pair_t(const BwdParams& prm, int grid, hipStream_t stream) {
   using C = PairCfg<D>;
   const int shmem = C::BYTES;
-  auto fn = prm.deterministic == 3 ? bwd_pair_kernel<D, true, true>
-            : prm.deterministic   ? bwd_pair_kernel<D, true, false>
-                                  : bwd_pair_kernel<D, false, false>;
+  auto fn = prm.deterministic == 3 ? bwd_pair_kernel<D, true, true, false>
+            : prm.deterministic && prm.dq ? bwd_pair_kernel<D, true, false, true>
+            : prm.deterministic   ? bwd_pair_kernel<D, true, false, false>
+                                  : bwd_pair_kernel<D, false, false, false>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(fn),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, shmem);
   if (e != hipSuccess) return e;

@@ -793,6 +793,7 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   bp.dk = static_cast<__bf16*>(dk);
   bp.dv = static_cast<__bf16*>(dv);
   bp.dqacc = dqacc;
+  bp.dq = nullptr;  // set below when the two-waves kernel writes dQ itself
   bp.sem = sem;
   bp.ctr = ctr;
   bp.err = err;
@@ -851,6 +852,15 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   const bool pair_ok = tab->tile == 128 && deterministic != 2 &&
                        (deterministic == 0 || deterministic == 3 || bp.xcd_local || st->num_xcd == 1);
   const bool use_pair = pair_ok && (kernel == DASH_KERNEL_TWO_WAVES_PER_SIMD || (kernel == DASH_KERNEL_AUTO && kPairAuto));
+  // The ordered reduction in the two-waves kernel with the full mask: the last contributor
+  // of every dQ block writes bf16 dQ itself (no cast kernel, and no final fp32 sum in the
+  // workspace). With the full mask every last contribution falls on an item's last task,
+  // which all CUs reach together; under the causal schedules they are spread over the
+  // run, and the extra work on those steps holds up the chains waiting behind them
+  // (measured: full mask d = 128 whole call 2.5 % faster, causal d = 128 N = 16384 2 %
+  // slower), so the causal calls keep the cast kernel.
+  const bool fused_dq = use_pair && deterministic == 1 && !causal;
+  if (fused_dq) bp.dq = static_cast<__bf16*>(dq);
   hipError_t e = !use_pair ? dash::launch_main(bp, d, tab->tile / 32, tab->workers, stream)
                  : d == 128 ? dash::launch_pair_d128(bp, tab->workers, stream)
                             : dash::launch_pair_d64(bp, tab->workers, stream);
@@ -883,6 +893,8 @@ int run_bwd(const void* q, const void* k, const void* v, const void* o, const vo
   } else if (deterministic == 3) {
     ec = dash::launch_dq_consolidate(dqacc, dq, int64_t(B) * H, N, L.row_stride, tab->tile, d, causal ? 1 : 0, scale,
                                      status, stream);
+  } else if (fused_dq) {
+    ec = dash::launch_status_copy(status, stream);
   } else if (deterministic == 1) {
     ec = dash::launch_dq_cast_blocks(dqacc, dq, int64_t(B) * H, N, L.row_stride, d, scale, status, stream,
                                      tab->seqlens, H);

@@ -66,6 +66,11 @@ struct BwdParams {
   float* replay;            // replay builds (DASH_REPLAY): dump of every ordered dQ partial, or null
   int replay_ranks;         // replay builds: rank slots per dQ block in the dump (KV tiles per head)
   const int* seqlens;       // non-null: batch b has seqlens[b] rows (<= N, the row stride of q, k, ...)
+  // Ordered reduction in the two-waves kernel: non-null = the last contributor of every
+  // dQ block writes bf16(scale * final sum) straight into dq [B*H][N][d] (rows past a
+  // batch's length untouched) instead of storing the final fp32 sum, so no cast kernel
+  // follows. Null: every sum goes to dqacc, and dq_cast_blocks_kernel writes dq.
+  __bf16* dq;
 };
 
 // Forward kernel (O and the natural-log LSE from Q, K, V).
@@ -221,6 +226,9 @@ struct StatusCopy {
   const int* err_in;
   int* status_out;
 };
+// Copies the call's error word into the stream's status slot (one thread), for calls
+// whose main kernel wrote dQ itself.
+hipError_t launch_status_copy(StatusCopy sc, hipStream_t stream);
 // dQ = bf16(scale * dqacc) for rows < N, from the ordered variant's block layout.
 hipError_t launch_dq_cast_blocks(const float* acc, void* dq, int64_t heads, int N, int row_stride, int d, float scale,
                                  StatusCopy sc, hipStream_t stream, const int* seqlens = nullptr, int H = 1);

@@ -228,15 +228,17 @@ def pair_asm(tmp_path_factory):
     return texts
 
 
-# The two-waves-per-SIMD kernel (d = 128 and 64): ordered, atomic and per-tile partials
-# instantiations, every flavour.
-PAIR_VARIANTS = [(d, det, part, fl) for d in (128, 64) for det, part in ((1, 0), (0, 0), (1, 1)) for fl in FLAVOURS]
+# The two-waves-per-SIMD kernel (d = 128 and 64): ordered (fp32 final sums, or bf16 dQ
+# written by the last contributors), atomic and per-tile partials instantiations, every
+# flavour.
+PAIR_VARIANTS = [(d, det, part, fused, fl) for d in (128, 64)
+                 for det, part, fused in ((1, 0, 0), (1, 0, 1), (0, 0, 0), (1, 1, 0)) for fl in FLAVOURS]
 
 
-@pytest.mark.parametrize("d,det,part,flavour", PAIR_VARIANTS,
-                         ids=[f"pair-d{v[0]}-det{v[1]}-part{v[2]}-{v[3]}" for v in PAIR_VARIANTS])
-def test_pair_kernel_inline_mfma_wait_states(pair_asm, d, det, part, flavour):
-    symbol = f"_ZN4dash15bwd_pair_kernelILi{d}ELb{det}ELb{part}EEEvNS_9BwdParamsE"
+@pytest.mark.parametrize("d,det,part,fused,flavour", PAIR_VARIANTS,
+                         ids=[f"pair-d{v[0]}-det{v[1]}-part{v[2]}-fused{v[3]}-{v[4]}" for v in PAIR_VARIANTS])
+def test_pair_kernel_inline_mfma_wait_states(pair_asm, d, det, part, fused, flavour):
+    symbol = f"_ZN4dash15bwd_pair_kernelILi{d}ELb{det}ELb{part}ELb{fused}EEEvNS_9BwdParamsE"
     insts, labels = parse_kernel(pair_asm[flavour], symbol)
     # Both roles' bodies, d = 128: 16 + 16 + 8 per step and 8 for an item's last dQ block,
     # each; d = 64: 8 + 8 + 8 (A), 8 + 8 (B), and 8.
