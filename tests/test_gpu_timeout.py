@@ -21,16 +21,19 @@ TOL = 1e-2
 DEFAULT_US = 5_000_000
 
 
+@pytest.mark.parametrize("mask", ["full", "causal"])
 @pytest.mark.parametrize("kernel", ["two_waves", "one_wave"])
-def test_timeout_is_reported_and_the_next_call_is_correct(kernel):
+def test_timeout_is_reported_and_the_next_call_is_correct(kernel, mask):
+    """Full mask, two-waves kernel: the main kernel writes dQ itself and a one-thread kernel
+    copies the status word; the other cases end with the dQ cast, which copies it."""
     from scheduling_fa_attn_amd import dash
-    case = make_case(1, 2, 2, 4096, 128, False, seed=97)
+    case = make_case(1, 2, 2, 4096, 128, mask == "causal", seed=97)
     dev = to_device(case)
     ref = oracle_grads(case)
     assert dash.dash_set_kernel(kernel) == dash.DASH_OK
     try:
         assert dash.dash_last_kernel_error() == dash.DASH_OK
-        print(f"kernel={kernel}: wait bound 0, naive schedule", flush=True)
+        print(f"kernel={kernel} mask={mask}: wait bound 0, naive schedule", flush=True)
         assert dash.dash_set_wait_timeout(0) == dash.DASH_OK
         try:
             with pytest.raises(dash.DashError) as e:
@@ -41,13 +44,13 @@ def test_timeout_is_reported_and_the_next_call_is_correct(kernel):
             ws = torch.empty(dash.dash_attn_bwd_workspace_size(B, H, Hkv, N, d), dtype=torch.uint8, device="cuda")
             outs = [torch.empty_like(dev[k]) for k in ("q", "k", "v")]
             st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs,
-                                    case["scale"], "full", "naive", 1, ws)
+                                    case["scale"], mask, "naive", 1, ws)
             assert st == dash.DASH_OK
         finally:
             assert dash.dash_set_wait_timeout(DEFAULT_US) == dash.DASH_OK
         print(f"kernel={kernel}: default bound, same workspace, error of the failed call never read", flush=True)
         st = dash.dash_attn_bwd(dev["q"], dev["k"], dev["v"], dev["o"], dev["do"], dev["lse"], *outs,
-                                case["scale"], "full", "naive", 1, ws)
+                                case["scale"], mask, "naive", 1, ws)
         assert st == dash.DASH_OK
         torch.cuda.synchronize()
         errs = rel_errs(outs, ref)
