@@ -20,8 +20,11 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-2
 
-# (B, H, Hkv, N, d, causal, schedule): the second call is smaller in every dimension.
-CALLS = [(2, 4, 2, 700, 128, True, "sym_shift"), (1, 2, 2, 256, 64, False, "shift")]
+# (B, H, Hkv, N, d, causal, schedule), each call smaller than the one before: the full
+# mask at 128-row tiles (the main kernel writes dQ itself there), the causal mask with a
+# ragged last tile, then 64-row tiles on the one-wave kernel.
+CALLS = [(2, 4, 2, 1024, 128, False, "shift"), (2, 4, 2, 700, 128, True, "sym_shift"),
+         (1, 2, 2, 256, 64, False, "shift")]
 
 
 def _noalloc(case, dev, schedule, det):
