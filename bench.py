@@ -271,9 +271,14 @@ def smi_sample():
         doc = json.loads(res.stdout)
     except Exception as e:  # noqa: BLE001
         return {"error": f"{type(e).__name__}: {e}"[:200]}
+    return parse_smi(doc)
+
+
+def parse_smi(doc):
+    """GFX clock per XCD (MHz) and socket power (W) from a parsed `amd-smi metric -c -p
+    --json` document: .../clock/gfx_<XCD>/clk/value and .../power/socket_power/value."""
     gfx, power = [], []
     for path, val in _smi_numbers(doc):
-        # .../clock/gfx_<XCD>/clk/value (MHz) and .../power/socket_power/value (W)
         if len(path) >= 3 and path[-1] == "value" and path[-2] == "clk" and path[-3].startswith("gfx"):
             gfx.append(val)
         elif len(path) >= 2 and path[-1] == "value" and path[-2] == "socket_power":
@@ -629,7 +634,7 @@ def main():
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE scale factor) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: measures one GPU only (asked for --gpus {args.gpus}); "
               "the backward of independent (batch, KV head) units would shard over GPUs with no exchange.",
               file=sys.stderr)
         sys.exit(2)
