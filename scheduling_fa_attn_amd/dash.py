@@ -70,8 +70,7 @@ def open_library(path: str) -> ctypes.CDLL:
     """Load a build of the library at `path` (the release build, or the profiling or
     replay build beside it) with the C signatures declared; independent of load()."""
     if not os.path.exists(path):
-        raise RuntimeError(f"HIP library {path} is not built; run scheduling_fa_attn_amd/build.py "
-                           "or __graft_entry__.build()")
+        raise RuntimeError(f"HIP library {path} is not built; run python scheduling_fa_attn_amd/build.py")
     lib = ctypes.CDLL(path)
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.dash_attn_bwd_workspace_size.argtypes = [i, i, i, i, i]

@@ -252,8 +252,9 @@ def test_auto_picks_measured_fastest_on_paper_grid():
                 assert dash.dash_schedule_resolve(B, H, H, N, d, mask, "auto", 8, 32) == want, (d, mask, N)
 
 
-# Main-kernel times on one MI355X, microseconds per call, and the
-# schedule measured fastest: (B, H, Hkv, N, d, mask, placement) -> fastest.
+# Main-kernel times measured on one MI355X, microseconds per call (naive / descending /
+# shift or symmetric shift), and the schedule measured fastest:
+# (B, H, Hkv, N, d, mask, placement) -> fastest.
 MEASURED_FASTEST = [
     ((2, 4, 2, 4096, 128, "causal", "aggregate"), "sym_shift"),   # 638 / 543 / 307
     ((1, 2, 2, 256, 64, "causal", "aggregate"), "descending"),    # 34 / 30 / 35
