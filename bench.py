@@ -286,15 +286,22 @@ def parse_smi(doc):
     return {"gfx_clk_mhz": gfx, "power_w": power}
 
 
-def sustained_clock(call, seconds=1.5, samples=3):
-    """Runs `call` back to back for `seconds` while amd-smi reads the clocks `samples`
-    times from another thread; returns the readings."""
+def sustained_clock(call, seconds=1.5, samples=3, settle=0.5):
+    """Runs `call` back to back for `settle` seconds, then for `seconds` more while
+    amd-smi reads the clocks `samples` times from another thread; returns the readings.
+    (The settle period keeps a reading of the idle board, or telemetry not yet updated
+    since the load began, out of the samples.)"""
     import threading
 
     import torch
 
     readings = []
     stop = threading.Event()
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle:
+        for _ in range(8):
+            call()
+        torch.cuda.synchronize()
 
     def sampler():
         for _ in range(samples):
@@ -317,6 +324,24 @@ def sustained_clock(call, seconds=1.5, samples=3):
     t.join()
     return {"calls": n, "seconds": round(time.perf_counter() - t0, 2), "readings": readings,
             "source": "amd-smi metric -c -p during back-to-back calls of the headline step"}
+
+
+def clock_summary(readings, achieved_tflops):
+    """The dense peak is quoted at 2.4 GHz; under this load the board's power limit holds
+    the clock lower. Mean of the XCD clocks over the readings, the bf16 peak at that clock
+    and the main kernel's fraction of it. Readings at less than half the highest socket
+    power are idle snapshots and are left out of the mean."""
+    pw = [max(r.get("power_w") or [0.0]) for r in readings]
+    used = [r for r, w in zip(readings, pw) if w >= 0.5 * max(pw + [0.0])]
+    out = {"readings_in_mean": len(used)}
+    clks = [c for r in used for c in (r.get("gfx_clk_mhz") or [])]
+    if clks:
+        mhz = sum(clks) / len(clks)
+        peak_at = PEAK_BF16_TFLOPS * mhz / PEAK_CLOCK_MHZ
+        out["mean_gfx_mhz"] = round(mhz, 1)
+        out["bf16_peak_at_mean_clock_tflops"] = round(peak_at, 1)
+        out["main_kernel_frac_at_mean_clock"] = round(achieved_tflops / peak_at, 4)
+    return out
 
 
 def cpu_baseline(shape, causal, seed, budget_s):
@@ -723,16 +748,7 @@ def main():
                 raise dash.DashError(st, "dash_attn_bwd")
 
         result["clock"] = sustained_clock(headline_call)
-        # The dense peak is quoted at 2.4 GHz; under this load the board's power limit
-        # holds the clock lower. The main kernel's fraction of the peak at the clock it
-        # actually ran at (mean of the XCD clocks over the readings):
-        clks = [c for r in result["clock"]["readings"] for c in (r.get("gfx_clk_mhz") or [])]
-        if clks:
-            mhz = sum(clks) / len(clks)
-            peak_at = PEAK_BF16_TFLOPS * mhz / PEAK_CLOCK_MHZ
-            result["clock"]["mean_gfx_mhz"] = round(mhz, 1)
-            result["clock"]["bf16_peak_at_mean_clock_tflops"] = round(peak_at, 1)
-            result["clock"]["main_kernel_frac_at_mean_clock"] = round(achieved / peak_at, 4)
+        result["clock"].update(clock_summary(result["clock"]["readings"], achieved))
         log(f"  clock during back-to-back calls: {result['clock']['readings']}")
         del outs
     if not args.no_cold:

@@ -59,3 +59,18 @@ def test_traffic_lookup_refuses_another_kernel():
     # were taken from.
     assert bench.traffic_bytes("full-d128-N2048", "bwd_main_kernel<128, 4, true, false, false, false>") is None
     assert bench.traffic_bytes("no-such-workload", "bwd_pair_kernel<128, true, false, true>") is None
+
+
+def test_clock_summary_leaves_idle_readings_out():
+    # An idle snapshot (300 W at the full 2.4 GHz) among loaded readings does not raise
+    # the mean clock; the fraction is taken at the mean of the loaded readings.
+    loaded = {"gfx_clk_mhz": [1800.0, 1700.0], "power_w": [1390.0]}
+    idle = {"gfx_clk_mhz": [2400.0, 2400.0], "power_w": [300.0]}
+    got = bench.clock_summary([idle, loaded, loaded], 850.0)
+    assert got["readings_in_mean"] == 2
+    assert got["mean_gfx_mhz"] == 1750.0
+    peak = bench.PEAK_BF16_TFLOPS * 1750.0 / bench.PEAK_CLOCK_MHZ
+    assert abs(got["main_kernel_frac_at_mean_clock"] - round(850.0 / peak, 4)) < 1e-12
+    # No power readings: every reading counts; no clocks: no mean.
+    assert bench.clock_summary([{"gfx_clk_mhz": [1800.0], "power_w": []}], 850.0)["readings_in_mean"] == 1
+    assert bench.clock_summary([], 850.0) == {"readings_in_mean": 0}
