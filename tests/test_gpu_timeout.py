@@ -21,19 +21,21 @@ TOL = 1e-2
 DEFAULT_US = 5_000_000
 
 
+@pytest.mark.parametrize("d", [128, 64])
 @pytest.mark.parametrize("mask", ["full", "causal"])
 @pytest.mark.parametrize("kernel", ["two_waves", "one_wave"])
-def test_timeout_is_reported_and_the_next_call_is_correct(kernel, mask):
+def test_timeout_is_reported_and_the_next_call_is_correct(kernel, mask, d):
     """Full mask, two-waves kernel: the main kernel writes dQ itself and a one-thread kernel
-    copies the status word; the other cases end with the dQ cast, which copies it."""
+    copies the status word; the other cases end with the dQ cast, which copies it. At
+    d = 64 the two-waves kernel's A waves own the dQ blocks (and their waits)."""
     from scheduling_fa_attn_amd import dash
-    case = make_case(1, 2, 2, 4096, 128, mask == "causal", seed=97)
+    case = make_case(1, 2, 2, 4096, d, mask == "causal", seed=97)
     dev = to_device(case)
     ref = oracle_grads(case)
     assert dash.dash_set_kernel(kernel) == dash.DASH_OK
     try:
         assert dash.dash_last_kernel_error() == dash.DASH_OK
-        print(f"kernel={kernel} mask={mask}: wait bound 0, naive schedule", flush=True)
+        print(f"kernel={kernel} mask={mask} d={d}: wait bound 0, naive schedule", flush=True)
         assert dash.dash_set_wait_timeout(0) == dash.DASH_OK
         try:
             with pytest.raises(dash.DashError) as e:
